@@ -1,0 +1,243 @@
+"""CPU oracle for the paged, quantized, query-aware sparse decode step.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path (the HIP library
+and its Python binding) never does.  The arithmetic lives in plain C
+(``kvq_oracle.c``, fp64 accumulation, fp32 quantization without contraction);
+this module only allocates numpy arrays and calls it through ctypes.
+
+Every function follows the pages it cites in ``kvq_oracle.c``:
+  append      -- paged store and INT8 quantization (pzsr.cn layout page,
+                 sections 2-3; uyd888.cn Gemini page, chapter 1)
+  page_meta   -- phi(K_j) = per-channel (min, max) in fp32 (TinyServe page,
+                 sections 2.1 and 5.2)
+  page_scores -- r = sum_i (q_i >= 0 ? q_i M_i : q_i m_i) (TinyServe page,
+                 section 2.1), GQA group score = max over the group's heads
+  topk        -- top-K pages per (sequence, KV head) (TinyServe page,
+                 sections 3.1 and 5.1)
+  attention   -- softmax(q k^T / sqrt(d)) v over the selected pages
+                 (intelliparadigm.com page, section 2.1; TinyServe page,
+                 section 3.1)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvq_oracle.c")
+_LIB = os.path.join(_HERE, "libkvq_oracle.so")
+PAGE = 16
+
+_CFLAGS = ["-O2", "-std=c11", "-Wall", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into oracle/libkvq_oracle.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        L.kvqo_append.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P]
+        L.kvqo_append.restype = I
+        L.kvqo_page_meta.argtypes = [I, I, I, I, I, P, P, P, P, P, P]
+        L.kvqo_page_meta.restype = None
+        L.kvqo_page_scores.argtypes = [I, I, I, I, I, P, P, P, P, P]
+        L.kvqo_page_scores.restype = None
+        L.kvqo_num_selected.argtypes = [I, I, I, I]
+        L.kvqo_num_selected.restype = I
+        L.kvqo_topk.argtypes = [I, I, I, P, P, I, I, I, I, P, P]
+        L.kvqo_topk.restype = I
+        L.kvqo_attention.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, ctypes.c_double, P]
+        L.kvqo_attention.restype = None
+        L.kvqo_decode_step.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, I, I, I,
+                                       ctypes.c_double, P, P, P, P, I]
+        L.kvqo_decode_step.restype = I
+        L.kvqo_half_to_float.argtypes = [ctypes.c_uint16]
+        L.kvqo_half_to_float.restype = ctypes.c_float
+        L.kvqo_dequant.argtypes = [ctypes.c_uint8, ctypes.c_float, ctypes.c_float]
+        L.kvqo_dequant.restype = ctypes.c_float
+        L.kvqo_quant_scale.argtypes = [ctypes.c_float, ctypes.c_float, P, P]
+        L.kvqo_quant_scale.restype = None
+        L.kvqo_quant_code.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_float]
+        L.kvqo_quant_code.restype = ctypes.c_uint8
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "oracle needs C-contiguous numpy arrays"
+    return a.ctypes.data
+
+
+def _bits(x: np.ndarray) -> np.ndarray:
+    """fp16 array -> its uint16 bit pattern (no arithmetic)."""
+    return np.ascontiguousarray(x).view(np.uint16) if x.dtype == np.float16 else np.ascontiguousarray(x, np.uint16)
+
+
+# --------------------------------------------------------------------- cache
+class Cache:
+    """One layer's paged cache as plain numpy arrays (the layout in kvq_oracle.c)."""
+
+    def __init__(self, fmt: int, num_phys_pages: int, num_kv_heads: int, head_dim: int):
+        self.fmt, self.P_phys, self.H, self.d = fmt, num_phys_pages, num_kv_heads, head_dim
+        shape = (num_phys_pages, num_kv_heads, PAGE, head_dim)
+        dt = np.uint16 if fmt == 0 else np.uint8
+        self.k_pages = np.zeros(shape, dtype=dt)
+        self.v_pages = np.zeros(shape, dtype=dt)
+        if fmt == 1:
+            self.params = np.zeros((num_phys_pages, num_kv_heads, PAGE, 4), dtype=np.float32)
+        elif fmt == 2:
+            self.params = np.zeros((num_phys_pages, num_kv_heads, 4), dtype=np.float32)
+        else:
+            self.params = np.zeros((1,), dtype=np.float32)
+        self.meta = np.zeros((num_phys_pages, num_kv_heads, 2, head_dim), dtype=np.float32)
+
+
+def append(cache: Cache, block_table, start_pos, new_off, k_new, v_new) -> None:
+    """Write packed new tokens k_new/v_new [N][H][d] (fp16) into the cache."""
+    bt = np.ascontiguousarray(block_table, np.int32)
+    sp = np.ascontiguousarray(start_pos, np.int32)
+    off = np.ascontiguousarray(new_off, np.int32)
+    kb, vb = _bits(k_new), _bits(v_new)
+    B = sp.shape[0]
+    rc = lib().kvqo_append(cache.fmt, B, cache.H, cache.d, bt.shape[1], _p(bt), _p(sp), _p(off),
+                           _p(kb), _p(vb), _p(cache.k_pages), _p(cache.v_pages), _p(cache.params))
+    if rc != 0:
+        raise ValueError("oracle append: precondition violated")
+
+
+def page_meta(cache: Cache, block_table, seq_lens, page_begin=None) -> None:
+    bt = np.ascontiguousarray(block_table, np.int32)
+    sl = np.ascontiguousarray(seq_lens, np.int32)
+    pb = None if page_begin is None else np.ascontiguousarray(page_begin, np.int32)
+    lib().kvqo_page_meta(cache.fmt, sl.shape[0], cache.H, cache.d, bt.shape[1], _p(bt), _p(sl), _p(pb),
+                         _p(cache.k_pages), _p(cache.params), _p(cache.meta))
+
+
+def page_scores(cache: Cache, block_table, seq_lens, q) -> np.ndarray:
+    """float64 [B][H_kv][max_pages]; pages past the sequence's end are -inf."""
+    bt = np.ascontiguousarray(block_table, np.int32)
+    sl = np.ascontiguousarray(seq_lens, np.int32)
+    qb = _bits(q)
+    B, Hq, d = qb.shape
+    out = np.empty((B, cache.H, bt.shape[1]), dtype=np.float64)
+    lib().kvqo_page_scores(B, Hq, cache.H, d, bt.shape[1], _p(bt), _p(sl), _p(qb), _p(cache.meta), _p(out))
+    return out
+
+
+def num_selected(P: int, ratio_num: int, ratio_den: int, k_fixed: int) -> int:
+    return lib().kvqo_num_selected(P, ratio_num, ratio_den, k_fixed)
+
+
+def topk(scores, seq_lens, ratio_num, ratio_den, k_fixed, k_cap) -> tuple[np.ndarray, np.ndarray]:
+    """(int32 [B][H][k_cap] ascending page ids padded with -1, int32 [B][H] counts)."""
+    sc = np.ascontiguousarray(scores, np.float64)
+    sl = np.ascontiguousarray(seq_lens, np.int32)
+    B, H, maxp = sc.shape
+    sel = np.empty((B, H, k_cap), dtype=np.int32)
+    cnt = np.empty((B, H), dtype=np.int32)
+    rc = lib().kvqo_topk(B, H, maxp, _p(sl), _p(sc), ratio_num, ratio_den, k_fixed, k_cap, _p(sel), _p(cnt))
+    if rc != 0:
+        raise ValueError("oracle topk: k_cap too small")
+    return sel, cnt
+
+
+def attention(cache: Cache, block_table, seq_lens, q, sel_pages=None, sel_count=None, sm_scale=None) -> np.ndarray:
+    """float64 [B][H_q][d]; sel_pages None attends to every page."""
+    bt = np.ascontiguousarray(block_table, np.int32)
+    sl = np.ascontiguousarray(seq_lens, np.int32)
+    qb = _bits(q)
+    B, Hq, d = qb.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    sp = None if sel_pages is None else np.ascontiguousarray(sel_pages, np.int32)
+    sc = None if sel_count is None else np.ascontiguousarray(sel_count, np.int32)
+    k_cap = 0 if sp is None else sp.shape[2]
+    out = np.empty((B, Hq, d), dtype=np.float64)
+    lib().kvqo_attention(cache.fmt, B, Hq, cache.H, d, bt.shape[1], _p(bt), _p(sl), _p(qb),
+                         _p(cache.k_pages), _p(cache.v_pages), _p(cache.params), _p(sp), _p(sc), k_cap,
+                         float(sm_scale), _p(out))
+    return out
+
+
+def decode_step(cache: Cache, block_table, seq_lens, q, ratio_num, ratio_den, k_fixed, k_cap,
+                sm_scale=None, nthreads=1):
+    """(scores, sel_pages, sel_count, out) of one decode step on nthreads host threads."""
+    bt = np.ascontiguousarray(block_table, np.int32)
+    sl = np.ascontiguousarray(seq_lens, np.int32)
+    qb = _bits(q)
+    B, Hq, d = qb.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    maxp = bt.shape[1]
+    scores = np.empty((B, cache.H, maxp), dtype=np.float64)
+    sel = np.empty((B, cache.H, k_cap), dtype=np.int32)
+    cnt = np.empty((B, cache.H), dtype=np.int32)
+    out = np.empty((B, Hq, d), dtype=np.float64)
+    rc = lib().kvqo_decode_step(cache.fmt, B, Hq, cache.H, d, maxp, _p(bt), _p(sl), _p(qb),
+                                _p(cache.k_pages), _p(cache.v_pages), _p(cache.params), _p(cache.meta),
+                                ratio_num, ratio_den, k_fixed, k_cap, float(sm_scale),
+                                _p(scores), _p(sel), _p(cnt), _p(out), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle decode_step: k_cap too small")
+    return scores, sel, cnt, out
+
+
+# ------------------------------------------------------------ element probes
+def half_to_float(bits: int) -> float:
+    return float(lib().kvqo_half_to_float(bits))
+
+
+def dequant(code: int, scale: float, zero: float) -> float:
+    return float(lib().kvqo_dequant(code, scale, zero))
+
+
+def quant_scale(lo: float, hi: float) -> tuple[np.float32, np.float32]:
+    s = ctypes.c_float()
+    inv = ctypes.c_float()
+    lib().kvqo_quant_scale(lo, hi, ctypes.byref(s), ctypes.byref(inv))
+    return np.float32(s.value), np.float32(inv.value)
+
+
+def quant_code(x: float, zero: float, inv: float) -> int:
+    return int(lib().kvqo_quant_code(x, zero, inv))
+
+
+# ------------------------------------------------------- whole-workload build
+def build_cache(w, upto=None) -> tuple[Cache, np.ndarray]:
+    """Build workload w's cache (every sequence, prefill of all its tokens, then
+    metadata of every page).  ``upto[b]`` limits sequence b to its first upto[b]
+    tokens.  Returns (cache, block_table)."""
+    table, n_phys = w.block_table()
+    lens = w.seq_lens() if upto is None else np.asarray(upto, np.int32)
+    cache = Cache(w.fmt, n_phys, w.num_kv_heads, w.head_dim)
+    for b in range(w.batch):
+        L = int(lens[b])
+        k = w.keys(b)[:L]
+        v = w.values(b)[:L]
+        sp = np.zeros(w.batch, np.int32)
+        off = np.zeros(w.batch + 1, np.int32)
+        off[b + 1:] = L                      # only sequence b receives rows in this call
+        append(cache, table, sp, off, k, v)
+    page_meta(cache, table, lens)
+    return cache, table

@@ -1,0 +1,554 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics
+fix, never against the oracle's own formulas retyped.
+
+Each test names the mistake it is there to catch.  Independent references are
+numpy routines on the unpaged arrays (fp16 casts, min/max, sort, dense
+softmax attention), hand-derived fixtures under tests/golden/, closed forms,
+and invariants (the no-underestimate property of the TinyServe page, section
+2.1; the scale/2 error bound of min/max quantization)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from workloads import PAGE
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------ helpers
+def np_dequant(codes, scale, zero):
+    """code*scale + zero rounded once to fp32.  code*scale is exact in fp64
+    (8 x 24 bits); the sum is checked exact against extended precision, so the
+    single fp64 -> fp32 rounding equals a fused multiply-add."""
+    c = codes.astype(np.float64)
+    s = np.asarray(scale, np.float32).astype(np.float64)
+    z = np.asarray(zero, np.float32).astype(np.float64)
+    r64 = c * s + z
+    rl = c.astype(np.longdouble) * s.astype(np.longdouble) + z.astype(np.longdouble)
+    assert np.all(rl == r64.astype(np.longdouble)), "fp64 sum not exact; reference would double-round"
+    return r64.astype(np.float32)
+
+
+def gather_tokens(arr, table_row, L):
+    """[P_phys][H][16][...] paged array -> [L][H][...] logical order."""
+    t = np.arange(L)
+    return arr[table_row[t // PAGE], :, t % PAGE]
+
+
+def decoded_keys_values(w, cache, table, b):
+    """(K, V) fp32 [L][H][d] of sequence b as stored, decoded by numpy."""
+    L = int(w.seq_lens()[b])
+    kc = gather_tokens(cache.k_pages, table[b], L)
+    vc = gather_tokens(cache.v_pages, table[b], L)
+    if w.fmt == workloads.FMT_FP16:
+        return kc.view(np.float16).astype(np.float32), vc.view(np.float16).astype(np.float32)
+    t = np.arange(L)
+    if w.fmt == workloads.FMT_INT8_TOKEN:
+        p = cache.params[table[b][t // PAGE], :, t % PAGE]          # [L][H][4]
+    else:
+        p = cache.params[table[b][t // PAGE]]                        # [L][H][4]
+    K = np_dequant(kc, p[..., 0:1], p[..., 1:2])
+    V = np_dequant(vc, p[..., 2:3], p[..., 3:4])
+    return K, V
+
+
+def dense_attention(q, K, V, scale):
+    """numpy fp64 softmax(q K^T * scale) V for one head: q [d], K/V [n][d]."""
+    lg = K.astype(np.float64) @ q.astype(np.float64) * scale
+    w = np.exp(lg - lg.max())
+    return (w[:, None] * V.astype(np.float64)).sum(0) / w.sum()
+
+
+def one_token_cache(fmt, x_k, x_v=None):
+    """Cache with one sequence of len(x_k) tokens, 1 KV head, d = row length."""
+    x_k = np.asarray(x_k, np.float16)
+    L, d = x_k.shape
+    x_v = x_k if x_v is None else np.asarray(x_v, np.float16)
+    P = (L + PAGE - 1) // PAGE
+    cache = oracle.Cache(fmt, P, 1, d)
+    table = np.arange(P, dtype=np.int32)[None]
+    oracle.append(cache, table, [0], [0, L], x_k[:, None, :], x_v[:, None, :])
+    return cache, table
+
+
+# ------------------------------------------------------------ fp16 decoding
+def test_half_decode_matches_numpy_for_every_bit_pattern():
+    """Catches a wrong exponent bias, subnormal or sign handling."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([oracle.half_to_float(int(b)) for b in bits[::7]], dtype=np.float32)
+    r = ref[::7]
+    nan = np.isnan(r)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), r[~nan].view(np.uint32))
+
+
+# ---------------------------------------------------------- quantization
+def test_quant_golden_rows():
+    """Hand-worked rows pin scale, zero, round-half-even and clamping."""
+    for row in gold("quant_rows.json")["rows"]:
+        x = np.array([row["x"]], np.float16)
+        cache, table = one_token_cache(workloads.FMT_INT8_TOKEN, x)
+        codes = cache.k_pages[0, 0, 0, :x.shape[1]]
+        assert codes.tolist() == row["codes"], row["derivation"]
+        s, z = cache.params[0, 0, 0, 0], cache.params[0, 0, 0, 1]
+        assert s == np.float32(row["scale"]) and z == np.float32(row["zero"])
+        dec = np_dequant(codes, s, z)
+        assert dec.tolist() == [float(v) for v in row["decoded"]]
+
+
+def _random_rows(rng, n, d):
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    x[: n // 3] *= 30.0                                      # wide rows
+    x[n // 3: n // 2, : d // 8] *= 15.0                      # outlier channels
+    x[-3:] = 0.75                                            # constant rows
+    return x.astype(np.float16)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_quant_error_within_half_scale_and_nearest_code(d):
+    """|x - decode(code)| <= scale/2 (+fp32 slack), the code is the nearest of
+    its neighbours, min -> code 0 decoding to min exactly, max -> 255.
+    Catches floor-instead-of-round, a wrong scale or zero, missing clamp."""
+    rng = np.random.default_rng(7)
+    x = _random_rows(rng, 300, d)
+    cache, table = one_token_cache(workloads.FMT_INT8_TOKEN, x)
+    L = x.shape[0]
+    t = np.arange(L)
+    codes = cache.k_pages[t // PAGE, 0, t % PAGE].astype(np.int64)      # [L][d]
+    p = cache.params[t // PAGE, 0, t % PAGE]                             # [L][4]
+    s, z = p[:, 0], p[:, 1]
+    xf = x.astype(np.float32)
+    lo, hi = xf.min(1), xf.max(1)
+    assert np.array_equal(z, lo), "zero-point must be the row minimum"
+    const = hi == lo
+    assert np.all(s[const] == 1.0) and np.all(codes[const] == 0)
+    rng_ = (hi - lo).astype(np.float64)
+    assert np.allclose(s[~const].astype(np.float64), rng_[~const] / 255.0, rtol=2 ** -22, atol=0)
+    dec = np_dequant(codes, s[:, None], z[:, None]).astype(np.float64)
+    err = np.abs(xf.astype(np.float64) - dec)
+    ulp = np.spacing(np.maximum(np.abs(lo), np.abs(hi)).astype(np.float32)).astype(np.float64)
+    slack = 2 * ulp + 255 * s.astype(np.float64) * 2 ** -22
+    assert np.all(err <= s[:, None] / 2 + slack[:, None])
+    # nearest code: neighbours are no closer
+    for dc in (-1, 1):
+        nb = np.clip(codes + dc, 0, 255)
+        dn = np.abs(xf - np_dequant(nb, s[:, None], z[:, None])).astype(np.float64)
+        assert np.all(err <= dn + slack[:, None])
+    amin = xf.argmin(1)
+    amax = xf.argmax(1)
+    assert np.all(codes[t, amin] == 0)
+    assert np.all(dec[t, amin] == lo)
+    assert np.all(codes[~const][:, None].squeeze(1)[np.arange((~const).sum()), amax[~const]] == 255)
+
+
+def test_value_rows_quantized_separately_with_same_scheme():
+    """K and V rows each get their own (scale, zero); catches V reusing K's."""
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((20, 64)).astype(np.float16)
+    v = (rng.standard_normal((20, 64)) * 7 + 3).astype(np.float16)
+    cache, _ = one_token_cache(workloads.FMT_INT8_TOKEN, k, v)
+    t = np.arange(20)
+    p = cache.params[t // PAGE, 0, t % PAGE]
+    assert np.array_equal(p[:, 3], v.astype(np.float32).min(1))
+    assert np.array_equal(p[:, 1], k.astype(np.float32).min(1))
+
+
+def test_group64_scope_alignment_and_partial_tail():
+    """Per-group quantization: 64-token groups aligned to logical positions 64g
+    (uyd888.cn Gemini page, chapter 1), all channels of a KV head share one
+    (scale, zero); a trailing partial group uses only its valid tokens.
+    Catches per-page or per-token scope and misaligned groups."""
+    rng = np.random.default_rng(11)
+    L, H, d = 150, 2, 64
+    k = rng.standard_normal((L, H, d)).astype(np.float32)
+    k[64:128] *= 40.0                     # second group is much wider
+    k[140, 1, 5] = -90.0                  # tail group, head 1 only
+    v = rng.standard_normal((L, H, d)).astype(np.float32)
+    k16, v16 = k.astype(np.float16), v.astype(np.float16)
+    P = (L + PAGE - 1) // PAGE
+    table = np.random.default_rng(5).permutation(P + 3)[:P].astype(np.int32)[None]
+    cache = oracle.Cache(workloads.FMT_INT8_GROUP64, P + 3, H, d)
+    oracle.append(cache, table, [0], [0, L], k16, v16)
+    kf = k16.astype(np.float32)
+    for g0 in range(0, L, 64):
+        g1 = min(g0 + 64, L)
+        for h in range(H):
+            lo = kf[g0:g1, h].min()
+            for j in range(g0 // PAGE, (g1 + PAGE - 1) // PAGE):
+                assert cache.params[table[0, j], h, 1] == lo, (g0, h, j)
+    # tokens of group 0 are not affected by group 1's range: their codes span 0..255
+    c0 = cache.k_pages[table[0, :4], 0]
+    assert c0.min() == 0 and c0.max() == 255
+    # decoded values within scale/2 of the inputs everywhere
+    w = workloads.small(5).with_(batch=1, num_kv_heads=H, num_q_heads=H, head_dim=d, seq_len=L)
+    K, _ = decoded_keys_values(w, cache, table, 0)
+    t = np.arange(L)
+    s = cache.params[table[0][t // PAGE], :, 0]
+    assert np.all(np.abs(K - kf) <= s[:, :, None] / 2 + 1e-5 * np.abs(kf).max())
+
+
+def test_group64_rejects_unaligned_start():
+    cache = oracle.Cache(workloads.FMT_INT8_GROUP64, 8, 1, 64)
+    x = np.zeros((3, 1, 64), np.float16)
+    with pytest.raises(ValueError):
+        oracle.append(cache, np.arange(8, dtype=np.int32)[None], [16], [0, 3], x, x)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_paged_placement_through_shuffled_table(n):
+    """Token t lands in physical page table[b][t/16], slot t%16 (pzsr.cn page,
+    section 3).  Checked by gathering with numpy: fp16 storage returns the input
+    bits exactly; INT8 storage decodes to within scale/2.  Slots past a
+    sequence's end stay untouched.  Catches transposed page/slot indexing."""
+    w = workloads.small(n)
+    cache, table = oracle.build_cache(w)
+    lens = w.seq_lens()
+    used = np.zeros(cache.P_phys, bool)
+    for b in range(w.batch):
+        L = int(lens[b])
+        kin = w.keys(b).astype(np.float32)
+        vin = w.values(b).astype(np.float32)
+        if w.fmt == workloads.FMT_FP16:
+            kc = gather_tokens(cache.k_pages, table[b], L)
+            assert np.array_equal(kc, w.keys(b).view(np.uint16))
+            assert np.array_equal(gather_tokens(cache.v_pages, table[b], L), w.values(b).view(np.uint16))
+        else:
+            K, V = decoded_keys_values(w, cache, table, b)
+            t = np.arange(L)
+            if w.fmt == workloads.FMT_INT8_TOKEN:
+                p = cache.params[table[b][t // PAGE], :, t % PAGE]
+            else:
+                p = cache.params[table[b][t // PAGE]]
+            tol_k = p[..., 0:1] / 2 + 1e-6 * np.abs(kin).max()
+            tol_v = p[..., 2:3] / 2 + 1e-6 * np.abs(vin).max()
+            assert np.all(np.abs(K - kin) <= tol_k)
+            assert np.all(np.abs(V - vin) <= tol_v)
+        P = (L + PAGE - 1) // PAGE
+        used[table[b, :P]] = True
+        tail = L % PAGE
+        if tail:
+            assert not cache.k_pages[table[b, P - 1], :, tail:].any()
+    assert not cache.k_pages[~used].any()
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_incremental_append_equals_prefill(fmt):
+    """Appending in decode-sized steps gives the same cache as one prefill.
+    Per-group storage re-supplies the open group from its first token."""
+    w = workloads.small(5).with_(fmt=fmt, batch=3, len_lo=60, len_hi=200)
+    full, table = oracle.build_cache(w)
+    lens = w.seq_lens()
+    inc = oracle.Cache(w.fmt, full.P_phys, w.num_kv_heads, w.head_dim)
+    cur = np.minimum(lens, 37)
+    ks = [w.keys(b) for b in range(w.batch)]
+    vs = [w.values(b) for b in range(w.batch)]
+    # prefill of the first 37 tokens
+    off = np.concatenate([[0], np.cumsum(cur)]).astype(np.int32)
+    oracle.append(inc, table, np.zeros(w.batch, np.int32), off,
+                  np.concatenate([ks[b][:cur[b]] for b in range(w.batch)]),
+                  np.concatenate([vs[b][:cur[b]] for b in range(w.batch)]))
+    while np.any(cur < lens):
+        nxt = np.minimum(cur + 1, lens)
+        start = (cur // 64) * 64 if fmt == 2 else cur
+        start = np.where(nxt > cur, start, cur)
+        rows_k = [ks[b][start[b]:nxt[b]] for b in range(w.batch)]
+        rows_v = [vs[b][start[b]:nxt[b]] for b in range(w.batch)]
+        cnt = np.array([len(r) for r in rows_k])
+        off = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+        oracle.append(inc, table, start.astype(np.int32), off, np.concatenate(rows_k), np.concatenate(rows_v))
+        cur = nxt
+    assert np.array_equal(inc.k_pages, full.k_pages)
+    assert np.array_equal(inc.v_pages, full.v_pages)
+    assert np.array_equal(inc.params, full.params)
+
+
+# -------------------------------------------------------------- metadata
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_meta_is_min_max_of_decoded_keys(n):
+    """phi(K_j) = per-channel (min, max) over the page's valid keys, as
+    decoded (TinyServe page, section 2.1), brute force with numpy.
+    Catches swapped rows, reading padding slots, wrong token ranges."""
+    w = workloads.small(n)
+    cache, table = oracle.build_cache(w)
+    lens = w.seq_lens()
+    for b in range(w.batch):
+        K, _ = decoded_keys_values(w, cache, table, b)
+        L = int(lens[b])
+        for j in range((L + PAGE - 1) // PAGE):
+            blk = K[j * PAGE: min((j + 1) * PAGE, L)]
+            m = cache.meta[table[b, j], :, 0]
+            M = cache.meta[table[b, j], :, 1]
+            assert np.array_equal(m, blk.min(0)) and np.array_equal(M, blk.max(0))
+
+
+def test_meta_ignores_padding_slots_and_honours_page_begin():
+    """Garbage in the unused slots of a partial last page must not leak into
+    phi; page_begin restricts the rebuild to the tail pages."""
+    w = workloads.small(4).with_(seq_len=40)
+    cache, table = oracle.build_cache(w)
+    ref = cache.meta.copy()
+    last = table[0, 2]
+    cache.k_pages[last, :, 8:] = 255                     # slots 40..47 are padding
+    cache.params[last, :, 8:, 0] = 1e6
+    cache.meta[:] = 0
+    oracle.page_meta(cache, table, w.seq_lens(), page_begin=np.array([2], np.int32))
+    assert np.array_equal(cache.meta[last], ref[last])
+    assert not cache.meta[table[0, :2]].any()
+
+
+# ---------------------------------------------------------------- scores
+def test_score_golden():
+    g = gold("page_score_hand.json")
+    cache = oracle.Cache(workloads.FMT_FP16, 1, 1, 4)
+    table = np.zeros((1, 1), np.int32)
+    keys = np.array(g["keys"], np.float16)[:, None, :]
+    oracle.append(cache, table, [0], [0, 2], keys, keys)
+    oracle.page_meta(cache, table, [2])
+    assert cache.meta[0, 0, 0].tolist() == g["min"] and cache.meta[0, 0, 1].tolist() == g["max"]
+    s = oracle.page_scores(cache, table, [2], np.array(g["q"], np.float16)[None, None])
+    assert s[0, 0, 0] == g["score"]
+
+
+@pytest.mark.parametrize("n", [2, 4, 5])
+def test_score_never_underestimates(n):
+    """r >= max over the page of q.k for every page and query head (TinyServe
+    page, section 2.1).  Catches swapped min/max or a flipped sign test."""
+    w = workloads.small(n)
+    cache, table = oracle.build_cache(w)
+    q = w.query().astype(np.float64)
+    sc = oracle.page_scores(cache, table, w.seq_lens(), w.query())
+    lens = w.seq_lens()
+    G = w.group
+    for b in range(w.batch):
+        K, _ = decoded_keys_values(w, cache, table, b)
+        L = int(lens[b])
+        P = (L + PAGE - 1) // PAGE
+        assert np.all(np.isneginf(sc[b, :, P:]))
+        for h in range(w.num_q_heads):
+            g = h // G
+            dots = K[:, g].astype(np.float64) @ q[b, h]              # [L]
+            for j in range(P):
+                mx = dots[j * PAGE: min((j + 1) * PAGE, L)].max()
+                mm = cache.meta[table[b, j], g].astype(np.float64)
+                slack = 1e-12 * (np.abs(q[b, h]) * np.abs(mm).max(0)).sum()
+                assert sc[b, g, j] >= mx - slack
+
+
+def test_score_exact_cases():
+    """A 1-token page, or a page of identical keys, scores exactly q.k; an
+    all-non-negative q scores q.M, an all-negative q scores q.m.
+    Catches a dropped or duplicated term."""
+    rng = np.random.default_rng(2)
+    d = 64
+    k = rng.standard_normal((17, d)).astype(np.float16)      # page 1 holds a single token
+    k[:16] = k[3]                                            # page 0: 16 identical keys
+    cache, table = one_token_cache(workloads.FMT_FP16, k)
+    oracle.page_meta(cache, table, [17])
+    q = rng.standard_normal(d).astype(np.float16)
+    s = oracle.page_scores(cache, table, [17], q[None, None])[0, 0]
+    kd = k.astype(np.float64)
+    qd = q.astype(np.float64)
+    assert s[0] == pytest.approx(kd[3] @ qd, rel=1e-13, abs=1e-13)
+    assert s[1] == pytest.approx(kd[16] @ qd, rel=1e-13, abs=1e-13)
+    k2 = rng.standard_normal((16, d)).astype(np.float16)
+    cache2, table2 = one_token_cache(workloads.FMT_FP16, k2)
+    oracle.page_meta(cache2, table2, [16])
+    qp = np.abs(q)
+    qn = -np.abs(q)
+    sp = oracle.page_scores(cache2, table2, [16], qp[None, None])[0, 0, 0]
+    sn = oracle.page_scores(cache2, table2, [16], qn[None, None])[0, 0, 0]
+    k2d = k2.astype(np.float64)
+    assert sp == pytest.approx(qp.astype(np.float64) @ k2d.max(0), rel=1e-13)
+    assert sn == pytest.approx(qn.astype(np.float64) @ k2d.min(0), rel=1e-13)
+
+
+def test_gqa_group_score_is_max_over_member_heads():
+    """KV head g serves query heads g*G .. g*G+G-1 and scores with the max of
+    their r.  Catches h % H_kv mapping and sum/first-head aggregation."""
+    w = workloads.small(5).with_(batch=2, len_lo=100, len_hi=130)
+    cache, table = oracle.build_cache(w)
+    q = w.query()
+    G = w.group
+    sc = oracle.page_scores(cache, table, w.seq_lens(), q)
+    for h in range(w.num_q_heads):
+        solo = np.zeros_like(q)
+        solo[:, h] = q[:, h]
+        # a query of zeros scores 0; every other head is silenced
+        per = oracle.page_scores(cache, table, w.seq_lens(), solo)
+        g = h // G
+        for b in range(w.batch):
+            P = (int(w.seq_lens()[b]) + PAGE - 1) // PAGE
+            assert np.all(per[b, g, :P] <= sc[b, g, :P])
+    # the group score equals the max of the single-head scores
+    singles = []
+    for hh in range(G):
+        qq = np.zeros_like(q)
+        for g in range(w.num_kv_heads):
+            qq[:, g * G:(g + 1) * G] = q[:, g * G + hh: g * G + hh + 1]
+        singles.append(oracle.page_scores(cache, table, w.seq_lens(), qq))
+    assert np.array_equal(np.maximum.reduce(singles), sc)
+
+
+# ------------------------------------------------------------------ top-K
+def test_num_selected_golden():
+    g = gold("num_selected.json")
+    rn, rd = g["ratio"]
+    for P, K in g["cases"]:
+        assert oracle.num_selected(P, rn, rd, 0) == K, (P, K)
+    for P, kf, K in g["fixed"]["cases"]:
+        assert oracle.num_selected(P, rn, rd, kf) == K
+    assert oracle.num_selected(37, 1, 1, 0) == 37
+
+
+def test_topk_matches_full_sort_with_ties():
+    """Against numpy lexsort by (-score, page): largest K, ties to the lower
+    logical index, emitted ascending, -1 padded."""
+    rng = np.random.default_rng(4)
+    B, H, maxp = 3, 4, 300
+    lens = np.array([300 * 16, 77 * 16 - 5, 1], np.int32)
+    sc = rng.standard_normal((B, H, maxp))
+    sc[:, :, 50:120] = 0.5                                   # a plateau of equal scores
+    sc[1, 2, :] = 1.0                                        # an all-equal row
+    k_cap = 128
+    sel, cnt = oracle.topk(sc, lens, 3, 10, 0, k_cap)
+    for b in range(B):
+        P = (int(lens[b]) + PAGE - 1) // PAGE
+        K = oracle.num_selected(P, 3, 10, 0)
+        for h in range(H):
+            order = np.lexsort((np.arange(P), -sc[b, h, :P]))
+            want = np.sort(order[:K])
+            assert cnt[b, h] == K
+            assert np.array_equal(sel[b, h, :K], want)
+            assert np.all(sel[b, h, K:] == -1)
+    assert np.array_equal(sel[1, 2, :cnt[1, 2]], np.arange(cnt[1, 2]))
+
+
+def test_topk_all_pages_when_k_equals_p():
+    rng = np.random.default_rng(8)
+    sc = rng.standard_normal((2, 3, 40))
+    lens = np.array([40 * 16, 13 * 16 + 1], np.int32)
+    sel, cnt = oracle.topk(sc, lens, 1, 1, 0, 40)
+    assert cnt.tolist() == [[40] * 3, [14] * 3]
+    assert np.array_equal(sel[0, 0], np.arange(40))
+    assert np.array_equal(sel[1, 1, :14], np.arange(14))
+
+
+# -------------------------------------------------------------- attention
+def test_attention_golden():
+    g = gold("attention_hand.json")
+    cache, table = one_token_cache(workloads.FMT_FP16, g["keys"], g["values"])
+    out = oracle.attention(cache, table, [2], np.array(g["q"], np.float16)[None, None])
+    assert np.allclose(out[0, 0], g["out"], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_dense_selection_equals_textbook_attention(n):
+    """K = P reduces to softmax(q K^T / sqrt(d)) V (intelliparadigm.com page,
+    section 2.1), computed by numpy in fp64 on the unpaged arrays.  Catches a
+    missing 1/sqrt(d), a dropped max-shift or normalizer, a wrong head map."""
+    w = workloads.small(n)
+    cache, table = oracle.build_cache(w)
+    lens = w.seq_lens()
+    q = w.query()
+    maxp = table.shape[1]
+    sc, sel, cnt, out = oracle.decode_step(cache, table, lens, q, 1, 1, 0, maxp)
+    out_null = oracle.attention(cache, table, lens, q)
+    assert np.array_equal(out, out_null)
+    for b in range(w.batch):
+        K, V = decoded_keys_values(w, cache, table, b)
+        for h in range(w.num_q_heads):
+            g = h // w.group
+            ref = dense_attention(q[b, h], K[:, g], V[:, g], 1 / math.sqrt(w.head_dim))
+            assert np.allclose(out[b, h], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [2, 4, 5])
+def test_sparse_attention_equals_dense_over_selected_tokens(n):
+    """With a selection, attention covers exactly the valid tokens of the
+    selected pages (TinyServe page, section 3.1 phase 3), partial last page
+    included."""
+    w = workloads.small(n)
+    cache, table = oracle.build_cache(w)
+    lens = w.seq_lens()
+    q = w.query()
+    k_cap = table.shape[1]
+    sc, sel, cnt, out = oracle.decode_step(cache, table, lens, q, 3, 10, 0, k_cap)
+    for b in range(w.batch):
+        K, V = decoded_keys_values(w, cache, table, b)
+        L = int(lens[b])
+        for h in range(w.num_q_heads):
+            g = h // w.group
+            pages = sel[b, g, :cnt[b, g]]
+            toks = np.concatenate([np.arange(j * PAGE, min((j + 1) * PAGE, L)) for j in pages])
+            ref = dense_attention(q[b, h], K[toks, g], V[toks, g], 1 / math.sqrt(w.head_dim))
+            assert np.allclose(out[b, h], ref, rtol=0, atol=1e-12)
+
+
+def test_attention_special_cases():
+    """L = 1 returns v; q = 0 gives equal logits and the mean of V."""
+    rng = np.random.default_rng(12)
+    k = rng.standard_normal((1, 64)).astype(np.float16)
+    v = rng.standard_normal((1, 64)).astype(np.float16)
+    cache, table = one_token_cache(workloads.FMT_FP16, k, v)
+    out = oracle.attention(cache, table, [1], rng.standard_normal((1, 1, 64)).astype(np.float16))
+    assert np.array_equal(out[0, 0], v[0].astype(np.float64))
+    k = rng.standard_normal((37, 64)).astype(np.float16)
+    v = rng.standard_normal((37, 64)).astype(np.float16)
+    cache, table = one_token_cache(workloads.FMT_FP16, k, v)
+    out = oracle.attention(cache, table, [37], np.zeros((1, 1, 64), np.float16))
+    assert np.allclose(out[0, 0], v.astype(np.float64).mean(0), rtol=0, atol=1e-14)
+
+
+def test_block_table_permutation_does_not_change_results():
+    """Same logical contents through identity and shuffled tables."""
+    w = workloads.small(4)
+    c1, t1 = oracle.build_cache(w.with_(table="identity"))
+    c2, t2 = oracle.build_cache(w)
+    assert not np.array_equal(t1, t2)
+    q = w.query()
+    lens = w.seq_lens()
+    r1 = oracle.decode_step(c1, t1, lens, q, 3, 10, 0, 64)
+    r2 = oracle.decode_step(c2, t2, lens, q, 3, 10, 0, 64)
+    for a, b in zip(r1, r2):
+        assert np.array_equal(a, b)
+
+
+def test_decode_step_threads_agree_and_compose():
+    """The threaded step equals the single-threaded one and the separate stages."""
+    w = workloads.small(5)
+    cache, table = oracle.build_cache(w)
+    lens, q = w.seq_lens(), w.query()
+    a = oracle.decode_step(cache, table, lens, q, 3, 10, 0, 64, nthreads=1)
+    b = oracle.decode_step(cache, table, lens, q, 3, 10, 0, 64, nthreads=4)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    sc = oracle.page_scores(cache, table, lens, q)
+    sel, cnt = oracle.topk(sc, lens, 3, 10, 0, 64)
+    out = oracle.attention(cache, table, lens, q, sel, cnt)
+    assert np.array_equal(sc, a[0]) and np.array_equal(sel, a[1]) and np.array_equal(out, a[3])
+
+
+def test_attention_large_logits_stay_finite():
+    """Logits near 1000 overflow exp() unless the softmax is shifted by its
+    max; the result must still equal the (shift-invariant) textbook value."""
+    rng = np.random.default_rng(13)
+    k = (rng.standard_normal((40, 64)) * 60).astype(np.float16)
+    v = rng.standard_normal((40, 64)).astype(np.float16)
+    q = (rng.standard_normal(64) * 60).astype(np.float16)
+    cache, table = one_token_cache(workloads.FMT_FP16, k, v)
+    out = oracle.attention(cache, table, [40], q[None, None])
+    lg = k.astype(np.float64) @ q.astype(np.float64) / 8.0
+    assert lg.max() > 800
+    ref = dense_attention(q, k, v, 1 / 8.0)
+    assert np.all(np.isfinite(out)) and np.allclose(out[0, 0], ref, rtol=0, atol=1e-12)
