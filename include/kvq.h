@@ -1,0 +1,210 @@
+/*
+ * kvq.h -- C ABI of the MI355X (gfx950) decode-step library for paged,
+ * quantized, query-aware sparse attention (libkvq.so).
+ *
+ * The decode step it implements, cited by page title and section:
+ *   - KV cache in 16-token pages reached through a per-sequence block table
+ *     ("KV-cache layout from the HBM-bandwidth viewpoint", pzsr.cn, section 2
+ *     layout C and section 3 block tables; "TinyServe", lpnh.cn, section 5.1
+ *     page_size 16);
+ *   - storage as fp16, INT8 per token (same pzsr.cn page, section 2: each
+ *     token's vector quantized with its own min/max) or INT8 per 64-token group
+ *     ("Gemini KV cache: FlashAttention-3 adaptation", uyd888.cn, chapter 1);
+ *   - per-page fp32 metadata phi(K_j) = (per-channel min, per-channel max) of
+ *     the page's keys, page score r = sum_i (q_i >= 0 ? q_i M_i : q_i m_i),
+ *     top-K page selection, attention over the selected pages only
+ *     ("TinyServe", sections 2.1, 3.1, 5.1, 5.2);
+ *   - Attention(Q,K,V) = softmax(Q K^T / sqrt(d)) V ("KV-cache optimization and
+ *     memory management", intelliparadigm.com, section 2.1).
+ *
+ * Conventions shared by every entry point:
+ *   - Every array pointer is DEVICE memory owned by the caller, unless a
+ *     comment says otherwise.  The library never allocates or frees memory and
+ *     keeps no state between calls; calls are reentrant.
+ *   - Each call only enqueues kernels on `stream` (a hipStream_t; NULL is the
+ *     default stream) and returns.  Nothing synchronizes.  The caller keeps the
+ *     buffers alive until the stream has drained.
+ *   - Host-checkable arguments are validated before anything is enqueued; a
+ *     rejected call enqueues nothing and returns the status.  A failed launch
+ *     returns KVQ_ERR_HIP.  Contents of device arrays are preconditions, listed
+ *     per call, that the library does not check.
+ *   - Page size is 16 tokens, head_dim is 64 or 128, H_q is a multiple of
+ *     H_kv with group size G = H_q / H_kv in {1, 2, 4, 8}; query head h reads
+ *     KV head h / G.
+ *
+ * Storage layout of one layer's cache (all C-contiguous):
+ *   k_pages, v_pages   [P_phys][H_kv][16][d]  fp16 bits (KVQ_FP16) or uint8 codes
+ *   kv_params          KVQ_INT8_TOKEN  : [P_phys][H_kv][16][4] fp32
+ *                                        (k_scale, k_zero, v_scale, v_zero) per token slot
+ *                      KVQ_INT8_GROUP64: [P_phys][H_kv][4] fp32, the 64-token
+ *                                        group's values repeated in each of its pages
+ *                      KVQ_FP16        : unused (may be NULL)
+ *   page_meta          [P_phys][H_kv][2][d] fp32: row 0 per-channel min, row 1 max
+ * A stored key or value decodes to fmaf(code, scale, zero) (INT8) or to the
+ * fp16 value (FP16).  Codes are unsigned 0..255 with zero = the quantized
+ * row's minimum and scale = (max - min) / 255; a constant row has scale 1.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+#define KVQ_PAGE_SIZE 16
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent shape */
+    KVQ_ERR_UNSUPPORTED = 2,   /* page size, head_dim, group size or row length not built */
+    KVQ_ERR_WORKSPACE = 3,     /* workspace missing or smaller than kvq_attn_workspace_bytes() */
+    KVQ_ERR_HIP = 4            /* a HIP launch failed */
+} kvq_status;
+
+typedef enum {
+    KVQ_FP16 = 0,
+    KVQ_INT8_TOKEN = 1,
+    KVQ_INT8_GROUP64 = 2
+} kvq_format;
+
+/* Non-owning view of one layer's paged cache (host struct, device pointers). */
+typedef struct {
+    int32_t format;            /* kvq_format */
+    int32_t num_phys_pages;    /* P_phys */
+    int32_t page_size;         /* must be 16 */
+    int32_t num_kv_heads;      /* H_kv */
+    int32_t head_dim;          /* d: 64 or 128 */
+    void *k_pages;
+    void *v_pages;
+    float *kv_params;
+    float *page_meta;
+} kvq_cache;
+
+/* The batch of sequences (host struct, device pointers). */
+typedef struct {
+    int32_t batch;                 /* B >= 1 */
+    int32_t max_pages;             /* block-table row stride, >= ceil(L_b / 16) for every b */
+    const int32_t *seq_lens;       /* [B] tokens in each sequence, 1 <= L_b <= 16 * max_pages */
+    const int32_t *block_table;    /* [B][max_pages] physical page of each logical page;
+                                      entries j < ceil(L_b/16) lie in [0, P_phys) */
+} kvq_seqs;
+
+/*
+ * kvq_append_quant -- write new tokens into their paged slots.
+ * (pzsr.cn layout page, sections 2-3: token t of sequence b goes to physical
+ * page block_table[b][t/16], slot t%16; per-token INT8 from the token's own
+ * min/max.  uyd888.cn Gemini page, chapter 1: 64 tokens share one
+ * scale/zero-point.)
+ *
+ * Sequence b receives rows new_off[b] .. new_off[b+1]-1 of k_new / v_new
+ * (fp16 bits, [N][H_kv][d]) at logical positions start_pos[b], start_pos[b]+1, ...
+ *   KVQ_FP16        : the rows are copied.
+ *   KVQ_INT8_TOKEN  : every (token, KV head) row of d values, K and V apart,
+ *                     is quantized with its own (scale, zero).
+ *   KVQ_INT8_GROUP64: every (64-token group aligned to logical position 64g,
+ *                     KV head), K and V apart, shares one (scale, zero) over
+ *                     the group's rows in this call; start_pos[b] must be a
+ *                     multiple of 64 whenever sequence b receives rows, and the
+ *                     rows must hold every token of each group they touch
+ *                     (an open group is re-supplied whole and re-quantized).
+ * Quantization arithmetic is IEEE fp32 with round-to-nearest-even, no fused
+ * operations: range = max - min, scale = range / 255, inv = 1 / scale,
+ * code = clamp(rint((x - zero) * inv), 0, 255).
+ *
+ * seqs->seq_lens is not read.  max_new (host) is an upper bound on the rows
+ * of any one sequence; it sizes the grid.  Rows beyond it are not written.
+ * Preconditions: new_off non-decreasing from 0; block-table entries of every
+ * written page valid.
+ */
+kvq_status kvq_append_quant(const kvq_cache *cache, const kvq_seqs *seqs,
+                            const int32_t *start_pos, const int32_t *new_off, int32_t max_new,
+                            const uint16_t *k_new, const uint16_t *v_new, void *stream);
+
+/*
+ * kvq_build_page_meta -- per (logical page j, KV head) of each sequence, for
+ * page_begin[b] <= j < ceil(L_b/16): page_meta[block_table[b][j]][h] = the
+ * per-channel min and max over the page's valid tokens (t < L_b) of the keys
+ * as decoded ("TinyServe", section 2.1 direction-aware bounding box; section
+ * 5.2 fp32 metadata).  Results are exact (min/max of fmaf-decoded values).
+ * page_begin NULL means 0.  max_span (host, > 0) is the expected number of
+ * pages per sequence and only sizes the grid; 0 means max_pages.
+ */
+kvq_status kvq_build_page_meta(const kvq_cache *cache, const kvq_seqs *seqs,
+                               const int32_t *page_begin, int32_t max_span, void *stream);
+
+/*
+ * kvq_page_scores -- page relevance of every logical page ("TinyServe",
+ * section 2.1): r(q, phi) = sum_i (q_i >= 0 ? q_i M_i : q_i m_i) with q the
+ * unscaled fp16 query, summed in fp32.  The KV group's score is the max over
+ * its G query heads.
+ *   q      : [B][H_q][d] fp16 bits
+ *   scores : [B][H_kv][max_pages] fp32 out; pages j >= ceil(L_b/16) get -inf.
+ * Reads page_meta through the block table; page_meta must be current.
+ */
+kvq_status kvq_page_scores(const kvq_cache *cache, const kvq_seqs *seqs,
+                           const uint16_t *q, int32_t num_q_heads, float *scores, void *stream);
+
+/*
+ * kvq_topk_pages -- per (sequence b, KV head) row of `scores`, select K_b of
+ * the P_b = ceil(L_b/16) pages ("TinyServe", section 3.1 phase 2; section 5.1
+ * selection_ratio):
+ *   K_b = min(P_b, k_fixed) if k_fixed > 0, else
+ *   K_b = clamp(ceil(ratio_num * P_b / ratio_den), 1, P_b) in integers.
+ * The K_b largest scores win; equal scores go to the lower logical page.
+ * -0.0 and +0.0 compare equal.  Scores must not be NaN.
+ *   sel_pages : [B][H_kv][k_cap] int32 out: selected logical pages, ascending,
+ *               then -1 up to k_cap.
+ *   sel_count : [B][H_kv] int32 out: K_b.
+ * k_cap must be >= K for P = max_pages (else KVQ_ERR_INVALID_ARG), and
+ * max_pages <= 15360 (else KVQ_ERR_UNSUPPORTED).
+ */
+kvq_status kvq_topk_pages(const float *scores, const kvq_seqs *seqs, int32_t num_kv_heads,
+                          int32_t ratio_num, int32_t ratio_den, int32_t k_fixed, int32_t k_cap,
+                          int32_t *sel_pages, int32_t *sel_count, void *stream);
+
+/*
+ * kvq_sparse_decode_attn -- single-token attention of every query head over
+ * the valid tokens of the selected pages of its KV head ("TinyServe", section
+ * 3.1 phases 3-4; intelliparadigm.com, section 2.1):
+ *   out[b][h] = sum_t softmax_t(sm_scale * q.k_t) v_t
+ * over t in the pages sel_pages[b][h/G][0 .. sel_count[b][h/G]) (logical page
+ * ids, any order, no repeats), or over every page when sel_pages is NULL
+ * (sel_count is then ignored).  Computed split-K: each split of
+ * pages_per_split selected pages keeps an online (max, sum, acc) in fp32, and
+ * a second kernel merges the splits with log-sum-exp weights.
+ *   q   : [B][H_q][d] fp16 bits
+ *   out : [B][H_q][d] fp32
+ *   ws  : workspace of at least kvq_attn_workspace_bytes(...) bytes (the
+ *         per-split partial results); ws_bytes is its size.
+ * pages_per_split 0 picks a default; otherwise 1..4096.  k_cap is the row
+ * stride of sel_pages and bounds sel_count (ignored when sel_pages is NULL).
+ */
+kvq_status kvq_sparse_decode_attn(const kvq_cache *cache, const kvq_seqs *seqs,
+                                  const uint16_t *q, int32_t num_q_heads,
+                                  const int32_t *sel_pages, const int32_t *sel_count, int32_t k_cap,
+                                  float sm_scale, int32_t pages_per_split,
+                                  float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes kvq_sparse_decode_attn needs for these sizes; k_cap 0
+ * means every page (sel_pages NULL).  Returns 0 for invalid sizes. */
+size_t kvq_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_pages, int32_t k_cap, int32_t pages_per_split);
+
+/* The pages_per_split kvq_sparse_decode_attn uses when given 0. */
+int32_t kvq_default_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t max_pages, int32_t k_cap);
+
+/* Static description of a status code (never NULL). */
+const char *kvq_status_string(kvq_status status);
+
+/* KVQ_ABI_VERSION of the built library. */
+int32_t kvq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,106 @@
+// kvq_device.h -- device helpers shared by the gfx950 kernels of libkvq.
+//
+// Wave64 reductions use DPP row operations inside a row of 16 lanes and
+// ds_bpermute (__shfl_xor) across rows.  All helpers are all-reduce: every
+// participating lane ends with the result.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kPage = 16;
+constexpr int kWave = 64;
+
+enum Format : int { kFp16 = 0, kInt8Token = 1, kInt8Group = 2 };
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// Lanes' DPP controls (row = 16 lanes).
+enum : int {
+  kDppXor1 = 0xB1,         // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,         // quad_perm [2,3,0,1]
+  kDppHalfMirror = 0x141,  // lane i <-> 7-i within each 8 lanes
+  kDppMirror = 0x140,      // lane i <-> 15-i within each 16 lanes
+  kDppRor4 = 0x124,        // row rotate right by 4
+  kDppRor8 = 0x128,        // row rotate right by 8
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, kWave); }
+
+// Sum over aligned blocks of W consecutive lanes (W = 1, 2, 4, 8, 16, 32, 64).
+template <int W>
+__device__ __forceinline__ float sum_contig(float x) {
+  if constexpr (W >= 2) x += dpp<kDppXor1>(x);
+  if constexpr (W >= 4) x += dpp<kDppXor2>(x);
+  if constexpr (W >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (W >= 16) x += dpp<kDppMirror>(x);
+  if constexpr (W >= 32) x += shfl_xor(x, 16);
+  if constexpr (W >= 64) x += shfl_xor(x, 32);
+  return x;
+}
+
+template <int W>
+__device__ __forceinline__ float max_contig(float x) {
+  if constexpr (W >= 2) x = fmaxf(x, dpp<kDppXor1>(x));
+  if constexpr (W >= 4) x = fmaxf(x, dpp<kDppXor2>(x));
+  if constexpr (W >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  if constexpr (W >= 16) x = fmaxf(x, dpp<kDppMirror>(x));
+  if constexpr (W >= 32) x = fmaxf(x, shfl_xor(x, 16));
+  if constexpr (W >= 64) x = fmaxf(x, shfl_xor(x, 32));
+  return x;
+}
+
+template <int W>
+__device__ __forceinline__ float min_contig(float x) {
+  if constexpr (W >= 2) x = fminf(x, dpp<kDppXor1>(x));
+  if constexpr (W >= 4) x = fminf(x, dpp<kDppXor2>(x));
+  if constexpr (W >= 8) x = fminf(x, dpp<kDppHalfMirror>(x));
+  if constexpr (W >= 16) x = fminf(x, dpp<kDppMirror>(x));
+  if constexpr (W >= 32) x = fminf(x, shfl_xor(x, 16));
+  if constexpr (W >= 64) x = fminf(x, shfl_xor(x, 32));
+  return x;
+}
+
+// Sum over the lanes congruent modulo S (S = 1, 2, 4, 8, 16, 32, 64): the
+// 64/S lanes l, l+S, l+2S, ... all end with their total.
+template <int S>
+__device__ __forceinline__ float sum_strided(float x) {
+  static_assert(S >= 4 && S <= 64, "strides 4..64");
+  if constexpr (S <= 4) x += dpp<kDppRor4>(x);
+  if constexpr (S <= 8) x += dpp<kDppRor8>(x);
+  if constexpr (S <= 16) x += shfl_xor(x, 16);
+  if constexpr (S <= 32) x += shfl_xor(x, 32);
+  return x;
+}
+
+// Order-preserving map fp32 -> uint32 (larger float, larger key); -0 == +0.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Number of pages selected from P by the ratio / fixed count (integers only).
+__host__ __device__ __forceinline__ int num_selected(int P, int rnum, int rden, int k_fixed) {
+  if (P <= 0) return 0;
+  long long k = k_fixed > 0 ? (long long)k_fixed : ((long long)rnum * P + rden - 1) / rden;
+  if (k < 1) k = 1;
+  if (k > P) k = P;
+  return (int)k;
+}
+
+}  // namespace kvq

@@ -1,0 +1,32 @@
+// kvq_internal.h -- launchers behind the C ABI of libkvq (host side).
+// Each launcher assumes its arguments were validated by kvq_api.hip and
+// returns the HIP error of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+hipError_t launch_append(const kvq_cache& c, const kvq_seqs& s, const int32_t* start_pos,
+                         const int32_t* new_off, int max_new, const uint16_t* k_new,
+                         const uint16_t* v_new, hipStream_t st);
+
+hipError_t launch_page_meta(const kvq_cache& c, const kvq_seqs& s, const int32_t* page_begin,
+                            int max_span, hipStream_t st);
+
+hipError_t launch_page_scores(const kvq_cache& c, const kvq_seqs& s, const uint16_t* q, int num_q_heads,
+                              float* scores, hipStream_t st);
+
+constexpr int kTopkMaxPages = 15360;
+hipError_t launch_topk(const float* scores, const kvq_seqs& s, int num_kv_heads, int rnum, int rden,
+                       int k_fixed, int k_cap, int32_t* sel_pages, int32_t* sel_count, hipStream_t st);
+
+hipError_t launch_decode_attn(const kvq_cache& c, const kvq_seqs& s, const uint16_t* q, int num_q_heads,
+                              const int32_t* sel_pages, const int32_t* sel_count, int k_cap, float sm_scale,
+                              int pages_per_split, int max_splits, float* out, void* ws, hipStream_t st);
+
+}  // namespace kvq

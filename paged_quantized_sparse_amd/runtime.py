@@ -1,0 +1,148 @@
+"""Caller-side plumbing around libkvq: device buffers for one decode step and
+a cache builder.  Every computation is a libkvq call; this module only
+allocates torch tensors, uploads caller data and sequences the calls.
+
+A decode step, as the TinyServe page (lpnh.cn, section 3.1) orders it:
+  append the new token (and re-quantize its open group) -> refresh the
+  metadata of the pages that changed -> score every page -> top-K ->
+  attention over the selected pages (split-K + combine).
+"""
+from __future__ import annotations
+
+from typing import Callable
+
+import numpy as np
+import torch
+
+from . import (KVQ_FP16, KVQ_INT8_GROUP64, PAGE_SIZE, PagedCache, Seqs, kvq_append_quant,
+               kvq_attn_workspace_bytes, kvq_build_page_meta, kvq_default_pages_per_split, kvq_page_scores,
+               kvq_sparse_decode_attn, kvq_topk_pages, num_selected)
+
+KVSource = Callable[[int], "tuple[np.ndarray, np.ndarray]"]  # b -> (K [L][H][d], V [L][H][d]) fp16
+
+
+def _dev_i32(x, device) -> torch.Tensor:
+    return torch.as_tensor(np.ascontiguousarray(x, np.int32)).to(device)
+
+
+def append_rows(cache: PagedCache, seqs: Seqs, rows: dict[int, tuple[int, np.ndarray, np.ndarray]],
+                device="cuda") -> None:
+    """Append rows[b] = (start_pos, K rows, V rows) for the listed sequences
+    with one kvq_append_quant call; other sequences receive nothing."""
+    B = seqs.batch
+    start = np.zeros(B, np.int32)
+    cnt = np.zeros(B, np.int64)
+    ks, vs = [], []
+    for b in range(B):
+        if b in rows:
+            s, k, v = rows[b]
+            start[b] = s
+            cnt[b] = k.shape[0]
+            ks.append(k)
+            vs.append(v)
+    off = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+    if not ks or off[-1] == 0:
+        return
+    k_new = torch.from_numpy(np.ascontiguousarray(np.concatenate(ks)).view(np.int16)).to(device)
+    v_new = torch.from_numpy(np.ascontiguousarray(np.concatenate(vs)).view(np.int16)).to(device)
+    kvq_append_quant(cache, seqs, _dev_i32(start, device), _dev_i32(off, device), int(cnt.max()), k_new, v_new)
+
+
+def build_cache(fmt: int, num_phys_pages: int, num_kv_heads: int, head_dim: int, block_table: np.ndarray,
+                seq_lens: np.ndarray, source: KVSource, prefill_lens: np.ndarray | None = None,
+                device="cuda", rows_per_call: int = 1 << 20) -> tuple[PagedCache, Seqs]:
+    """Allocate a cache and prefill sequence b with its first prefill_lens[b]
+    tokens (default: all) from source(b), then build every page's metadata.
+    Uploads are batched to about rows_per_call tokens per append call."""
+    cache = PagedCache.empty(fmt, num_phys_pages, num_kv_heads, head_dim, device)
+    seqs = Seqs(_dev_i32(seq_lens, device), _dev_i32(block_table, device))
+    pre = np.asarray(seq_lens if prefill_lens is None else prefill_lens, np.int64)
+    batch: dict[int, tuple[int, np.ndarray, np.ndarray]] = {}
+    rows = 0
+    for b in range(len(pre)):
+        if pre[b] == 0:
+            continue
+        k, v = source(b)
+        batch[b] = (0, k[: pre[b]], v[: pre[b]])
+        rows += int(pre[b])
+        if rows >= rows_per_call:
+            append_rows(cache, seqs, batch, device)
+            torch.cuda.current_stream().synchronize()
+            batch, rows = {}, 0
+    append_rows(cache, seqs, batch, device)
+    # metadata over the prefilled tokens, then the real lengths are installed
+    pre_seqs = Seqs(_dev_i32(pre, device), seqs.block_table)
+    kvq_build_page_meta(cache, pre_seqs)
+    torch.cuda.current_stream().synchronize()
+    return cache, seqs
+
+
+class DecodeAppend:
+    """Device buffers to append each sequence's newest token at position
+    L_b - 1 (INT8_GROUP64: re-supply its open 64-token group) and refresh the
+    metadata of the pages it touched."""
+
+    def __init__(self, cache: PagedCache, seqs: Seqs, seq_lens: np.ndarray, source_rows: KVSource,
+                 device="cuda"):
+        self.cache, self.seqs = cache, seqs
+        lens = np.asarray(seq_lens, np.int64)
+        last = lens - 1
+        if cache.format == KVQ_INT8_GROUP64:
+            start = (last // 64) * 64
+        else:
+            start = last
+        ks, vs = [], []
+        for b in range(len(lens)):
+            k, v = source_rows(b)
+            ks.append(k[start[b]: lens[b]])
+            vs.append(v[start[b]: lens[b]])
+        cnt = lens - start
+        self.max_new = int(cnt.max())
+        self.start = _dev_i32(start, device)
+        self.off = _dev_i32(np.concatenate([[0], np.cumsum(cnt)]), device)
+        self.k_new = torch.from_numpy(np.ascontiguousarray(np.concatenate(ks)).view(np.int16)).to(device)
+        self.v_new = torch.from_numpy(np.ascontiguousarray(np.concatenate(vs)).view(np.int16)).to(device)
+        self.page_begin = _dev_i32(start // PAGE_SIZE, device)
+        self.span = int(((lens - 1) // PAGE_SIZE - start // PAGE_SIZE).max()) + 1
+
+    def run(self, stream=None) -> None:
+        kvq_append_quant(self.cache, self.seqs, self.start, self.off, self.max_new, self.k_new, self.v_new, stream)
+        kvq_build_page_meta(self.cache, self.seqs, self.page_begin, self.span, stream)
+
+
+class DecodeStep:
+    """Device buffers for score -> top-K -> sparse attention of one step.
+    dense=True skips scoring and selection and attends to every page."""
+
+    def __init__(self, cache: PagedCache, seqs: Seqs, num_q_heads: int, ratio_num: int, ratio_den: int,
+                 k_fixed: int, dense: bool = False, pages_per_split: int = 0, device="cuda"):
+        self.cache, self.seqs, self.Hq = cache, seqs, num_q_heads
+        self.ratio = (ratio_num, ratio_den, k_fixed)
+        self.dense = dense
+        B, H, d, maxp = seqs.batch, cache.num_kv_heads, cache.head_dim, seqs.max_pages
+        self.k_cap = 0 if dense else num_selected(maxp, ratio_num, ratio_den, k_fixed)
+        self.pps = pages_per_split or kvq_default_pages_per_split(B, H, maxp, self.k_cap)
+        self.scores = torch.empty((B, H, maxp), dtype=torch.float32, device=device)
+        self.sel_pages = torch.empty((B, H, max(self.k_cap, 1)), dtype=torch.int32, device=device)
+        self.sel_count = torch.empty((B, H), dtype=torch.int32, device=device)
+        self.out = torch.empty((B, num_q_heads, d), dtype=torch.float32, device=device)
+        nbytes = kvq_attn_workspace_bytes(B, num_q_heads, d, maxp, self.k_cap, self.pps)
+        self.workspace = torch.empty((nbytes + 255) // 4, dtype=torch.float32, device=device)
+        self.sm_scale = 1.0 / float(np.sqrt(d))
+
+    def select(self, q, stream=None) -> None:
+        kvq_page_scores(self.cache, self.seqs, q, self.scores, stream)
+        rn, rd, kf = self.ratio
+        kvq_topk_pages(self.scores, self.seqs, self.cache.num_kv_heads, rn, rd, kf, self.sel_pages,
+                       self.sel_count, stream)
+
+    def attend(self, q, sel_pages=None, sel_count=None, stream=None) -> torch.Tensor:
+        kvq_sparse_decode_attn(self.cache, self.seqs, q, sel_pages, sel_count, self.out, self.workspace,
+                               self.sm_scale, self.pps, stream)
+        return self.out
+
+    def run(self, q, stream=None) -> torch.Tensor:
+        if self.dense:
+            return self.attend(q, None, None, stream)
+        self.select(q, stream)
+        return self.attend(q, self.sel_pages, self.sel_count, stream)

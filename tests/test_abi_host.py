@@ -1,0 +1,141 @@
+"""Host-only checks of libkvq's C ABI: the library loads, exports every
+function include/kvq.h declares, sizes workspaces, and rejects bad arguments
+with the documented status before touching the GPU.  No kernel runs here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+LIB = os.path.join(ROOT, "paged_quantized_sparse_amd", "libkvq.so")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every case below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kvq_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libkvq.so not built")
+    import paged_quantized_sparse_amd as kvq
+    return kvq.lib()
+
+
+def test_header_declares_the_five_decode_step_calls():
+    names = declared_functions()
+    for f in ("kvq_append_quant", "kvq_build_page_meta", "kvq_page_scores", "kvq_topk_pages",
+              "kvq_sparse_decode_attn"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for f in names:
+        assert hasattr(lib, f), f
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (kvq_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_library_never_allocates_or_synchronizes():
+    """The ABI promises no allocation and no synchronization: the library
+    imports no HIP allocator, free or device/stream synchronize."""
+    if not os.path.exists(LIB):
+        pytest.skip("libkvq.so not built")
+    out = subprocess.run(["nm", "-D", "--undefined-only", LIB], capture_output=True, text=True, check=True).stdout
+    banned = re.compile(r"\b(hipMalloc\w*|hipFree\w*|hipHostMalloc|hipDeviceSynchronize|hipStreamSynchronize|"
+                        r"hipMemcpy\b|hipMemset\b|hipExtMallocWithFlags|hipMallocAsync)\b")
+    assert not banned.findall(out), banned.findall(out)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kvq_abi_version() == 1
+    assert "#define KVQ_ABI_VERSION 1" in open(HEADER).read()
+    for s, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP"), (99, b"unknown")]:
+        assert word in lib.kvq_status_string(s)
+
+
+def test_workspace_bytes(lib):
+    # B * Hq * ceil(cap / pps) * (d + 2) * 4
+    assert lib.kvq_attn_workspace_bytes(1, 32, 128, 2048, 615, 16) == 1 * 32 * 39 * 130 * 4
+    assert lib.kvq_attn_workspace_bytes(4, 32, 128, 128, 0, 8) == 4 * 32 * 16 * 130 * 4
+    assert lib.kvq_attn_workspace_bytes(0, 32, 128, 128, 0, 8) == 0
+    assert lib.kvq_attn_workspace_bytes(1, 32, 128, 128, 0, 0) == 0
+    pps = lib.kvq_default_pages_per_split(1, 32, 2048, 615)
+    assert 8 <= pps <= 64 and pps % 4 == 0
+
+
+def _structs(fmt=1, page=16, d=128, H=4, B=1, maxp=8, meta=True):
+    import paged_quantized_sparse_amd as kvq
+    c = kvq.CacheStruct(fmt, 64, page, H, d, FAKE, FAKE, FAKE, FAKE if meta else None)
+    s = kvq.SeqsStruct(B, maxp, FAKE, FAKE)
+    return c, s
+
+
+def _attn(lib, c, s, hq=4, sel=FAKE, cnt=FAKE, k_cap=3, pps=8, ws=FAKE, ws_bytes=1 << 30, q=FAKE, scale=0.1):
+    return lib.kvq_sparse_decode_attn(ctypes.byref(c), ctypes.byref(s), q, hq, sel, cnt, k_cap, scale, pps, FAKE,
+                                      ws, ws_bytes, None)
+
+
+def test_attention_argument_errors(lib):
+    c, s = _structs()
+    assert lib.kvq_sparse_decode_attn(None, ctypes.byref(s), FAKE, 4, None, None, 0, 0.1, 8, FAKE, FAKE, 1 << 20,
+                                      None) == INVALID
+    assert _attn(lib, c, s, hq=6) == INVALID                 # H_q not a multiple of H_kv
+    assert _attn(lib, c, s, hq=12) == UNSUPPORTED            # group size 3
+    assert _attn(lib, c, s, cnt=None) == INVALID             # selection without counts
+    assert _attn(lib, c, s, k_cap=0) == INVALID
+    assert _attn(lib, c, s, pps=5000) == INVALID
+    assert _attn(lib, c, s, q=FAKE + 2) == INVALID           # misaligned query
+    assert _attn(lib, c, s, ws=None) == WORKSPACE
+    assert _attn(lib, c, s, ws_bytes=16) == WORKSPACE
+    assert _attn(lib, c, s, scale=float("nan")) == INVALID
+    c2, s2 = _structs(page=8)
+    assert _attn(lib, c2, s2) == UNSUPPORTED
+    c3, s3 = _structs(d=96)
+    assert _attn(lib, c3, s3) == UNSUPPORTED
+    c4, s4 = _structs(fmt=7)
+    assert _attn(lib, c4, s4) == UNSUPPORTED
+    c5, s5 = _structs(B=0)
+    assert _attn(lib, c5, s5) == INVALID
+
+
+def test_stage_argument_errors(lib):
+    c, s = _structs()
+    # append: null offsets, negative max_new, missing rows
+    assert lib.kvq_append_quant(ctypes.byref(c), ctypes.byref(s), None, FAKE, 1, FAKE, FAKE, None) == INVALID
+    assert lib.kvq_append_quant(ctypes.byref(c), ctypes.byref(s), FAKE, FAKE, -1, FAKE, FAKE, None) == INVALID
+    assert lib.kvq_append_quant(ctypes.byref(c), ctypes.byref(s), FAKE, FAKE, 4, None, FAKE, None) == INVALID
+    c_nop, _ = _structs()
+    c_nop.kv_params = None
+    assert lib.kvq_append_quant(ctypes.byref(c_nop), ctypes.byref(s), FAKE, FAKE, 1, FAKE, FAKE, None) == INVALID
+    # metadata needs the metadata array
+    cm, sm = _structs(meta=False)
+    assert lib.kvq_build_page_meta(ctypes.byref(cm), ctypes.byref(sm), None, 0, None) == INVALID
+    assert lib.kvq_build_page_meta(ctypes.byref(c), ctypes.byref(s), None, -1, None) == INVALID
+    # scores
+    assert lib.kvq_page_scores(ctypes.byref(c), ctypes.byref(s), FAKE, 5, FAKE, None) == INVALID
+    assert lib.kvq_page_scores(ctypes.byref(c), ctypes.byref(s), None, 4, FAKE, None) == INVALID
+    # top-K: k_cap below K(max_pages), bad ratio, over-long rows
+    assert lib.kvq_topk_pages(FAKE, ctypes.byref(s), 4, 3, 10, 0, 2, FAKE, FAKE, None) == INVALID   # K(8) = 3
+    assert lib.kvq_topk_pages(FAKE, ctypes.byref(s), 4, 0, 10, 0, 8, FAKE, FAKE, None) == INVALID
+    assert lib.kvq_topk_pages(FAKE, ctypes.byref(s), 4, 3, 10, -1, 8, FAKE, FAKE, None) == INVALID
+    _, s_long = _structs(maxp=20000)
+    assert lib.kvq_topk_pages(FAKE, ctypes.byref(s_long), 4, 3, 10, 0, 8000, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import paged_quantized_sparse_amd as kvq
+    monkeypatch.setattr(kvq, "_lib", None)
+    monkeypatch.setattr(kvq, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="libkvq.so not found"):
+        kvq.lib()

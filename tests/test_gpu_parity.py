@@ -1,0 +1,349 @@
+"""GPU parity of every libkvq stage against the CPU oracle, through the C ABI.
+
+Bars (the decode-step contract):
+  * INT8 codes, their fp32 (scale, zero) and the fp32 page metadata: bit-exact
+    (metadata compares +0 == -0);
+  * page scores: |gpu - oracle| <= 1e-4 |oracle|, or, where the sum cancels
+    (|oracle| < 1e-2 S), <= 1e-4 S with S = sum_i |q_i c_i| over the terms the
+    score picks;
+  * top-K fed identical fp32 scores: identical selections (index work);
+    fed its own scores: identical except pages whose oracle score lies within
+    1e-4 (relative) of the oracle's K-th score;
+  * attention: max abs error <= 2e-3 against fp64 (unit-variance V).
+Each stage is fed the oracle's inputs for that stage; the end-to-end test runs
+the GPU pipeline alone and checks its output against the oracle evaluated on
+the selection the GPU made, once that selection passes the near-tie rule.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import PAGE
+
+pytestmark = pytest.mark.gpu
+
+SCORE_RTOL = 1e-4
+ATTN_ATOL = 2e-3
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_quantized_sparse_amd as kvq
+    kvq.lib()  # raises if the HIP library is missing
+
+
+def kvq_mod():
+    import paged_quantized_sparse_amd as kvq
+    from paged_quantized_sparse_amd import runtime
+    return kvq, runtime
+
+
+# --------------------------------------------------------------- builders
+class Built:
+    """A workload built on the GPU (prefill of L-1 tokens, then the decode-time
+    append of the last token) and by the oracle (one prefill)."""
+
+    def __init__(self, w, with_oracle=True):
+        kvq, runtime = kvq_mod()
+        self.w = w
+        self.table, self.n_phys = w.block_table()
+        self.lens = w.seq_lens()
+        src = lambda b: (w.keys(b), w.values(b))  # noqa: E731
+        log(f"[build] {w.name} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
+            f"fmt={workloads.FORMAT_NAMES[w.fmt]} pages={self.n_phys}")
+        self.cache, self.seqs = runtime.build_cache(w.fmt, self.n_phys, w.num_kv_heads, w.head_dim, self.table,
+                                                    self.lens, src, prefill_lens=self.lens - 1)
+        runtime.DecodeAppend(self.cache, self.seqs, self.lens, src).run()
+        torch.cuda.synchronize()
+        self.q = w.query()
+        self.q_dev = torch.from_numpy(self.q.view(np.int16)).cuda()
+        self.ocache = oracle.build_cache(w)[0] if with_oracle else None
+
+    def step(self, **kw):
+        _, runtime = kvq_mod()
+        w = self.w
+        return runtime.DecodeStep(self.cache, self.seqs, w.num_q_heads, w.ratio_num, w.ratio_den, w.k_fixed, **kw)
+
+
+_BUILT = {}
+
+
+def built(key, w):
+    if key not in _BUILT:
+        _BUILT[key] = Built(w)
+    return _BUILT[key]
+
+
+SMALL = [1, 2, 3, 4, 5]
+FULL = [1, 2, 3, 4]
+
+
+def workload(kind, n):
+    return workloads.small(n) if kind == "small" else workloads.config(n)
+
+
+CASES = [("small", n) for n in SMALL] + [("full", n) for n in FULL]
+IDS = [f"{k}{n}" for k, n in CASES]
+
+
+# ------------------------------------------------------------ comparisons
+def score_tolerance(ocache, table, lens, q, G):
+    """Per (b, g, j): max(1e-4 |r|, 1e-4 S) where S = sum_i |q_i c_i| when
+    |r| < 1e-2 S (cancellation); c_i is the M_i or m_i term the score picks."""
+    B, Hq, d = q.shape
+    H = Hq // G
+    maxp = table.shape[1]
+    S = np.zeros((B, H, maxp))
+    qd = q.astype(np.float64)
+    for b in range(B):
+        P = (int(lens[b]) + PAGE - 1) // PAGE
+        meta = ocache.meta[table[b, :P]].astype(np.float64)       # [P][H][2][d]
+        for h in range(Hq):
+            g = h // G
+            c = np.where(qd[b, h] >= 0, meta[:, g, 1], meta[:, g, 0])   # [P][d]
+            S[b, g, :P] = np.maximum(S[b, g, :P], np.abs(c * qd[b, h]).sum(1))
+    return S
+
+
+def check_scores(got, want, S):
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isneginf(got), np.isneginf(want))
+    err = np.abs(got[fin].astype(np.float64) - want[fin])
+    r = np.abs(want[fin])
+    tol = np.where(r < 1e-2 * S[fin], SCORE_RTOL * S[fin], SCORE_RTOL * r)
+    bad = err > tol
+    assert not bad.any(), f"{bad.sum()} scores off, worst rel {np.max(err / np.maximum(r, 1e-30)):.3g}"
+
+
+def check_selection_near_ties(sel_gpu, cnt_gpu, oscores, osel, ocnt):
+    """Sets equal except pages whose oracle score is within 1e-4 of the K-th."""
+    B, H, _ = osel.shape
+    n_tie = 0
+    for b in range(B):
+        for g in range(H):
+            K = int(ocnt[b, g])
+            assert int(cnt_gpu[b, g]) == K
+            a = set(sel_gpu[b, g, :K].tolist())
+            o = set(osel[b, g, :K].tolist())
+            assert len(a) == K
+            assert np.all(np.diff(sel_gpu[b, g, :K]) > 0), "selection not ascending"
+            assert np.all(sel_gpu[b, g, K:] == -1)
+            diff = a ^ o
+            if diff:
+                row = oscores[b, g]
+                kth = np.sort(row[np.isfinite(row)])[::-1][K - 1]
+                for j in diff:
+                    assert abs(row[j] - kth) <= SCORE_RTOL * abs(kth), (b, g, j, row[j], kth)
+                n_tie += len(diff)
+    return n_tie
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+# ------------------------------------------------------------------ tests
+@pytest.mark.parametrize("kind,n", CASES, ids=IDS)
+def test_append_codes_params_and_meta_bit_exact(kind, n):
+    bt = built((kind, n), workload(kind, n))
+    oc = bt.ocache
+    k = to_np(bt.cache.k_pages)
+    v = to_np(bt.cache.v_pages)
+    if bt.w.fmt == workloads.FMT_FP16:
+        k, v = k.view(np.uint16), v.view(np.uint16)
+    assert np.array_equal(k, oc.k_pages), "K storage differs"
+    assert np.array_equal(v, oc.v_pages), "V storage differs"
+    if bt.w.fmt != workloads.FMT_FP16:
+        p = to_np(bt.cache.kv_params)
+        assert np.array_equal(p.view(np.uint32), oc.params.view(np.uint32)), "scale/zero bits differ"
+    meta = to_np(bt.cache.page_meta)
+    assert np.array_equal(meta, oc.meta), "page metadata differs"   # == treats +0 and -0 alike
+
+
+@pytest.mark.parametrize("kind,n", CASES, ids=IDS)
+def test_page_scores(kind, n):
+    kvq, _ = kvq_mod()
+    bt = built((kind, n), workload(kind, n))
+    st = bt.step()
+    kvq.kvq_page_scores(bt.cache, bt.seqs, bt.q_dev, st.scores)
+    got = to_np(st.scores)
+    want = oracle.page_scores(bt.ocache, bt.table, bt.lens, bt.q)
+    check_scores(got, want, score_tolerance(bt.ocache, bt.table, bt.lens, bt.q, bt.w.group))
+
+
+@pytest.mark.parametrize("kind,n", CASES, ids=IDS)
+def test_topk_on_identical_scores_is_exact(kind, n):
+    kvq, _ = kvq_mod()
+    bt = built((kind, n), workload(kind, n))
+    w = bt.w
+    if w.is_dense():
+        pytest.skip("selection bypassed for ratio 1")
+    st = bt.step()
+    sc32 = oracle.page_scores(bt.ocache, bt.table, bt.lens, bt.q).astype(np.float32)
+    st.scores.copy_(torch.from_numpy(sc32))
+    kvq.kvq_topk_pages(st.scores, bt.seqs, w.num_kv_heads, w.ratio_num, w.ratio_den, w.k_fixed,
+                       st.sel_pages, st.sel_count)
+    osel, ocnt = oracle.topk(sc32.astype(np.float64), bt.lens, w.ratio_num, w.ratio_den, w.k_fixed, st.k_cap)
+    assert np.array_equal(to_np(st.sel_count), ocnt)
+    assert np.array_equal(to_np(st.sel_pages), osel)
+
+
+def test_topk_ties_plateaus_and_ragged_rows():
+    """Constructed equal scores must go to the lowest logical pages; rows of
+    different lengths; K = P rows; a row of one page."""
+    kvq, _ = kvq_mod()
+    rng = np.random.default_rng(21)
+    B, H, maxp = 5, 3, 700
+    lens = np.array([700 * 16, 699 * 16 + 3, 1, 37 * 16, 300 * 16 - 15], np.int32)
+    sc = rng.integers(-3, 4, size=(B, H, maxp)).astype(np.float32)  # heavy ties
+    sc[0, 0] = 0.0
+    sc[0, 0, ::2] = -0.0                                            # -0 and +0 tie
+    sc[1, 2, 100:400] = 7.5
+    P = (lens + PAGE - 1) // PAGE
+    for b in range(B):
+        sc[b, :, P[b]:] = -np.inf
+    seqs = kvq.Seqs(torch.from_numpy(lens).cuda(), torch.zeros((B, maxp), dtype=torch.int32, device="cuda"))
+    for rn, rd, kf in [(3, 10, 0), (1, 1, 0), (1, 7, 0), (0, 1, 5)]:
+        k_cap = kvq.num_selected(maxp, rn, rd, kf)
+        sel = torch.empty((B, H, k_cap), dtype=torch.int32, device="cuda")
+        cnt = torch.empty((B, H), dtype=torch.int32, device="cuda")
+        kvq.kvq_topk_pages(torch.from_numpy(sc).cuda(), seqs, H, rn, rd, kf, sel, cnt)
+        osel, ocnt = oracle.topk(sc.astype(np.float64), lens, rn, rd, kf, k_cap)
+        assert np.array_equal(to_np(cnt), ocnt)
+        assert np.array_equal(to_np(sel), osel), (rn, rd, kf)
+
+
+@pytest.mark.parametrize("kind,n", CASES, ids=IDS)
+def test_attention_on_oracle_selection(kind, n):
+    kvq, _ = kvq_mod()
+    bt = built((kind, n), workload(kind, n))
+    w = bt.w
+    st = bt.step()
+    if w.is_dense():
+        out = st.attend(bt.q_dev)
+        want = oracle.attention(bt.ocache, bt.table, bt.lens, bt.q)
+    else:
+        osc = oracle.page_scores(bt.ocache, bt.table, bt.lens, bt.q)
+        osel, ocnt = oracle.topk(osc, bt.lens, w.ratio_num, w.ratio_den, w.k_fixed, st.k_cap)
+        sel = torch.from_numpy(osel).cuda()
+        cnt = torch.from_numpy(ocnt).cuda()
+        out = st.attend(bt.q_dev, sel, cnt)
+        want = oracle.attention(bt.ocache, bt.table, bt.lens, bt.q, osel, ocnt)
+    err = np.abs(to_np(out).astype(np.float64) - want).max()
+    log(f"[attn] {w.name}: max abs err {err:.3g}")
+    assert err <= ATTN_ATOL
+
+
+@pytest.mark.parametrize("n", [2, 4, 5])
+@pytest.mark.parametrize("pps", [1, 3, 4, 16, 64])
+def test_attention_independent_of_split_size(n, pps):
+    _, runtime = kvq_mod()
+    bt = built(("small", n), workloads.small(n))
+    w = bt.w
+    ref = bt.step()
+    ref.run(bt.q_dev)
+    base = to_np(ref.out).copy()
+    st = bt.step(pages_per_split=pps)
+    out = to_np(st.attend(bt.q_dev, ref.sel_pages, ref.sel_count)).astype(np.float64)
+    assert np.abs(out - base).max() <= 1e-5
+    want = oracle.attention(bt.ocache, bt.table, bt.lens, bt.q, to_np(ref.sel_pages), to_np(ref.sel_count))
+    assert np.abs(out - want).max() <= ATTN_ATOL
+    dense = to_np(bt.step(dense=True, pages_per_split=pps).attend(bt.q_dev)).astype(np.float64)
+    assert np.abs(dense - oracle.attention(bt.ocache, bt.table, bt.lens, bt.q)).max() <= ATTN_ATOL
+
+
+@pytest.mark.parametrize("kind,n", CASES, ids=IDS)
+def test_end_to_end_step(kind, n):
+    bt = built((kind, n), workload(kind, n))
+    w = bt.w
+    st = bt.step(dense=w.is_dense())
+    out = to_np(st.run(bt.q_dev)).astype(np.float64)
+    if w.is_dense():
+        want = oracle.attention(bt.ocache, bt.table, bt.lens, bt.q)
+    else:
+        osc, osel, ocnt, _ = oracle.decode_step(bt.ocache, bt.table, bt.lens, bt.q, w.ratio_num, w.ratio_den,
+                                                w.k_fixed, st.k_cap, nthreads=8)
+        gsel, gcnt = to_np(st.sel_pages), to_np(st.sel_count)
+        ties = check_selection_near_ties(gsel, gcnt, osc, osel, ocnt)
+        log(f"[step] {w.name}: {ties} near-tie page swaps")
+        want = oracle.attention(bt.ocache, bt.table, bt.lens, bt.q, gsel, gcnt)
+    err = np.abs(out - want).max()
+    log(f"[step] {w.name}: max abs err {err:.3g}")
+    assert err <= ATTN_ATOL
+
+
+def test_k_equals_all_pages_matches_dense():
+    """Config 1 with K = 64 of 64 pages: the full selection path equals the
+    dense path and the oracle's dense attention."""
+    w = workloads.config(1).with_(k_fixed=64)
+    bt = built(("k64", 1), w)
+    st = bt.step()
+    sparse = to_np(st.run(bt.q_dev)).copy()
+    assert np.array_equal(to_np(st.sel_count), np.full((1, 4), 64))
+    dense = to_np(st.attend(bt.q_dev))
+    want = oracle.attention(bt.ocache, bt.table, bt.lens, bt.q)
+    assert np.abs(sparse - want).max() <= ATTN_ATOL
+    assert np.abs(sparse - dense).max() <= 1e-6
+
+
+@pytest.mark.parametrize("n", [4, 5])
+def test_deterministic(n):
+    """Two runs give bitwise-equal codes, metadata, scores, selections, outputs."""
+    w = workloads.small(n)
+    a, b = Built(w, with_oracle=False), Built(w, with_oracle=False)
+    for x, y in [(a.cache.k_pages, b.cache.k_pages), (a.cache.kv_params, b.cache.kv_params),
+                 (a.cache.page_meta, b.cache.page_meta)]:
+        assert torch.equal(x, y)
+    sa, sb = a.step(), b.step()
+    oa, ob = sa.run(a.q_dev), sb.run(b.q_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(sa.scores, sb.scores) and torch.equal(sa.sel_pages, sb.sel_pages)
+    assert torch.equal(oa, ob)
+
+
+# ------------------------------------------------------- the GQA full size
+def test_config5_full_size_sampled():
+    """Config 5 at full size (64 ragged sequences, 32 q / 8 KV heads, INT8 per
+    group) in the launch configuration the benchmark uses; the oracle checks
+    three sampled sequences (shortest, longest, one more) end to end."""
+    w = workloads.config(5)
+    bt = Built(w, with_oracle=False)
+    st = bt.step()
+    out = to_np(st.run(bt.q_dev)).astype(np.float64)
+    scores = to_np(st.scores)
+    gsel, gcnt = to_np(st.sel_pages), to_np(st.sel_count)
+    k = to_np(bt.cache.k_pages)
+    params = to_np(bt.cache.kv_params)
+    meta = to_np(bt.cache.page_meta)
+    lens = bt.lens
+    picks = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 17})
+    for b in picks:
+        L = int(lens[b])
+        P = (L + PAGE - 1) // PAGE
+        kb, vb = w.keys(b), w.values(b)
+        ocache = oracle.Cache(w.fmt, P, w.num_kv_heads, w.head_dim)
+        tab = np.arange(P, dtype=np.int32)[None]
+        oracle.append(ocache, tab, [0], [0, L], kb, vb)
+        oracle.page_meta(ocache, tab, [L])
+        phys = bt.table[b, :P]
+        assert np.array_equal(k[phys], ocache.k_pages), f"codes of sequence {b}"
+        assert np.array_equal(params[phys].view(np.uint32), ocache.params.view(np.uint32))
+        assert np.array_equal(meta[phys], ocache.meta)
+        qb = bt.q[b:b + 1]
+        osc, osel, ocnt, _ = oracle.decode_step(ocache, tab, [L], qb, w.ratio_num, w.ratio_den, w.k_fixed,
+                                                st.k_cap, nthreads=8)
+        S = score_tolerance(ocache, tab, np.array([L]), qb, w.group)
+        check_scores(scores[b:b + 1, :, :P], osc[:, :, :P], S[:, :, :P])
+        check_selection_near_ties(gsel[b:b + 1], gcnt[b:b + 1], osc, osel, ocnt)
+        want = oracle.attention(ocache, tab, [L], qb, gsel[b:b + 1], gcnt[b:b + 1])
+        err = np.abs(out[b] - want[0]).max()
+        log(f"[cfg5] seq {b} L={L}: max abs err {err:.3g}")
+        assert err <= ATTN_ATOL
