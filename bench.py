@@ -1,0 +1,247 @@
+"""Decode-step benchmark: paged, INT8, query-aware sparse attention at 32K context.
+
+One step = the whole hot path for one layer of the Llama-2-7B-shaped workload
+(1 sequence, 32 heads, head_dim 128, 32768 tokens in 16-token pages, INT8 per
+token, selection ratio 0.3 -> 615 of 2048 pages per head):
+  append the newest token (quantize into its page) -> refresh that page's
+  metadata -> score all pages -> top-K -> split-K attention + combine.
+Steps rotate over `--layers` independent copies of the layer cache (distinct
+device buffers), so a step never finds the previous step's working set in the
+256 MB Infinity Cache, as in a real decode pass over many layers.
+
+Prints one JSON line: achieved GB/s of the whole step (metadata of every page
++ the selected KV tiles with their scale/zero, i.e. the bytes the method must
+read), microseconds per step, the sparse attention kernels' own GB/s against
+the 8 TB/s HBM peak (timed with HIP events on the launch stream), and the CPU
+oracle timed on the host on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(w, k_per_row):
+    """(metadata bytes of every page, selected KV bytes): each (page, KV head)
+    counted once; an INT8 tile carries its codes and its fp32 scale/zero."""
+    import workloads
+    d = w.head_dim
+    pages = w.pages_per_seq().astype(np.int64)
+    meta = int(pages.sum()) * w.num_kv_heads * 8 * d
+    if w.fmt == workloads.FMT_FP16:
+        tile = 2 * 16 * d * 2
+    elif w.fmt == workloads.FMT_INT8_TOKEN:
+        tile = 2 * 16 * d + 16 * 16
+    else:
+        tile = 2 * 16 * d + 16
+    return meta, int(np.asarray(k_per_row, np.int64).sum()) * tile
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle's decode step (scores -> top-K -> attention) on host threads."""
+    import oracle
+    cache, table = oracle.build_cache(w)
+    lens, q = w.seq_lens(), w.query()
+    k_cap = oracle.num_selected(int(table.shape[1]), w.ratio_num, w.ratio_den, w.k_fixed)
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    threads = max(1, min(16, threads))
+    times = []
+    t_end = time.perf_counter() + seconds
+    while True:
+        t0 = time.perf_counter()
+        oracle.decode_step(cache, table, lens, q, w.ratio_num, w.ratio_den, w.k_fixed, k_cap, nthreads=threads)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_end or len(times) >= 20:
+            break
+    return float(np.median(times)), threads, len(times)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", type=int, default=4, help="workload number 1-5 (default 4: 32K INT8 sparse)")
+    ap.add_argument("--layers", type=int, default=8, help="independent layer caches rotated per step")
+    ap.add_argument("--eager", action="store_true", help="launch every kernel from the host (no HIP graph)")
+    ap.add_argument("--pages-per-split", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this decode-step path runs on one GPU; multi-GPU runs are not part of it "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads
+    import paged_quantized_sparse_amd as kvq
+    from paged_quantized_sparse_amd import runtime
+
+    kvq.lib()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = workloads.config(args.config)
+    table, n_phys = w.block_table()
+    lens = w.seq_lens()
+    src = lambda b: (w.keys(b), w.values(b))  # noqa: E731
+    print(f"[bench] building {w.name} ...", file=sys.stderr, flush=True)
+    base, seqs = runtime.build_cache(w.fmt, n_phys, w.num_kv_heads, w.head_dim, table, lens, src,
+                                     prefill_lens=lens - 1, device=dev)
+    layers = [base]
+    for _ in range(args.layers - 1):
+        layers.append(kvq.PagedCache(base.format, base.num_phys_pages, base.num_kv_heads, base.head_dim,
+                                     base.k_pages.clone(), base.v_pages.clone(),
+                                     None if base.kv_params is None else base.kv_params.clone(),
+                                     base.page_meta.clone()))
+    q = torch.from_numpy(w.query().view(np.int16)).to(dev)
+    dense = w.is_dense()
+    appends = [runtime.DecodeAppend(c, seqs, lens, src, device=dev) for c in layers]
+    steps = [runtime.DecodeStep(c, seqs, w.num_q_heads, w.ratio_num, w.ratio_den, w.k_fixed, dense=dense,
+                                pages_per_split=args.pages_per_split, device=dev) for c in layers]
+    torch.cuda.synchronize()
+
+    def one_step(i):
+        appends[i % len(layers)].run()
+        steps[i % len(layers)].run(q)
+
+    # warm-up (eager), which also fills every layer's selection
+    for i in range(max(args.warmup, len(layers))):
+        one_step(i)
+    torch.cuda.synchronize()
+
+    # HIP graphs: one per layer, and one holding a whole rotation over the
+    # layers (a multi-layer decode pass is captured once and replayed)
+    stream = torch.cuda.current_stream()
+    graphs = rotation = None
+    if not args.eager:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        graphs = []
+        with torch.cuda.stream(cap):
+            for li in range(len(layers)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    one_step(li)
+                graphs.append(g)
+            rotation = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(rotation, stream=cap):
+                for li in range(len(layers)):
+                    one_step(li)
+        stream.wait_stream(cap)
+        for _ in range(2):
+            rotation.replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` decode steps
+    n_rot, rest = divmod(args.steps, len(layers))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graphs is not None:
+        for _ in range(n_rot):
+            rotation.replay()
+        for i in range(rest):
+            graphs[i].replay()
+    else:
+        for i in range(args.steps):
+            one_step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+
+    # ---- the sparse attention call alone (split kernel + combine), HIP events
+    # on the stream it is launched on, rotating over the same layers
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_attn = args.steps
+    for i in range(len(layers)):
+        st = steps[i]
+        st.attend(q, None if dense else st.sel_pages, None if dense else st.sel_count)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(n_attn):
+        st = steps[i % len(layers)]
+        st.attend(q, None if dense else st.sel_pages, None if dense else st.sel_count)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    attn_us = ev0.elapsed_time(ev1) * 1e3 / n_attn
+
+    counts = steps[0].sel_count.cpu().numpy() if not dense else np.tile(w.pages_per_seq()[:, None], (1, w.num_kv_heads))
+    meta_b, kv_b = algorithmic_bytes(w, counts)
+    step_bytes = (0 if dense else meta_b) + kv_b
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    attn_gbs = kv_b / (attn_us * 1e-6) / 1e9
+
+    # streaming-read ceiling of this GPU (2 GiB fp32 sum), for context
+    big = torch.empty(1 << 29, dtype=torch.float32, device=dev).fill_(1.0)
+    big.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        big.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = 5 * big.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del big
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
+        t_cpu, threads, reps = cpu_baseline(w, args.cpu_seconds)
+        cpu = {"value": round(step_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"full decode step (scores, top-K, attention) of this workload, median of {reps} runs, "
+                         f"{t_cpu * 1e3:.1f} ms each",
+               "us_per_step": round(t_cpu * 1e6, 1)}
+
+    ratio = f"{w.ratio_num}/{w.ratio_den}" if not w.k_fixed else f"k={w.k_fixed}"
+    rec = {
+        "metric": "achieved HBM GB/s (% of peak) + us/decode-step, 32K ctx INT8 sparse",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "context": int(lens.max()), "page": 16,
+                   "storage": workloads.FORMAT_NAMES[w.fmt], "selection": ratio,
+                   "selected_pages_per_head": int(counts.max()), "layers_rotated": len(layers),
+                   "launch": "eager" if graphs is None else "hip_graph",
+                   "pages_per_split": steps[0].pps},
+        "bytes_per_step": {"metadata": meta_b if not dense else 0, "selected_kv": kv_b},
+        "roofline": {"bound": "hbm", "kernel": "kvq_sparse_decode_attn (split kernel + combine)",
+                     "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "us_per_launch": round(attn_us, 2)},
+        "stream_read_ceiling_gbs": round(read_gbs, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

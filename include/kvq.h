@@ -125,6 +125,22 @@ kvq_status kvq_append_quant(const kvq_cache *cache, const kvq_seqs *seqs,
                             const uint16_t *k_new, const uint16_t *v_new, void *stream);
 
 /*
+ * kvq_append_decode -- the decode-time append: kvq_append_quant followed by
+ * kvq_build_page_meta on exactly the pages the new rows land in, in one
+ * kernel.  Each sequence's rows are its newest tokens: after the call the
+ * sequence holds start_pos[b] + rows tokens, and page metadata covers the
+ * valid tokens below that.  At most KVQ_DECODE_MAX_ROWS rows per sequence
+ * (max_new larger: KVQ_ERR_UNSUPPORTED); INT8_GROUP64 rows re-supply the open
+ * group from its aligned start, as in kvq_append_quant.  seqs->seq_lens is
+ * not read; cache->page_meta is required.  Codes, scales, zero-points and
+ * metadata are bit-identical to the two separate calls.
+ */
+#define KVQ_DECODE_MAX_ROWS 64
+kvq_status kvq_append_decode(const kvq_cache *cache, const kvq_seqs *seqs,
+                             const int32_t *start_pos, const int32_t *new_off, int32_t max_new,
+                             const uint16_t *k_new, const uint16_t *v_new, void *stream);
+
+/*
  * kvq_build_page_meta -- per (logical page j, KV head) of each sequence, for
  * page_begin[b] <= j < ceil(L_b/16): page_meta[block_table[b][j]][h] = the
  * per-channel min and max over the page's valid tokens (t < L_b) of the keys
@@ -160,7 +176,7 @@ kvq_status kvq_page_scores(const kvq_cache *cache, const kvq_seqs *seqs,
  *               then -1 up to k_cap.
  *   sel_count : [B][H_kv] int32 out: K_b.
  * k_cap must be >= K for P = max_pages (else KVQ_ERR_INVALID_ARG), and
- * max_pages <= 15360 (else KVQ_ERR_UNSUPPORTED).
+ * max_pages <= 12288 (else KVQ_ERR_UNSUPPORTED).
  */
 kvq_status kvq_topk_pages(const float *scores, const kvq_seqs *seqs, int32_t num_kv_heads,
                           int32_t ratio_num, int32_t ratio_den, int32_t k_fixed, int32_t k_cap,
@@ -179,7 +195,8 @@ kvq_status kvq_topk_pages(const float *scores, const kvq_seqs *seqs, int32_t num
  *   q   : [B][H_q][d] fp16 bits
  *   out : [B][H_q][d] fp32
  *   ws  : workspace of at least kvq_attn_workspace_bytes(...) bytes (the
- *         per-split partial results); ws_bytes is its size.
+ *         per-split partial results); ws_bytes is its size.  Calls that share
+ *         a workspace must not overlap in time (one stream, or synchronized).
  * pages_per_split 0 picks a default; otherwise 1..4096.  k_cap is the row
  * stride of sel_pages and bounds sel_count (ignored when sel_pages is NULL).
  */

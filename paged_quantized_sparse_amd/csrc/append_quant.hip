@@ -28,26 +28,6 @@ struct AppendArgs {
   int max_pages;
 };
 
-__device__ __forceinline__ void quant_params(float lo, float hi, float& scale, float& inv) {
-#pragma clang fp contract(off)
-  if (hi > lo) {
-    float range = hi - lo;
-    scale = range / 255.0f;
-    inv = 1.0f / scale;
-  } else {
-    scale = 1.0f;
-    inv = 1.0f;
-  }
-}
-
-__device__ __forceinline__ uint32_t quant_code(float x, float zero, float inv) {
-#pragma clang fp contract(off)
-  float t = (x - zero) * inv;
-  float r = __builtin_rintf(t);
-  r = fminf(fmaxf(r, 0.0f), 255.0f);
-  return (uint32_t)r;
-}
-
 // ---------------------------------------------------------------- fp16 copy
 // grid (ceil(max_new / 4), B), 256 threads: 4 tokens per block, 16-byte chunks.
 template <int D>

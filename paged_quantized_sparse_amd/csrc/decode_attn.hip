@@ -8,20 +8,35 @@
 // holds a whole (page, KV head) tile in flight as 16-byte loads: for a token
 // row of RB = d * elem bytes, LPT = RB/16 lanes share a token, so one load
 // instruction covers TPL = 64/LPT tokens, and NL = 16/TPL loads cover the page.
-// INT8 codes are dequantized in registers with the dequant folded into the
-// dot product: q.k = s * sum(q_i c_i) + z * sum(q_i); values accumulate
-// (p s) * c per channel plus p z once per token.  The G query heads of a KV
-// group share every loaded tile.  Each wave keeps an online softmax
-// (running max m, sum l, acc[d]) per query head in the exp2 domain; waves merge
-// through LDS and the block writes one partial (m, l, acc) per query head and
-// split.  combine_kernel then merges a row's splits with log-sum-exp weights.
+// The next tile's loads are issued before the current tile is consumed.
+//
+// Keys: q.k runs on v_dot2_f32_f16 with the fp16 query.  An INT8 code c
+// becomes the fp16 value 1024 + c with one byte permute (0x64 is the high byte
+// of 1024.0h), so for per-token or per-group (scale s, zero z)
+//   q.k = s * sum q_i (1024 + c_i) + (z - 1024 s) * sum q_i.
+// Values: acc += (p s) * c per channel (byte converts + fma), plus p z once per
+// token.  The G query heads of a KV group share every loaded tile.
+//
+// Online softmax per lane (exp2 domain): each lane keeps the running max m of
+// the tokens it saw and rescales only when a logit exceeds m by more than
+// kLazy (weights stay below 2^kLazy), so the inner loop needs no cross-lane
+// max.  Lanes, then waves, merge with log-sum-exp weights; each block writes a
+// partial (m, l, acc) per query head and split, and combine_kernel merges a
+// row's splits.  (Merging in the last-arriving split block instead needs a
+// device-scope release/acquire per block, which on gfx950 writes back and
+// invalidates the XCD's L2 each time and costs far more than a second launch.)
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
+#ifndef KVQ_ATTN_PREFETCH
+#define KVQ_ATTN_PREFETCH 2
+#endif
 constexpr int kAttnWaves = 4;
+constexpr int kPrefetch = KVQ_ATTN_PREFETCH;  // tiles in flight ahead of the one being consumed
+constexpr float kLazy = 8.0f;
 
 struct AttnArgs {
   const void* k_pages;
@@ -32,9 +47,9 @@ struct AttnArgs {
   const uint16_t* q;
   const int32_t* sel_pages;  // NULL: all pages
   const int32_t* sel_count;
-  float* part_acc;  // [B][Hq][max_splits][D]
-  float* part_ml;   // [B][Hq][max_splits][2]
-  float* out;       // [B][Hq][D]
+  float* part_acc;    // [B][Hq][max_splits][D]
+  float* part_ml;     // [B][Hq][max_splits][2]
+  float* out;         // [B][Hq][D]
   int H;
   int Hq;
   int max_pages;
@@ -48,59 +63,114 @@ template <int FMT, int D>
 struct Tile {
   static constexpr int ELEM = FMT == kFp16 ? 2 : 1;
   static constexpr int RB = D * ELEM;
-  static constexpr int LPT = RB / 16;  // lanes per token
-  static constexpr int TPL = 64 / LPT;  // tokens per load
+  static constexpr int LPT = RB / 16;     // lanes per token
+  static constexpr int TPL = 64 / LPT;    // tokens per load
   static constexpr int NL = kPage / TPL;  // loads per page
-  static constexpr int CH = 16 / ELEM;  // channels per lane
+  static constexpr int CH = 16 / ELEM;    // channels per lane
 };
 
 __device__ __forceinline__ float byte_to_float(uint32_t w, int i) { return (float)((w >> (8 * i)) & 0xFFu); }
 
+__device__ __forceinline__ half2v as_half2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
+
+// grid (B * Hq), 256 threads: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
+// with M = max_s m_s.  Threads split the splits; loads are unrolled so a
+// thread keeps several partials in flight.
+template <int D, int G>
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
+  constexpr int PARTS = 256 / D;
+  __shared__ float red[4];
+  __shared__ float sm_num[PARTS][D];
+  __shared__ float sm_den[PARTS];
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq, h = bh % a.Hq;
+  const int row = b * a.H + h / G;
+  const int tid = threadIdx.x;
+  const float* ml = a.part_ml + (size_t)bh * a.max_splits * 2;
+  const float* pa = a.part_acc + (size_t)bh * a.max_splits * D;
+  // the first 256 split maxima are loaded alongside the split count
+  const float m_spec = tid < a.max_splits ? ml[2 * tid] : -INFINITY;
+  const int P = (a.seq_lens[b] + kPage - 1) / kPage;
+  const int K = a.sel_pages ? a.sel_count[row] : P;
+  const int ns = (K + a.pps - 1) / a.pps;
+  float M = tid < ns ? m_spec : -INFINITY;
+  for (int s = tid + 256; s < ns; s += 256) M = fmaxf(M, ml[2 * s]);
+  M = max_contig<64>(M);
+  if (lane_id() == 0) red[wave_id()] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int c = tid % D, part = tid / D;
+  float num = 0.0f, den = 0.0f;
+#pragma unroll 4
+  for (int s = part; s < ns; s += PARTS) {
+    const float2 mls = *(const float2*)(ml + 2 * s);
+    const float f = mls.x == -INFINITY ? 0.0f : exp2f(mls.x - M);
+    num = __builtin_fmaf(f, pa[(size_t)s * D + c], num);
+    den = __builtin_fmaf(f, mls.y, den);
+  }
+  sm_num[part][c] = num;
+  if (c == 0) sm_den[part] = den;
+  __syncthreads();
+  if (part == 0) {
+    float n = 0.0f, dd = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PARTS; ++p) { n += sm_num[p][c]; dd += sm_den[p]; }
+    a.out[(size_t)bh * D + c] = dd > 0.0f ? n / dd : 0.0f;
+  }
+}
+
 template <int FMT, int D, int G, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
+  static_assert(NW == 4, "the split merge and the combine assume 4 waves");
   using T = Tile<FMT, D>;
   constexpr int LPT = T::LPT, TPL = T::TPL, NL = T::NL, CH = T::CH;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int row = b * a.H + g;
+  const int first = s * a.pps;
+  const int w = wave_id();
+  const int lane = lane_id();
+  // Speculative gather of this wave's first 64 selected page ids, issued
+  // together with the count loads (any index below k_cap is in bounds), so
+  // the tile loads wait on two dependent loads (selection, block table)
+  // instead of three.
+  int jlog_spec = 0;
+  const int idx0 = first + w + lane * NW;
+  if (a.sel_pages) {
+    if (idx0 < a.k_cap && lane * NW < a.pps) jlog_spec = a.sel_pages[(size_t)row * a.k_cap + idx0];
+  } else {
+    jlog_spec = idx0;
+  }
   const int L = a.seq_lens[b];
   const int P = (L + kPage - 1) / kPage;
   const int K = a.sel_pages ? a.sel_count[row] : P;
-  const int first = s * a.pps;
   if (first >= K) return;
   const int n = min(a.pps, K - first);
 
-  const int w = wave_id();
-  const int lane = lane_id();
   const int tg = lane / LPT;  // token group
   const int cc = lane % LPT;  // channel chunk
   const int ch0 = cc * CH;
 
-  // ---- query chunk in registers
-  float qf[G][CH];
+  // ---- query chunk in registers: fp16 pairs for v_dot2, and its fp32 sum
+  half2v qh[G][CH / 2];
   float qsum[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    const uint16_t* qp = a.q + ((size_t)b * a.Hq + g * G + hh) * D + ch0;
-    const uint4 raw = *(const uint4*)qp;  // CH = 8 halves for fp16 tiles ...
-    uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+    const uint32_t* qp = (const uint32_t*)(a.q + ((size_t)b * a.Hq + g * G + hh) * D + ch0);
     float acc = 0.0f;
-    if constexpr (CH == 8) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qf[hh][i] = half_bits_to_float((wds[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
-    } else {  // ... 16 halves for INT8 tiles
-      const uint4 raw2 = *(const uint4*)(qp + 8);
-      uint32_t wds2[4] = {raw2.x, raw2.y, raw2.z, raw2.w};
+    for (int i = 0; i < CH / 8; ++i) {
+      const uint4 raw = *(const uint4*)(qp + 4 * i);
+      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qf[hh][i] = half_bits_to_float((wds[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qf[hh][8 + i] = half_bits_to_float((wds2[i / 2] >> (16 * (i % 2))) & 0xFFFFu);
+      for (int j = 0; j < 4; ++j) {
+        qh[hh][4 * i + j] = as_half2(wd[j]);
+        acc += half_bits_to_float(wd[j] & 0xFFFFu) + half_bits_to_float(wd[j] >> 16);
+      }
     }
-#pragma unroll
-    for (int i = 0; i < CH; ++i) acc += qf[hh][i];
     qsum[hh] = acc;
   }
 
-  // ---- this wave's pages: k-th page is split index w + k*NW
+  // ---- per-lane online softmax state
   const int nw = n > w ? (n - w + NW - 1) / NW : 0;
   float m[G], l[G], acc[G][CH], zacc[G];
 #pragma unroll
@@ -113,107 +183,173 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
   }
 
   const size_t tile_elems = (size_t)kPage * D;
+  struct PageRegs {
+    uint4 kr[NL], vr[NL];
+    float4 pr[NL];
+    int nvalid;
+  };
+  // issue every load of one (page, KV head) tile
+  auto load_page = [&](int jl, int ph, PageRegs& r) {
+    r.nvalid = min(kPage, L - jl * kPage);
+    const size_t tile = ((size_t)ph * a.H + g) * tile_elems;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const size_t off = (tile + (size_t)(i * TPL + tg) * D + ch0) * T::ELEM;
+      r.kr[i] = *(const uint4*)((const char*)a.k_pages + off);
+      r.vr[i] = *(const uint4*)((const char*)a.v_pages + off);
+      if constexpr (FMT == kInt8Token)
+        r.pr[i] = *(const float4*)(a.params + ((size_t)ph * a.H + g) * (kPage * 4) + (i * TPL + tg) * 4);
+    }
+    if constexpr (FMT == kInt8Group) {
+      const float4 gp = *(const float4*)(a.params + ((size_t)ph * a.H + g) * 4);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) r.pr[i] = gp;
+    }
+  };
+  // fold one loaded tile into the online softmax of the G heads
+  auto consume_page = [&](PageRegs& r) {
+    const int nvalid = r.nvalid;
+    // Padding slots of a partial last page hold no data (possibly NaN bits):
+    // zero their values and scale/zero with per-lane selects.  A branch that
+    // rewrote the loaded registers would make the compiler wait for every
+    // outstanding load, including the prefetched tiles, at its join.
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const bool pad = i * TPL + tg >= nvalid;
+      r.vr[i].x = pad ? 0u : r.vr[i].x;
+      r.vr[i].y = pad ? 0u : r.vr[i].y;
+      r.vr[i].z = pad ? 0u : r.vr[i].z;
+      r.vr[i].w = pad ? 0u : r.vr[i].w;
+      if constexpr (FMT != kFp16) {
+        r.pr[i].z = pad ? 0.0f : r.pr[i].z;
+        r.pr[i].w = pad ? 0.0f : r.pr[i].w;
+      }
+    }
+    // logits
+    float lg[G][NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const uint32_t kw[4] = {r.kr[i].x, r.kr[i].y, r.kr[i].z, r.kr[i].w};
+      float dot[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) dot[hh] = 0.0f;
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4) {
+        if constexpr (FMT == kFp16) {
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) dot[hh] = __builtin_amdgcn_fdot2(as_half2(kw[d4]), qh[hh][d4], dot[hh], false);
+        } else {
+          const half2v lo = as_half2(__builtin_amdgcn_perm(0x64646464u, kw[d4], 0x04010400u));
+          const half2v hi = as_half2(__builtin_amdgcn_perm(0x64646464u, kw[d4], 0x04030402u));
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            dot[hh] = __builtin_amdgcn_fdot2(lo, qh[hh][2 * d4], dot[hh], false);
+            dot[hh] = __builtin_amdgcn_fdot2(hi, qh[hh][2 * d4 + 1], dot[hh], false);
+          }
+        }
+      }
+      const bool valid = i * TPL + tg < nvalid;
+      float zz = 0.0f;
+      if constexpr (FMT != kFp16) zz = __builtin_fmaf(-1024.0f, r.pr[i].x, r.pr[i].y);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float part = dot[hh];
+        if constexpr (FMT != kFp16) part = __builtin_fmaf(r.pr[i].x, dot[hh], zz * qsum[hh]);
+        part = sum_contig<LPT>(part);
+        lg[hh][i] = valid ? part * a.scale_log2 : -INFINITY;
+      }
+    }
+    // values, decoded once for the G heads
+    float vf[NL][CH];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const uint32_t vw[4] = {r.vr[i].x, r.vr[i].y, r.vr[i].z, r.vr[i].w};
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if constexpr (FMT == kFp16)
+          vf[i][c] = half_bits_to_float((vw[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
+        else
+          vf[i][c] = byte_to_float(vw[c / 4], c % 4);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float mx = lg[hh][0];
+#pragma unroll
+      for (int i = 1; i < NL; ++i) mx = fmaxf(mx, lg[hh][i]);
+      const bool need = mx > m[hh] + kLazy;
+      if (__ballot(need)) {  // wave-uniform branch; rare once the max settles
+        const float mn = need ? mx : m[hh];
+        const float alpha = mn == m[hh] ? 1.0f : __builtin_amdgcn_exp2f(m[hh] - mn);
+        l[hh] *= alpha;
+        zacc[hh] *= alpha;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) acc[hh][c] *= alpha;
+        m[hh] = mn;
+      }
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const float p = lg[hh][i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lg[hh][i] - m[hh]);
+        l[hh] += p;
+        if constexpr (FMT == kFp16) {
+#pragma unroll
+          for (int c = 0; c < CH; ++c) acc[hh][c] = __builtin_fmaf(p, vf[i][c], acc[hh][c]);
+        } else {
+          const float ps = p * r.pr[i].z;
+          zacc[hh] = __builtin_fmaf(p, r.pr[i].w, zacc[hh]);
+#pragma unroll
+          for (int c = 0; c < CH; ++c) acc[hh][c] = __builtin_fmaf(ps, vf[i][c], acc[hh][c]);
+        }
+      }
+    }
+  };
+
   for (int k0 = 0; k0 < nw; k0 += 64) {
-    // gather up to 64 page ids with one lane each
+    // page ids with one lane each (the first 64 were gathered speculatively)
     int jlog_v = 0, phys_v = 0;
     if (k0 + lane < nw) {
       const int idx = first + w + (k0 + lane) * NW;
-      jlog_v = a.sel_pages ? a.sel_pages[(size_t)row * a.k_cap + idx] : idx;
+      jlog_v = k0 == 0 ? jlog_spec : (a.sel_pages ? a.sel_pages[(size_t)row * a.k_cap + idx] : idx);
       phys_v = a.block_table[(size_t)b * a.max_pages + jlog_v];
     }
     const int cnt = min(64, nw - k0);
-    for (int k = 0; k < cnt; ++k) {
-      const int jl = __builtin_amdgcn_readlane(jlog_v, k);
-      const int ph = __builtin_amdgcn_readlane(phys_v, k);
-      const int nvalid = min(kPage, L - jl * kPage);
-      const size_t tile = ((size_t)ph * a.H + g) * tile_elems;
-      uint4 kr[NL], vr[NL];
-      float4 pr[NL];
+    // Software pipeline over a ring of R = kPrefetch + 1 register tiles: the
+    // loads of tiles k+1 .. k+kPrefetch are in flight while tile k is consumed.
+    // Every load is unconditional (an index past the chunk re-reads its last
+    // tile, which is cached), so the compiler's wait counts stay exact; a
+    // conditional load would make it wait for all outstanding loads.  The main
+    // loop is unrolled by R so ring indices are compile-time constants.
+    constexpr int R = kPrefetch + 1;
+    PageRegs ring[R];
+    auto load_idx = [&](int k, PageRegs& r) {
+      const int kk = min(k, cnt - 1);
+      load_page(__builtin_amdgcn_readlane(jlog_v, kk), __builtin_amdgcn_readlane(phys_v, kk), r);
+    };
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const size_t off = (tile + (size_t)(i * TPL + tg) * D + ch0) * T::ELEM;
-        kr[i] = *(const uint4*)((const char*)a.k_pages + off);
-        vr[i] = *(const uint4*)((const char*)a.v_pages + off);
-        if constexpr (FMT == kInt8Token)
-          pr[i] = *(const float4*)(a.params + ((size_t)ph * a.H + g) * (kPage * 4) + (i * TPL + tg) * 4);
-      }
-      if constexpr (FMT == kInt8Group) {
-        const float4 gp = *(const float4*)(a.params + ((size_t)ph * a.H + g) * 4);
+    for (int u = 0; u < kPrefetch; ++u) load_idx(u, ring[u]);
+    int k = 0;
+    for (; k + R <= cnt; k += R) {
 #pragma unroll
-        for (int i = 0; i < NL; ++i) pr[i] = gp;
-      }
-      if (nvalid < kPage) {  // partial last page (wave-uniform): padding slots hold no data
-#pragma unroll
-        for (int i = 0; i < NL; ++i)
-          if (i * TPL + tg >= nvalid) {
-            vr[i] = make_uint4(0, 0, 0, 0);
-            pr[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-          }
-      }
-      // decode this lane's chunk of each token once; reused by the G heads
-      float kf[NL][CH], vf[NL][CH];
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-        const uint32_t vw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-          if constexpr (FMT == kFp16) {
-            kf[i][c] = half_bits_to_float((kw[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
-            vf[i][c] = half_bits_to_float((vw[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
-          } else {
-            kf[i][c] = byte_to_float(kw[c / 4], c % 4);
-            vf[i][c] = byte_to_float(vw[c / 4], c % 4);
-          }
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float lg[NL];
-        float pmax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-          float dot = 0.0f;
-#pragma unroll
-          for (int c = 0; c < CH; ++c) dot = __builtin_fmaf(qf[hh][c], kf[i][c], dot);
-          if constexpr (FMT != kFp16) dot = __builtin_fmaf(pr[i].x, dot, pr[i].y * qsum[hh]);
-          dot = sum_contig<LPT>(dot);
-          lg[i] = (i * TPL + tg) < nvalid ? dot * a.scale_log2 : -INFINITY;
-          pmax = fmaxf(pmax, lg[i]);
-        }
-        pmax = max_contig<64>(pmax);
-        if (pmax > m[hh]) {  // wave-uniform
-          const float alpha = exp2f(m[hh] - pmax);
-          l[hh] *= alpha;
-          zacc[hh] *= alpha;
-#pragma unroll
-          for (int c = 0; c < CH; ++c) acc[hh][c] *= alpha;
-          m[hh] = pmax;
-        }
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-          const float p = exp2f(lg[i] - m[hh]);
-          l[hh] += p;
-          if constexpr (FMT == kFp16) {
-#pragma unroll
-            for (int c = 0; c < CH; ++c) acc[hh][c] = __builtin_fmaf(p, vf[i][c], acc[hh][c]);
-          } else {
-            const float ps = p * pr[i].z;
-            zacc[hh] = __builtin_fmaf(p, pr[i].w, zacc[hh]);
-#pragma unroll
-            for (int c = 0; c < CH; ++c) acc[hh][c] = __builtin_fmaf(ps, vf[i][c], acc[hh][c]);
-          }
-        }
+      for (int u = 0; u < R; ++u) {
+        load_idx(k + u + kPrefetch, ring[(u + kPrefetch) % R]);
+        consume_page(ring[u]);
       }
     }
+    // fewer than R tiles remain; they are already in ring[0 ..] (no loads here)
+#pragma unroll
+    for (int u = 0; u < kPrefetch; ++u)
+      if (k + u < cnt) consume_page(ring[u]);
   }
 
-  // ---- reduce over token groups (lanes congruent mod LPT)
+  // ---- merge the token groups of the wave (lanes congruent mod LPT)
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    l[hh] = sum_strided<LPT>(l[hh]);
+    const float M = max_strided<LPT>(m[hh]);
+    const float f = m[hh] == -INFINITY ? 0.0f : exp2f(m[hh] - M);
+    l[hh] = sum_strided<LPT>(l[hh] * f);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) acc[hh][c] = sum_strided<LPT>(acc[hh][c] + zacc[hh]);
+    for (int c = 0; c < CH; ++c) acc[hh][c] = sum_strided<LPT>((acc[hh][c] + zacc[hh]) * f);
+    m[hh] = M;
   }
 
   // ---- merge the block's waves through LDS and write the split's partials
@@ -239,7 +375,8 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
     float sa = 0.0f, sl = 0.0f;
 #pragma unroll
     for (int v = 0; v < NW; ++v) {
-      const float f = exp2f(sm_ml[v][hh][0] - M);  // 0 for a wave without pages
+      const float mv = sm_ml[v][hh][0];
+      const float f = mv == -INFINITY ? 0.0f : exp2f(mv - M);  // 0 for a wave without pages
       sa = __builtin_fmaf(f, sm_acc[v][hh][c], sa);
       sl = __builtin_fmaf(f, sm_ml[v][hh][1], sl);
     }
@@ -250,29 +387,7 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
       a.part_ml[prow * 2 + 1] = sl;
     }
   }
-}
 
-// grid (B * Hq), D threads: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
-template <int D, int G>
-__global__ __launch_bounds__(D) void combine_kernel(AttnArgs a) {
-  const int bh = blockIdx.x;
-  const int b = bh / a.Hq, h = bh % a.Hq;
-  const int row = b * a.H + h / G;
-  const int P = (a.seq_lens[b] + kPage - 1) / kPage;
-  const int K = a.sel_pages ? a.sel_count[row] : P;
-  const int ns = (K + a.pps - 1) / a.pps;
-  const int c = threadIdx.x;
-  const float* ml = a.part_ml + (size_t)bh * a.max_splits * 2;
-  const float* pa = a.part_acc + (size_t)bh * a.max_splits * D;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-  float num = 0.0f, den = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float f = exp2f(ml[2 * s] - M);
-    num = __builtin_fmaf(f, pa[(size_t)s * D + c], num);
-    den = __builtin_fmaf(f, ml[2 * s + 1], den);
-  }
-  a.out[(size_t)bh * D + c] = ns > 0 ? num / den : 0.0f;
 }
 
 template <int FMT, int D, int G>
@@ -281,7 +396,7 @@ hipError_t run(const AttnArgs& a, int B, hipStream_t st) {
   hipLaunchKernelGGL((decode_attn_kernel<FMT, D, G, kAttnWaves>), grid, dim3(kAttnWaves * 64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((combine_kernel<D, G>), dim3(B * a.Hq), dim3(D), 0, st, a);
+  hipLaunchKernelGGL((combine_kernel<D, G>), dim3(B * a.Hq), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -306,11 +421,11 @@ hipError_t launch_decode_attn(const kvq_cache& c, const kvq_seqs& s, const uint1
                               const int32_t* sel_pages, const int32_t* sel_count, int k_cap, float sm_scale,
                               int pages_per_split, int max_splits, float* out, void* ws, hipStream_t st) {
   const size_t n_part = (size_t)s.batch * num_q_heads * max_splits;
-  float* part_acc = (float*)ws;
-  float* part_ml = part_acc + n_part * c.head_dim;
+  float* part_ml = (float*)ws;
+  float* part_acc = part_ml + n_part * 2;
   AttnArgs a{c.k_pages, c.v_pages, c.kv_params, s.block_table, s.seq_lens, q, sel_pages, sel_count,
-             part_acc, part_ml, out, c.num_kv_heads, num_q_heads, s.max_pages, k_cap, pages_per_split,
-             max_splits, sm_scale * 1.4426950408889634f};
+             part_acc, part_ml, out, c.num_kv_heads, num_q_heads, s.max_pages, k_cap,
+             pages_per_split, max_splits, sm_scale * 1.4426950408889634f};
   const int G = num_q_heads / c.num_kv_heads;
   if (c.format == KVQ_FP16) return run_d<kFp16>(a, s.batch, c.head_dim, G, st);
   if (c.format == KVQ_INT8_TOKEN) return run_d<kInt8Token>(a, s.batch, c.head_dim, G, st);

@@ -62,6 +62,21 @@ kvq_status kvq_append_quant(const kvq_cache* cache, const kvq_seqs* seqs, const 
                                      (hipStream_t)stream));
 }
 
+kvq_status kvq_append_decode(const kvq_cache* cache, const kvq_seqs* seqs, const int32_t* start_pos,
+                             const int32_t* new_off, int32_t max_new, const uint16_t* k_new,
+                             const uint16_t* v_new, void* stream) {
+  kvq_status st = check_cache(cache, true);
+  if (st != KVQ_OK) return st;
+  if (!seqs || !seqs->block_table || seqs->batch < 1 || seqs->batch > 65535 || seqs->max_pages < 1)
+    return KVQ_ERR_INVALID_ARG;
+  if (!start_pos || !new_off || max_new < 0) return KVQ_ERR_INVALID_ARG;
+  if (max_new > KVQ_DECODE_MAX_ROWS) return KVQ_ERR_UNSUPPORTED;
+  if (max_new == 0) return KVQ_OK;
+  if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
+  if (cache->num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  return from_hip(kvq::launch_append_decode(*cache, *seqs, start_pos, new_off, k_new, v_new, (hipStream_t)stream));
+}
+
 kvq_status kvq_build_page_meta(const kvq_cache* cache, const kvq_seqs* seqs, const int32_t* page_begin,
                                int32_t max_span, void* stream) {
   kvq_status st = check_cache(cache, true);

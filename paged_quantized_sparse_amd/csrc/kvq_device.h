@@ -84,6 +84,16 @@ __device__ __forceinline__ float sum_strided(float x) {
   return x;
 }
 
+template <int S>
+__device__ __forceinline__ float max_strided(float x) {
+  static_assert(S >= 4 && S <= 64, "strides 4..64");
+  if constexpr (S <= 4) x = fmaxf(x, dpp<kDppRor4>(x));
+  if constexpr (S <= 8) x = fmaxf(x, dpp<kDppRor8>(x));
+  if constexpr (S <= 16) x = fmaxf(x, shfl_xor(x, 16));
+  if constexpr (S <= 32) x = fmaxf(x, shfl_xor(x, 32));
+  return x;
+}
+
 // Order-preserving map fp32 -> uint32 (larger float, larger key); -0 == +0.
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
@@ -93,6 +103,30 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Asymmetric min/max INT8 quantization of a row with minimum lo and maximum
+// hi: zero = lo, scale = (hi - lo) / 255, code = clamp(rint((x - zero) / scale))
+// with 1/scale precomputed; IEEE fp32, round to nearest even, no contraction,
+// so codes are reproducible bit for bit.  A constant row gets scale 1.
+__device__ __forceinline__ void quant_params(float lo, float hi, float& scale, float& inv) {
+#pragma clang fp contract(off)
+  if (hi > lo) {
+    float range = hi - lo;
+    scale = range / 255.0f;
+    inv = 1.0f / scale;
+  } else {
+    scale = 1.0f;
+    inv = 1.0f;
+  }
+}
+
+__device__ __forceinline__ uint32_t quant_code(float x, float zero, float inv) {
+#pragma clang fp contract(off)
+  float t = (x - zero) * inv;
+  float r = __builtin_rintf(t);
+  r = fminf(fmaxf(r, 0.0f), 255.0f);
+  return (uint32_t)r;
+}
 
 // Number of pages selected from P by the ratio / fixed count (integers only).
 __host__ __device__ __forceinline__ int num_selected(int P, int rnum, int rden, int k_fixed) {

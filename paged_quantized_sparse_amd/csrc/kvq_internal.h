@@ -15,13 +15,17 @@ hipError_t launch_append(const kvq_cache& c, const kvq_seqs& s, const int32_t* s
                          const int32_t* new_off, int max_new, const uint16_t* k_new,
                          const uint16_t* v_new, hipStream_t st);
 
+hipError_t launch_append_decode(const kvq_cache& c, const kvq_seqs& s, const int32_t* start_pos,
+                                const int32_t* new_off, const uint16_t* k_new, const uint16_t* v_new,
+                                hipStream_t st);
+
 hipError_t launch_page_meta(const kvq_cache& c, const kvq_seqs& s, const int32_t* page_begin,
                             int max_span, hipStream_t st);
 
 hipError_t launch_page_scores(const kvq_cache& c, const kvq_seqs& s, const uint16_t* q, int num_q_heads,
                               float* scores, hipStream_t st);
 
-constexpr int kTopkMaxPages = 15360;
+constexpr int kTopkMaxPages = 12288;
 hipError_t launch_topk(const float* scores, const kvq_seqs& s, int num_kv_heads, int rnum, int rden,
                        int k_fixed, int k_cap, int32_t* sel_pages, int32_t* sel_count, hipStream_t st);
 

@@ -20,37 +20,49 @@ struct MetaArgs {
   int max_pages;
 };
 
-// grid (span blocks, B), 256 threads.  Block x handles logical pages
-// page_begin + x, + gridDim.x, ...; each thread one (KV head, channel).
+// grid (ceil(span * H / 4), B), 4 waves per block.  Each wave takes one
+// (logical page, KV head) item: lane l owns channels l*E .. l*E+E-1 (E = d/64)
+// and loads all 16 token slots at once (padding slots are not read).
 template <int FMT, int D>
 __global__ __launch_bounds__(256) void page_meta_kernel(MetaArgs a) {
+  constexpr int E = D / 64;
   const int b = blockIdx.y;
   const int L = a.seq_lens[b];
   const int P = (L + kPage - 1) / kPage;
   const int j0 = a.page_begin ? a.page_begin[b] : 0;
-  for (int j = j0 + blockIdx.x; j < P; j += gridDim.x) {
+  const int lane = lane_id();
+  for (int item = blockIdx.x * 4 + wave_id();; item += gridDim.x * 4) {
+    const int j = j0 + item / a.H, h = item % a.H;
+    if (j >= P) break;
     const int phys = a.block_table[(size_t)b * a.max_pages + j];
     const int nvalid = min(kPage, L - j * kPage);
-    for (int e = threadIdx.x; e < a.H * D; e += 256) {
-      const int h = e / D, ch = e % D;
-      const size_t tile = ((size_t)phys * a.H + h) * kPage;
-      float lo = INFINITY, hi = -INFINITY;
-      for (int t = 0; t < nvalid; ++t) {
-        float k;
+    const size_t tile = ((size_t)phys * a.H + h) * kPage;
+    float lo[E], hi[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) { lo[e] = INFINITY; hi[e] = -INFINITY; }
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) {
+      if (t < nvalid) {
+        const size_t row = (tile + t) * D + lane * E;
+        float k[E];
         if constexpr (FMT == kFp16) {
-          k = half_bits_to_float(((const uint16_t*)a.k_pages)[(tile + t) * D + ch]);
+          const uint16_t* src = (const uint16_t*)a.k_pages + row;
+#pragma unroll
+          for (int e = 0; e < E; ++e) k[e] = half_bits_to_float(src[e]);
         } else {
-          const float c = (float)((const uint8_t*)a.k_pages)[(tile + t) * D + ch];
+          const uint8_t* src = (const uint8_t*)a.k_pages + row;
           const float* p = FMT == kInt8Token ? a.params + (tile + t) * 4 : a.params + ((size_t)phys * a.H + h) * 4;
-          k = __builtin_fmaf(c, p[0], p[1]);
+          const float sc = p[0], zr = p[1];
+#pragma unroll
+          for (int e = 0; e < E; ++e) k[e] = __builtin_fmaf((float)src[e], sc, zr);
         }
-        lo = fminf(lo, k);
-        hi = fmaxf(hi, k);
+#pragma unroll
+        for (int e = 0; e < E; ++e) { lo[e] = fminf(lo[e], k[e]); hi[e] = fmaxf(hi[e], k[e]); }
       }
-      float* m = a.meta + ((size_t)phys * a.H + h) * 2 * D;
-      m[ch] = lo;
-      m[D + ch] = hi;
     }
+    float* m = a.meta + ((size_t)phys * a.H + h) * 2 * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) { m[e] = lo[e]; m[D + e] = hi[e]; }
   }
 }
 
@@ -70,7 +82,8 @@ hipError_t launch_page_meta(const kvq_cache& c, const kvq_seqs& s, const int32_t
   MetaArgs a{c.k_pages, c.kv_params, c.page_meta, s.block_table, s.seq_lens, page_begin,
              c.num_kv_heads, s.max_pages};
   const int span = max_span > 0 ? (max_span < s.max_pages ? max_span : s.max_pages) : s.max_pages;
-  dim3 grid(span, s.batch);
+  const long long items = (long long)span * c.num_kv_heads;
+  dim3 grid((unsigned)((items + 3) / 4 < 65536 ? (items + 3) / 4 : 65536), s.batch);
   if (c.format == KVQ_FP16) return launch_fmt<kFp16>(a, c.head_dim, grid, st);
   if (c.format == KVQ_INT8_TOKEN) return launch_fmt<kInt8Token>(a, c.head_dim, grid, st);
   return launch_fmt<kInt8Group>(a, c.head_dim, grid, st);

@@ -2,18 +2,23 @@
 // largest scores ("TinyServe", lpnh.cn, section 3.1 phase 2; section 5.1
 // selection_ratio), ties to the lower logical page, output ascending.
 //
-// One 256-thread block per row.  Scores become order-preserving uint32 keys
-// in LDS; a 4-pass 8-bit radix select (MSB first, LDS histograms) finds the
-// K-th largest key T and how many keys equal to T are still needed.  A
-// block-wide exclusive scan over contiguous index chunks then writes every
-// key > T and the first `need` keys == T in ascending page order.
+// One 1024-thread block per row.  Scores become order-preserving uint32 keys
+// in LDS.  All keys share the bits above the highest bit where the row's
+// minimum and maximum key differ; radix passes of up to 11 bits (MSB first,
+// LDS histograms) over the bits below it find the K-th largest key T and how
+// many keys equal to T are still needed.  (Starting at the top bit instead
+// would put nearly every score of similar magnitude into one or two bins of
+// the first pass and serialize its LDS atomics.)  Block-wide scans over
+// 1024-key rounds, in page order, then write every key > T and the first
+// `need` keys == T, ascending.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
 
 struct TopkArgs {
   const float* scores;
@@ -25,27 +30,35 @@ struct TopkArgs {
   int rnum, rden, k_fixed, k_cap;
 };
 
-// Exclusive scan of one value per thread over the block; returns the total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int& total) {
-  const int tid = threadIdx.x;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kTopkThreads; off <<= 1) {
-    const int add = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+// Inclusive scan of one value per thread over the 1024-thread block.
+__device__ __forceinline__ int block_inclusive_scan(int v, int* wsum) {
+  const int lane = lane_id(), w = wave_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
   }
-  total = tmp[kTopkThreads - 1];
-  const int excl = tmp[tid] - v;
+  if (lane == 63) wsum[w] = v;
   __syncthreads();
-  return excl;
+  if (w == 0) {
+    int x = lane < kTopkWaves ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kTopkWaves; off <<= 1) {
+      const int t = __shfl_up(x, off, 64);
+      if (lane >= off) x += t;
+    }
+    if (lane < kTopkWaves) wsum[kTopkWaves + lane] = x - wsum[lane];  // exclusive wave offsets
+  }
+  __syncthreads();
+  v += wsum[kTopkWaves + w];
+  __syncthreads();
+  return v;
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   extern __shared__ uint32_t keys[];  // [max_pages]
-  __shared__ int hist[256];
-  __shared__ int scan_tmp[kTopkThreads];
+  __shared__ int hist[2048];
+  __shared__ int wsum[2 * kTopkWaves];
   __shared__ int pick[2];
 
   const int row = blockIdx.x;  // b * H + g
@@ -62,72 +75,100 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   }
 
   const float* sc = a.scores + (size_t)row * a.max_pages;
-  for (int j = tid; j < P; j += kTopkThreads) keys[j] = float_key(sc[j]);
-  __syncthreads();
+  for (int j0 = 0; j0 < P; j0 += 4 * kTopkThreads) {  // four loads in flight per thread
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * kTopkThreads + tid;
+      v[u] = j < P ? sc[j] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * kTopkThreads + tid;
+      if (j < P) keys[j] = float_key(v[u]);
+    }
+  }
 
-  uint32_t prefix = 0, mask = 0;
+  // the row's key range: every key shares the bits above `lead`
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int j = tid; j < P; j += kTopkThreads) {
+    const uint32_t k = keys[j];
+    kmin = min(kmin, k);
+    kmax = max(kmax, k);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
+  }
+  if (lane_id() == 0) {
+    wsum[wave_id()] = (int)kmin;
+    wsum[kTopkWaves + wave_id()] = (int)kmax;
+  }
+  __syncthreads();
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
+#pragma unroll
+  for (int v = 0; v < kTopkWaves; ++v) {
+    kmin = min(kmin, (uint32_t)wsum[v]);
+    kmax = max(kmax, (uint32_t)wsum[kTopkWaves + v]);
+  }
+  __syncthreads();
+  const int lead = kmax == kmin ? -1 : 31 - __builtin_clz(kmax ^ kmin);  // highest differing bit
+  uint32_t mask = lead < 0 ? 0xFFFFFFFFu : (lead >= 31 ? 0u : ~((2u << lead) - 1u));
+  uint32_t prefix = kmax & mask;
   int need = K;  // keys still to take among those matching the prefix
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
+  int hi_bit = lead;  // next bit to resolve
+#pragma unroll 1
+  while (hi_bit >= 0) {
+    const int bits = hi_bit + 1 < 11 ? hi_bit + 1 : 11;
+    const int shift = hi_bit + 1 - bits;
+    const int nbins = 1 << bits;
+    for (int i = tid; i < 2048; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
     for (int j = tid; j < P; j += kTopkThreads) {
       const uint32_t k = keys[j];
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (nbins - 1)], 1);
     }
     __syncthreads();
-    if (tid < 64) {
-      // suffix counts over digits: lane l owns digits 4l..4l+3
-      int c[4], s = 0;
-#pragma unroll
-      for (int i = 3; i >= 0; --i) { c[i] = hist[4 * tid + i]; }
-      const int own = c[0] + c[1] + c[2] + c[3];
-      // inclusive suffix sum of `own` across lanes (lanes above me)
-      int suf = own;
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_down(suf, off, 64);
-        if (tid + off < 64) suf += o;
-      }
-      const int above = suf - own;  // count of digits > 4*tid+3
-      // find the digit D with count(> D) < need <= count(>= D)
-      s = above;
-#pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        if (s < need && s + c[i] >= need) { pick[0] = 4 * tid + i; pick[1] = need - s; }
-        s += c[i];
-      }
-    }
+    // thread t owns bins 2047-2t and 2046-2t of a 2048-bin view (bins at or
+    // above nbins are empty), counted from the top
+    const int top = 2047 - 2 * tid;
+    const int c0 = hist[top], c1 = hist[top - 1];
+    const int own = c0 + c1;
+    const int incl = block_inclusive_scan(own, wsum);  // keys in bins above mine, plus mine
+    int above = incl - own;
+    if (above < need && above + c0 >= need) { pick[0] = top; pick[1] = need - above; }
+    above += c0;
+    if (above < need && above + c1 >= need) { pick[0] = top - 1; pick[1] = need - above; }
     __syncthreads();
-    const int digit = pick[0];
+    prefix |= (uint32_t)pick[0] << shift;
+    mask |= (uint32_t)(nbins - 1) << shift;
     need = pick[1];
-    prefix |= (uint32_t)digit << shift;
-    mask |= 255u << shift;
+    hi_bit = shift - 1;
     __syncthreads();
   }
   const uint32_t T = prefix;
 
-  // contiguous chunk of pages per thread keeps the output ascending
-  const int chunk = (P + kTopkThreads - 1) / kTopkThreads;
-  const int lo = min(P, tid * chunk), hi = min(P, lo + chunk);
-  int n_gt = 0, n_eq = 0;
-  for (int j = lo; j < hi; ++j) {
-    const uint32_t k = keys[j];
-    n_gt += k > T;
-    n_eq += k == T;
-  }
-  int tot;
-  int gt_before = block_exclusive_scan(n_gt, scan_tmp, tot);
-  int eq_before = block_exclusive_scan(n_eq, scan_tmp, tot);
-  for (int j = lo; j < hi; ++j) {
-    const uint32_t k = keys[j];
-    const int pos = gt_before + min(eq_before, need);
-    if (k > T) {
-      out[pos] = j;
-      ++gt_before;
-    } else if (k == T) {
-      if (eq_before < need) out[pos] = j;
-      ++eq_before;
+  // rounds of 1024 consecutive pages keep the output ascending
+  int gt_base = 0, eq_base = 0;
+  for (int j0 = 0; j0 < P; j0 += kTopkThreads) {
+    const int j = j0 + tid;
+    const uint32_t k = j < P ? keys[j] : 0u;
+    const int is_gt = j < P && k > T, is_eq = j < P && k == T;
+    const int packed = block_inclusive_scan(is_gt | (is_eq << 16), wsum);  // both counts <= 1024
+    const int gt_before = gt_base + (packed & 0xFFFF) - is_gt;
+    const int eq_before = eq_base + (packed >> 16) - is_eq;
+    if (is_gt) out[gt_before + min(eq_before, need)] = j;
+    else if (is_eq && eq_before < need) out[gt_before + eq_before] = j;
+    if (tid == kTopkThreads - 1) {
+      pick[0] = packed & 0xFFFF;
+      pick[1] = packed >> 16;
     }
+    __syncthreads();
+    gt_base += pick[0];
+    eq_base += pick[1];
+    __syncthreads();
   }
   for (int i = K + tid; i < a.k_cap; i += kTopkThreads) out[i] = -1;
 }

@@ -14,7 +14,7 @@ from typing import Callable
 import numpy as np
 import torch
 
-from . import (KVQ_FP16, KVQ_INT8_GROUP64, PAGE_SIZE, PagedCache, Seqs, kvq_append_quant,
+from . import (KVQ_INT8_GROUP64, PAGE_SIZE, PagedCache, Seqs, kvq_append_decode, kvq_append_quant,
                kvq_attn_workspace_bytes, kvq_build_page_meta, kvq_default_pages_per_split, kvq_page_scores,
                kvq_sparse_decode_attn, kvq_topk_pages, num_selected)
 
@@ -106,6 +106,10 @@ class DecodeAppend:
         self.span = int(((lens - 1) // PAGE_SIZE - start // PAGE_SIZE).max()) + 1
 
     def run(self, stream=None) -> None:
+        kvq_append_decode(self.cache, self.seqs, self.start, self.off, self.max_new, self.k_new, self.v_new, stream)
+
+    def run_separate(self, stream=None) -> None:
+        """The same step as two calls: kvq_append_quant, then kvq_build_page_meta."""
         kvq_append_quant(self.cache, self.seqs, self.start, self.off, self.max_new, self.k_new, self.v_new, stream)
         kvq_build_page_meta(self.cache, self.seqs, self.page_begin, self.span, stream)
 
@@ -127,7 +131,7 @@ class DecodeStep:
         self.sel_count = torch.empty((B, H), dtype=torch.int32, device=device)
         self.out = torch.empty((B, num_q_heads, d), dtype=torch.float32, device=device)
         nbytes = kvq_attn_workspace_bytes(B, num_q_heads, d, maxp, self.k_cap, self.pps)
-        self.workspace = torch.empty((nbytes + 255) // 4, dtype=torch.float32, device=device)
+        self.workspace = torch.zeros((nbytes + 255) // 4, dtype=torch.float32, device=device)
         self.sm_scale = 1.0 / float(np.sqrt(d))
 
     def select(self, q, stream=None) -> None:

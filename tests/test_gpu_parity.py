@@ -347,3 +347,80 @@ def test_config5_full_size_sampled():
         err = np.abs(out[b] - want[0]).max()
         log(f"[cfg5] seq {b} L={L}: max abs err {err:.3g}")
         assert err <= ATTN_ATOL
+
+
+@pytest.mark.parametrize("n", [4, 5])
+def test_graph_replay_matches_eager(n):
+    """The decode step (append, metadata refresh, scores, top-K, attention)
+    captured in a HIP graph and replayed several times, with eager work and
+    synchronizations in between, gives the eager result bit for bit."""
+    _, runtime = kvq_mod()
+    w = workloads.small(n)
+    bt = Built(w, with_oracle=False)
+    src = lambda b: (w.keys(b), w.values(b))  # noqa: E731
+    app = runtime.DecodeAppend(bt.cache, bt.seqs, bt.lens, src)
+    st = bt.step()
+    app.run()
+    eager = st.run(bt.q_dev).clone()
+    eager_sel = st.sel_pages.clone()
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            app.run()
+            st.run(bt.q_dev)
+    torch.cuda.current_stream().wait_stream(cap)
+    for i in range(4):
+        st.out.zero_()
+        st.sel_pages.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.out, eager), f"replay {i}"
+        assert torch.equal(st.sel_pages, eager_sel), f"replay {i}"
+        st.run(bt.q_dev)  # eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("rows", [1, 17, 64])
+def test_append_decode_equals_separate_calls_and_oracle(fmt, rows):
+    """kvq_append_decode (append + metadata of the touched pages, one kernel)
+    gives the same codes, scale/zero bits and metadata as kvq_append_quant
+    followed by kvq_build_page_meta, and as the oracle's one-shot build.
+    INT8_GROUP64 re-supplies the open group from its 64-aligned start."""
+    kvq, runtime = kvq_mod()
+    w = workloads.small(5).with_(fmt=fmt, batch=4, len_lo=70, len_hi=300)
+    lens = w.seq_lens().astype(np.int64)
+    table, n_phys = w.block_table()
+    start = (lens - 1) // 64 * 64 if fmt == workloads.FMT_INT8_GROUP64 else lens - rows
+    src = lambda b: (w.keys(b), w.values(b))  # noqa: E731
+    built_caches = []
+    for fused in (True, False):
+        cache, seqs = runtime.build_cache(w.fmt, n_phys, w.num_kv_heads, w.head_dim, table, lens, src,
+                                          prefill_lens=start)
+        cnt = lens - start
+        k_new = np.concatenate([w.keys(b)[start[b]:lens[b]] for b in range(w.batch)])
+        v_new = np.concatenate([w.values(b)[start[b]:lens[b]] for b in range(w.batch)])
+        args = (torch.from_numpy(start.astype(np.int32)).cuda(),
+                torch.from_numpy(np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)).cuda(), int(cnt.max()),
+                torch.from_numpy(k_new.view(np.int16)).cuda(), torch.from_numpy(v_new.view(np.int16)).cuda())
+        if fused:
+            kvq.kvq_append_decode(cache, seqs, *args)
+        else:
+            kvq.kvq_append_quant(cache, seqs, *args)
+            kvq.kvq_build_page_meta(cache, seqs, torch.from_numpy((start // PAGE).astype(np.int32)).cuda(), 5)
+        torch.cuda.synchronize()
+        built_caches.append(cache)
+    a, b = built_caches
+    for x, y in [(a.k_pages, b.k_pages), (a.v_pages, b.v_pages), (a.page_meta, b.page_meta)]:
+        assert torch.equal(x, y)
+    if fmt != workloads.FMT_FP16:
+        assert torch.equal(a.kv_params, b.kv_params)
+    oc, _ = oracle.build_cache(w)
+    k = to_np(a.k_pages)
+    assert np.array_equal(k.view(np.uint16) if fmt == workloads.FMT_FP16 else k, oc.k_pages)
+    if fmt != workloads.FMT_FP16:
+        assert np.array_equal(to_np(a.kv_params).view(np.uint32), oc.params.view(np.uint32))
+    assert np.array_equal(to_np(a.page_meta), oc.meta)
