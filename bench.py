@@ -48,6 +48,26 @@ def algorithmic_bytes(w, k_per_row):
     return meta, int(np.asarray(k_per_row, np.int64).sum()) * tile
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_attn_cfg4_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the attention split kernel from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE record, or None once its sources changed."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+        h = hashlib.sha256()
+        for p in rec["sources"]:
+            with open(os.path.join(ROOT, p), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
+        return int(rec["read_bytes"]) + int(rec["write_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, seconds: float):
     """The oracle's decode step (scores -> top-K -> attention) on host threads."""
     import oracle
@@ -81,6 +101,8 @@ def main() -> int:
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB 10 times (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -89,6 +111,17 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 10}))
+        return 0
 
     import workloads
     import paged_quantized_sparse_amd as kvq
@@ -232,10 +265,11 @@ def main() -> int:
                    "launch": "eager" if graphs is None else "hip_graph",
                    "pages_per_split": steps[0].pps},
         "bytes_per_step": {"metadata": meta_b if not dense else 0, "selected_kv": kv_b},
-        "roofline": {"bound": "hbm", "kernel": "kvq_sparse_decode_attn (split kernel + combine)",
+        "roofline": {"bound": "hbm", "kernel": "kvq_sparse_decode_attn (split kernel + combine kernel)",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "us_per_launch": round(attn_us, 2)},
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic() if args.config == 4 and not args.pages_per_split else None,
+                     "algorithmic_bytes": kv_b, "us_per_launch": round(attn_us, 2)},
         "stream_read_ceiling_gbs": round(read_gbs, 1),
         "cpu_baseline": cpu,
     }

@@ -176,7 +176,7 @@ kvq_status kvq_page_scores(const kvq_cache *cache, const kvq_seqs *seqs,
  *               then -1 up to k_cap.
  *   sel_count : [B][H_kv] int32 out: K_b.
  * k_cap must be >= K for P = max_pages (else KVQ_ERR_INVALID_ARG), and
- * max_pages <= 12288 (else KVQ_ERR_UNSUPPORTED).
+ * max_pages <= 12000 (else KVQ_ERR_UNSUPPORTED).
  */
 kvq_status kvq_topk_pages(const float *scores, const kvq_seqs *seqs, int32_t num_kv_heads,
                           int32_t ratio_num, int32_t ratio_den, int32_t k_fixed, int32_t k_cap,

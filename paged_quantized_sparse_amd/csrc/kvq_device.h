@@ -94,6 +94,25 @@ __device__ __forceinline__ float max_strided(float x) {
   return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, DPP only: Hillis-Steele
+// inside each row of 16 (row_shr 1, 2, 4, 8), then row_bcast:15 adds row 0's
+// total to row 1 and row 2's to row 3, and row_bcast:31 adds lane 31's
+// running total to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan_add(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Lanes below this one whose bit is set in a 64-bit lane mask.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // Order-preserving map fp32 -> uint32 (larger float, larger key); -0 == +0.
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);

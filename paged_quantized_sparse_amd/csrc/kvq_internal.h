@@ -25,7 +25,7 @@ hipError_t launch_page_meta(const kvq_cache& c, const kvq_seqs& s, const int32_t
 hipError_t launch_page_scores(const kvq_cache& c, const kvq_seqs& s, const uint16_t* q, int num_q_heads,
                               float* scores, hipStream_t st);
 
-constexpr int kTopkMaxPages = 12288;
+constexpr int kTopkMaxPages = 12000;  // keys in LDS beside 16.9 KB of histograms, within 64 KB
 hipError_t launch_topk(const float* scores, const kvq_seqs& s, int num_kv_heads, int rnum, int rden,
                        int k_fixed, int k_cap, int32_t* sel_pages, int32_t* sel_count, hipStream_t st);
 

@@ -4,13 +4,17 @@
 //
 // One 1024-thread block per row.  Scores become order-preserving uint32 keys
 // in LDS.  All keys share the bits above the highest bit where the row's
-// minimum and maximum key differ; radix passes of up to 11 bits (MSB first,
-// LDS histograms) over the bits below it find the K-th largest key T and how
-// many keys equal to T are still needed.  (Starting at the top bit instead
-// would put nearly every score of similar magnitude into one or two bins of
-// the first pass and serialize its LDS atomics.)  Block-wide scans over
-// 1024-key rounds, in page order, then write every key > T and the first
-// `need` keys == T, ascending.
+// minimum and maximum key differ; radix passes of up to 11 bits (MSB first)
+// over the bits below it, with LDS histograms, find the K-th largest key T and
+// how many keys equal to T are still needed.  (Starting at the top bit
+// instead would put nearly every score of similar magnitude into one or two
+// bins and serialize the histogram atomics.)  Selection is a chain of short
+// dependent steps, so the block is built for latency: cross-lane work is DPP
+// and ballots (no LDS shuffles), histograms are double-buffered so zeroing the
+// next one overlaps the current pass, and every wave finds the chosen bin
+// itself instead of waiting for a broadcast -- two barriers per pass.  Rounds
+// of 1024 pages in page order then write every key > T and the first `need`
+// keys == T, ascending.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -19,6 +23,7 @@ namespace {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kHistBins = 2048;
 
 struct TopkArgs {
   const float* scores;
@@ -30,40 +35,58 @@ struct TopkArgs {
   int rnum, rden, k_fixed, k_cap;
 };
 
-// Inclusive scan of one value per thread over the 1024-thread block.
-__device__ __forceinline__ int block_inclusive_scan(int v, int* wsum) {
-  const int lane = lane_id(), w = wave_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(v, off, 64);
-    if (lane >= off) v += t;
-  }
-  if (lane == 63) wsum[w] = v;
-  __syncthreads();
-  if (w == 0) {
-    int x = lane < kTopkWaves ? wsum[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < kTopkWaves; off <<= 1) {
-      const int t = __shfl_up(x, off, 64);
-      if (lane >= off) x += t;
-    }
-    if (lane < kTopkWaves) wsum[kTopkWaves + lane] = x - wsum[lane];  // exclusive wave offsets
-  }
-  __syncthreads();
-  v += wsum[kTopkWaves + w];
-  __syncthreads();
-  return v;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
 }
+
+// Min / max over the wave: DPP inside each row of 16, then the four row
+// results through readlane (wave-uniform result).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, dpp_u32<kDppXor1>(x));
+  x = min(x, dpp_u32<kDppXor2>(x));
+  x = min(x, dpp_u32<kDppHalfMirror>(x));
+  x = min(x, dpp_u32<kDppMirror>(x));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return min(min(a, b), min(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<kDppXor1>(x));
+  x = max(x, dpp_u32<kDppXor2>(x));
+  x = max(x, dpp_u32<kDppHalfMirror>(x));
+  x = max(x, dpp_u32<kDppMirror>(x));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Inclusive prefix sum inside each row of 16 lanes (DPP row_shr 1, 2, 4, 8).
+__device__ __forceinline__ int row16_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
+  return x;
+}
+
+// The 16 per-wave values of an LDS array, one per lane of row 0 (lanes
+// 16..63 read a copy of row 0 and are not used): a single LDS read instead of
+// sixteen serialized ones.
+__device__ __forceinline__ int per_wave_value(const int* arr, int lane) { return arr[lane & (kTopkWaves - 1)]; }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   extern __shared__ uint32_t keys[];  // [max_pages]
-  __shared__ int hist[2048];
-  __shared__ int wsum[2 * kTopkWaves];
-  __shared__ int pick[2];
+  __shared__ int hist[2][kHistBins];
+  __shared__ int wtot[2][kTopkWaves];   // radix passes
+  __shared__ int ctot[2][kTopkWaves];   // compaction rounds (a separate buffer: a slow wave may still
+                                        // be reading wtot from the last pass)
+  __shared__ uint32_t wrange[2][kTopkWaves];
 
   const int row = blockIdx.x;  // b * H + g
   const int b = row / a.H;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int P = (a.seq_lens[b] + kPage - 1) / kPage;
   const int K = num_selected(P, a.rnum, a.rden, a.k_fixed);
   int32_t* out = a.sel_pages + (size_t)row * a.k_cap;
@@ -74,8 +97,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     return;
   }
 
+  // keys into LDS (four loads in flight per thread), the key range, and the
+  // first histogram zeroed
   const float* sc = a.scores + (size_t)row * a.max_pages;
-  for (int j0 = 0; j0 < P; j0 += 4 * kTopkThreads) {  // four loads in flight per thread
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int j0 = 0; j0 < P; j0 += 4 * kTopkThreads) {
     float v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -85,90 +111,103 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int j = j0 + u * kTopkThreads + tid;
-      if (j < P) keys[j] = float_key(v[u]);
+      if (j < P) {
+        const uint32_t k = float_key(v[u]);
+        keys[j] = k;
+        kmin = min(kmin, k);
+        kmax = max(kmax, k);
+      }
     }
   }
-
-  // the row's key range: every key shares the bits above `lead`
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int j = tid; j < P; j += kTopkThreads) {
-    const uint32_t k = keys[j];
-    kmin = min(kmin, k);
-    kmax = max(kmax, k);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
-  }
-  if (lane_id() == 0) {
-    wsum[wave_id()] = (int)kmin;
-    wsum[kTopkWaves + wave_id()] = (int)kmax;
+  for (int i = tid; i < kHistBins; i += kTopkThreads) hist[0][i] = 0;
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) {
+    wrange[0][w] = kmin;
+    wrange[1][w] = kmax;
   }
   __syncthreads();
-  kmin = 0xFFFFFFFFu;
-  kmax = 0u;
-#pragma unroll
-  for (int v = 0; v < kTopkWaves; ++v) {
-    kmin = min(kmin, (uint32_t)wsum[v]);
-    kmax = max(kmax, (uint32_t)wsum[kTopkWaves + v]);
-  }
-  __syncthreads();
+  kmin = wave_min_u32(wrange[0][lane & (kTopkWaves - 1)]);
+  kmax = wave_max_u32(wrange[1][lane & (kTopkWaves - 1)]);
   const int lead = kmax == kmin ? -1 : 31 - __builtin_clz(kmax ^ kmin);  // highest differing bit
   uint32_t mask = lead < 0 ? 0xFFFFFFFFu : (lead >= 31 ? 0u : ~((2u << lead) - 1u));
   uint32_t prefix = kmax & mask;
   int need = K;  // keys still to take among those matching the prefix
   int hi_bit = lead;  // next bit to resolve
+  int cur = 0;
+
 #pragma unroll 1
   while (hi_bit >= 0) {
     const int bits = hi_bit + 1 < 11 ? hi_bit + 1 : 11;
     const int shift = hi_bit + 1 - bits;
     const int nbins = 1 << bits;
-    for (int i = tid; i < 2048; i += kTopkThreads) hist[i] = 0;
-    __syncthreads();
+    int* h = hist[cur];
     for (int j = tid; j < P; j += kTopkThreads) {
       const uint32_t k = keys[j];
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (nbins - 1)], 1);
+      if ((k & mask) == prefix) atomicAdd(&h[(k >> shift) & (nbins - 1)], 1);
     }
     __syncthreads();
-    // thread t owns bins 2047-2t and 2046-2t of a 2048-bin view (bins at or
-    // above nbins are empty), counted from the top
-    const int top = 2047 - 2 * tid;
-    const int c0 = hist[top], c1 = hist[top - 1];
+    // thread t owns bins 2047-2t and 2046-2t, counted from the top (bins at
+    // or above nbins stay empty); the next pass's histogram is zeroed now
+    const int top = kHistBins - 1 - 2 * tid;
+    const int c0 = h[top], c1 = h[top - 1];
+    hist[cur ^ 1][tid] = 0;
+    hist[cur ^ 1][tid + kTopkThreads] = 0;
     const int own = c0 + c1;
-    const int incl = block_inclusive_scan(own, wsum);  // keys in bins above mine, plus mine
-    int above = incl - own;
-    if (above < need && above + c0 >= need) { pick[0] = top; pick[1] = need - above; }
-    above += c0;
-    if (above < need && above + c1 >= need) { pick[0] = top - 1; pick[1] = need - above; }
+    const int incl = wave_incl_scan_add(own);
+    if (lane == 63) wtot[cur][w] = incl;
     __syncthreads();
-    prefix |= (uint32_t)pick[0] << shift;
+    // every wave finds the crossing wave (the first whose running total
+    // reaches need), then the crossing bin, itself
+    const int wt = per_wave_value(wtot[cur], lane);
+    const int wrun = row16_incl_scan(wt);
+    const uint64_t reach = __ballot(lane < kTopkWaves && wrun >= need);
+    int wv = reach ? (int)__builtin_ctzll(reach) : kTopkWaves - 1;  // empty: unreachable, candidates cover need
+    const int before = __builtin_amdgcn_readlane(wrun, wv) - __builtin_amdgcn_readlane(wt, wv);
+    // lane l of the crossing wave covers bins 2047-2(64 wv + l) and below
+    const int tb = kHistBins - 1 - 2 * (64 * wv + lane);
+    const int d0 = h[tb], d1 = h[tb - 1];
+    const int within = wave_incl_scan_add(d0 + d1);
+    const int above = before + within - d0 - d1;
+    const bool hit0 = above < need && above + d0 >= need;
+    const bool hit1 = !hit0 && above + d0 < need && above + d0 + d1 >= need;
+    const uint64_t m0 = __ballot(hit0), m1 = __ballot(hit1);
+    const int src = m0 ? (int)__builtin_ctzll(m0) : (int)__builtin_ctzll(m1);
+    const int src_above = __builtin_amdgcn_readlane(above, src);
+    const int src_d0 = __builtin_amdgcn_readlane(d0, src);
+    const int digit = m0 ? kHistBins - 1 - 2 * (64 * wv + src) : kHistBins - 2 - 2 * (64 * wv + src);
+    need = m0 ? need - src_above : need - src_above - src_d0;
+    prefix |= (uint32_t)digit << shift;
     mask |= (uint32_t)(nbins - 1) << shift;
-    need = pick[1];
     hi_bit = shift - 1;
-    __syncthreads();
+    cur ^= 1;
   }
   const uint32_t T = prefix;
 
-  // rounds of 1024 consecutive pages keep the output ascending
-  int gt_base = 0, eq_base = 0;
-  for (int j0 = 0; j0 < P; j0 += kTopkThreads) {
+  // rounds of 1024 consecutive pages, in page order
+  int gt_base = 0, eq_base = 0, par = 0;
+  for (int j0 = 0; j0 < P; j0 += kTopkThreads, par ^= 1) {
     const int j = j0 + tid;
     const uint32_t k = j < P ? keys[j] : 0u;
-    const int is_gt = j < P && k > T, is_eq = j < P && k == T;
-    const int packed = block_inclusive_scan(is_gt | (is_eq << 16), wsum);  // both counts <= 1024
-    const int gt_before = gt_base + (packed & 0xFFFF) - is_gt;
-    const int eq_before = eq_base + (packed >> 16) - is_eq;
-    if (is_gt) out[gt_before + min(eq_before, need)] = j;
-    else if (is_eq && eq_before < need) out[gt_before + eq_before] = j;
-    if (tid == kTopkThreads - 1) {
-      pick[0] = packed & 0xFFFF;
-      pick[1] = packed >> 16;
-    }
+    const bool is_gt = j < P && k > T, is_eq = j < P && k == T;
+    const uint64_t gm = __ballot(is_gt), em = __ballot(is_eq);
+    if (lane == 0) ctot[par][w] = __builtin_popcountll(gm) | (__builtin_popcountll(em) << 16);
     __syncthreads();
-    gt_base += pick[0];
-    eq_base += pick[1];
-    __syncthreads();
+    // both counts (< 2^16 each) scan together in one packed int
+    const int ct = per_wave_value(ctot[par], lane);
+    const int crun = row16_incl_scan(ct);
+    const int excl = __builtin_amdgcn_readlane(crun, w) - __builtin_amdgcn_readlane(ct, w);
+    const int total = __builtin_amdgcn_readlane(crun, kTopkWaves - 1);
+    const int gt_w = excl & 0xFFFF, eq_w = excl >> 16, gt_r = total & 0xFFFF, eq_r = total >> 16;
+    const int gt_before = gt_base + gt_w + lanes_below(gm);
+    const int eq_before = eq_base + eq_w + lanes_below(em);
+    // positions stay below K by construction; the guards keep every write
+    // inside the row regardless
+    const int pos_gt = gt_before + min(eq_before, need), pos_eq = gt_before + eq_before;
+    if (is_gt && pos_gt < K) out[pos_gt] = j;
+    else if (is_eq && eq_before < need && pos_eq < K) out[pos_eq] = j;
+    gt_base += gt_r;
+    eq_base += eq_r;
   }
   for (int i = K + tid; i < a.k_cap; i += kTopkThreads) out[i] = -1;
 }

@@ -71,7 +71,9 @@ def test_workspace_bytes(lib):
     assert lib.kvq_attn_workspace_bytes(0, 32, 128, 128, 0, 8) == 0
     assert lib.kvq_attn_workspace_bytes(1, 32, 128, 128, 0, 0) == 0
     pps = lib.kvq_default_pages_per_split(1, 32, 2048, 615)
-    assert 8 <= pps <= 64 and pps % 4 == 0
+    assert pps == 40   # ceil(32 * 615 / 512) = 39, rounded up to a multiple of 4
+    assert lib.kvq_default_pages_per_split(1, 4, 64, 16) == 16
+    assert lib.kvq_default_pages_per_split(64, 8, 2048, 615) == 64
 
 
 def _structs(fmt=1, page=16, d=128, H=4, B=1, maxp=8, meta=True):
