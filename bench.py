@@ -3,8 +3,9 @@
 One step = the whole hot path for one layer of the Llama-2-7B-shaped workload
 (1 sequence, 32 heads, head_dim 128, 32768 tokens in 16-token pages, INT8 per
 token, selection ratio 0.3 -> 615 of 2048 pages per head):
-  append the newest token (quantize into its page) -> refresh that page's
-  metadata -> score all pages -> top-K -> split-K attention + combine.
+  append the newest token (quantize into its page) and refresh that page's
+  metadata, fused into scoring all pages -> top-K -> split-K attention +
+  combine.
 Steps rotate over `--layers` independent copies of the layer cache (distinct
 device buffers), so a step never finds the previous step's working set in the
 256 MB Infinity Cache, as in a real decode pass over many layers.
@@ -151,8 +152,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     def one_step(i):
-        appends[i % len(layers)].run()
-        steps[i % len(layers)].run(q)
+        steps[i % len(layers)].run_with_append(appends[i % len(layers)], q)
 
     # warm-up (eager), which also fills every layer's selection
     for i in range(max(args.warmup, len(layers))):

@@ -165,6 +165,18 @@ kvq_status kvq_page_scores(const kvq_cache *cache, const kvq_seqs *seqs,
                            const uint16_t *q, int32_t num_q_heads, float *scores, void *stream);
 
 /*
+ * kvq_append_decode_scores -- kvq_append_decode followed by kvq_page_scores,
+ * in one kernel (same arguments as the two calls).  For every sequence that
+ * receives rows, seq_lens[b] must equal start_pos[b] + rows (the rows are its
+ * newest tokens).  Codes, scale/zero, metadata and scores are bit-identical to
+ * the two separate calls.
+ */
+kvq_status kvq_append_decode_scores(const kvq_cache *cache, const kvq_seqs *seqs,
+                                    const int32_t *start_pos, const int32_t *new_off, int32_t max_new,
+                                    const uint16_t *k_new, const uint16_t *v_new,
+                                    const uint16_t *q, int32_t num_q_heads, float *scores, void *stream);
+
+/*
  * kvq_topk_pages -- per (sequence b, KV head) row of `scores`, select K_b of
  * the P_b = ceil(L_b/16) pages ("TinyServe", section 3.1 phase 2; section 5.1
  * selection_ratio):

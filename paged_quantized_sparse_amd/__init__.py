@@ -7,7 +7,8 @@ There is no CPU or PyTorch fallback; if the library is missing, importing the
 entry points raises.
 
 Entry points keep the C names:
-  kvq_append_quant, kvq_append_decode, kvq_build_page_meta, kvq_page_scores, kvq_topk_pages,
+  kvq_append_quant, kvq_append_decode, kvq_append_decode_scores, kvq_build_page_meta,
+  kvq_page_scores, kvq_topk_pages,
   kvq_sparse_decode_attn, kvq_attn_workspace_bytes, kvq_default_pages_per_split
 """
 from __future__ import annotations
@@ -59,12 +60,13 @@ def lib() -> ctypes.CDLL:
         P, I, C, S = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(CacheStruct), ctypes.POINTER(SeqsStruct)
         L.kvq_append_quant.argtypes = [C, S, P, P, I, P, P, P]
         L.kvq_append_decode.argtypes = [C, S, P, P, I, P, P, P]
+        L.kvq_append_decode_scores.argtypes = [C, S, P, P, I, P, P, P, I, P, P]
         L.kvq_build_page_meta.argtypes = [C, S, P, I, P]
         L.kvq_page_scores.argtypes = [C, S, P, I, P, P]
         L.kvq_topk_pages.argtypes = [P, S, I, I, I, I, I, P, P, P]
         L.kvq_sparse_decode_attn.argtypes = [C, S, P, I, P, P, I, ctypes.c_float, I, P, P, ctypes.c_size_t, P]
-        for f in ("kvq_append_quant", "kvq_append_decode", "kvq_build_page_meta", "kvq_page_scores", "kvq_topk_pages",
-                  "kvq_sparse_decode_attn"):
+        for f in ("kvq_append_quant", "kvq_append_decode", "kvq_append_decode_scores", "kvq_build_page_meta",
+                  "kvq_page_scores", "kvq_topk_pages", "kvq_sparse_decode_attn"):
             getattr(L, f).restype = ctypes.c_int
         L.kvq_attn_workspace_bytes.argtypes = [I, I, I, I, I, I]
         L.kvq_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -183,6 +185,16 @@ def kvq_append_decode(cache: PagedCache, seqs: Seqs, start_pos, new_off, max_new
     _check("kvq_append_decode", lib().kvq_append_decode(
         ctypes.byref(cache.struct()), ctypes.byref(seqs.struct()), _ptr(start_pos), _ptr(new_off),
         int(max_new), _ptr(k), _ptr(v), _stream(stream)))
+
+
+def kvq_append_decode_scores(cache: PagedCache, seqs: Seqs, start_pos, new_off, max_new: int, k_new, v_new, q,
+                             scores, stream=None) -> None:
+    k = _half_bits(k_new) if k_new is not None else None
+    v = _half_bits(v_new) if v_new is not None else None
+    qb = _half_bits(q)
+    _check("kvq_append_decode_scores", lib().kvq_append_decode_scores(
+        ctypes.byref(cache.struct()), ctypes.byref(seqs.struct()), _ptr(start_pos), _ptr(new_off),
+        int(max_new), _ptr(k), _ptr(v), _ptr(qb), int(qb.shape[1]), _ptr(scores), _stream(stream)))
 
 
 def kvq_build_page_meta(cache: PagedCache, seqs: Seqs, page_begin=None, max_span: int = 0, stream=None) -> None:

@@ -1,0 +1,197 @@
+// append_body.h -- the decode-time append of one (sequence, KV head), as a
+// block-level device function shared by append_decode.hip and the fused
+// append + scores kernel.  Called by all 256 threads of a block.
+//
+// Writes sequence b's newest rows for KV head h into their pages (fp16 copy,
+// INT8 per token, or INT8 per 64-token group: "KV-cache layout from the
+// HBM-bandwidth viewpoint", pzsr.cn, sections 2-3; "Gemini KV cache:
+// FlashAttention-3 adaptation", uyd888.cn, chapter 1), and rebuilds the
+// metadata phi = (per-channel min, max of the decoded keys) of every page the
+// rows touch ("TinyServe", lpnh.cn, section 2.1).  The rows end the sequence,
+// so a touched page's valid tokens are those before start + rows.
+//
+// Nothing written here is read back.  Each touched page belongs to one wave
+// (page pi of the touched run to wave pi mod 4), which loads the page's older
+// tokens, quantizes the page's new rows, keeps their decoded keys in
+// registers (lane l owns channels l*E .. l*E+E-1) and so holds the page's
+// whole min/max without any exchange between waves.  The metadata is written
+// to HBM and, for a caller that scores the touched pages, to `sm_meta` in LDS.
+// Decoded INT8 keys are fmaf(code, scale, zero) exactly as every other reader
+// computes them.
+#pragma once
+
+#include "kvq_device.h"
+
+namespace kvq {
+
+constexpr int kMaxTouched = 5;  // 64 rows starting anywhere in a page touch at most 5 pages
+
+struct AppendView {
+  void* k_pages;
+  void* v_pages;
+  float* params;
+  float* meta;
+  const int32_t* block_table;
+  const int32_t* start_pos;
+  const int32_t* new_off;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int H;
+  int max_pages;
+};
+
+// Touched pages [first, first + count) of sequence b (count 0: no rows).
+__device__ __forceinline__ void touched_pages(const AppendView& a, int b, int& first, int& count) {
+  const int n = min(a.new_off[b + 1] - a.new_off[b], 64);
+  const int start = a.start_pos[b];
+  first = start / kPage;
+  count = n > 0 ? (start + n - 1) / kPage - first + 1 : 0;
+}
+
+template <int FMT, int D>
+__device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b, int h,
+                                                     float (*sm_meta)[2][D]) {
+  constexpr int E = D / 64;
+  // at most 64 rows (the documented limit; clamping keeps every index in range)
+  const int r0 = a.new_off[b], n = min(a.new_off[b + 1] - r0, 64);
+  if (n <= 0) return;  // block-uniform
+  const int start = a.start_pos[b];
+  const int j_lo = start / kPage;
+  const int npages = (start + n - 1) / kPage - j_lo + 1;
+  const int w = wave_id(), lane = lane_id();
+  const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+
+  // ---- group (scale, zero): one per (64-token group, KV head), K and V apart
+  float gk[2] = {0.0f, 0.0f}, gv[2] = {0.0f, 0.0f}, ginv[2] = {1.0f, 1.0f};
+  if constexpr (FMT == kInt8Group) {
+    float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
+    for (int e = threadIdx.x; e < n * D; e += 256) {
+      const size_t src = ((size_t)(r0 + e / D) * a.H + h) * D + e % D;
+      const float kx = half_bits_to_float(a.k_new[src]), vx = half_bits_to_float(a.v_new[src]);
+      klo = fminf(klo, kx); khi = fmaxf(khi, kx);
+      vlo = fminf(vlo, vx); vhi = fmaxf(vhi, vx);
+    }
+    klo = min_contig<64>(klo); khi = max_contig<64>(khi);
+    vlo = min_contig<64>(vlo); vhi = max_contig<64>(vhi);
+    __shared__ float red[4][4];
+    if (lane == 0) { red[w][0] = klo; red[w][1] = khi; red[w][2] = vlo; red[w][3] = vhi; }
+    __syncthreads();
+    klo = fminf(fminf(red[0][0], red[1][0]), fminf(red[2][0], red[3][0]));
+    khi = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1]));
+    vlo = fminf(fminf(red[0][2], red[1][2]), fminf(red[2][2], red[3][2]));
+    vhi = fmaxf(fmaxf(red[0][3], red[1][3]), fmaxf(red[2][3], red[3][3]));
+    quant_params(klo, khi, gk[0], ginv[0]);
+    quant_params(vlo, vhi, gv[0], ginv[1]);
+    gk[1] = klo;
+    gv[1] = vlo;
+    if (threadIdx.x < 4 && threadIdx.x * kPage < n) {  // every page holding a row of the group
+      const int phys = bt[(start + threadIdx.x * kPage) / kPage];
+      *(float4*)(a.params + ((size_t)phys * a.H + h) * 4) = make_float4(gk[0], gk[1], gv[0], gv[1]);
+    }
+  }
+
+  for (int pi = w; pi < npages; pi += 4) {  // wave-uniform
+    const int j = j_lo + pi;
+    const int phys = bt[j];
+    const size_t tile = ((size_t)phys * a.H + h) * kPage;  // first token row of the page
+    const int t_begin = max(start, j * kPage), t_end = min(start + n, (j + 1) * kPage);
+    float lo[E], hi[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) { lo[e] = INFINITY; hi[e] = -INFINITY; }
+
+    // older tokens of the page (only the first touched page has any): all 16
+    // slots are loaded at once and the slots at or past `start` masked out,
+    // so no load waits on another
+    const int nold = t_begin - j * kPage;
+    if (nold > 0) {  // wave-uniform
+      float kold[kPage][E];
+#pragma unroll
+      for (int t = 0; t < kPage; ++t) {
+        const size_t row = (tile + t) * D + lane * E;
+        if constexpr (FMT == kFp16) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) kold[t][e] = half_bits_to_float(((const uint16_t*)a.k_pages)[row + e]);
+        } else {
+          const float* p = FMT == kInt8Token ? a.params + (tile + t) * 4 : a.params + ((size_t)phys * a.H + h) * 4;
+          const float s = p[0], z = p[1];
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            kold[t][e] = __builtin_fmaf((float)((const uint8_t*)a.k_pages)[row + e], s, z);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kPage; ++t)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          lo[e] = fminf(lo[e], t < nold ? kold[t][e] : INFINITY);
+          hi[e] = fmaxf(hi[e], t < nold ? kold[t][e] : -INFINITY);
+        }
+    }
+
+    // the page's new rows
+    for (int t = t_begin; t < t_end; ++t) {
+      const size_t src = ((size_t)(r0 + t - start) * a.H + h) * D + lane * E;
+      const size_t dst = (tile + t % kPage) * D + lane * E;
+      float kdec[E];
+      if constexpr (FMT == kFp16) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint16_t kb = a.k_new[src + e];
+          ((uint16_t*)a.k_pages)[dst + e] = kb;
+          ((uint16_t*)a.v_pages)[dst + e] = a.v_new[src + e];
+          kdec[e] = half_bits_to_float(kb);
+        }
+      } else {
+        float kx[E], vx[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          kx[e] = half_bits_to_float(a.k_new[src + e]);
+          vx[e] = half_bits_to_float(a.v_new[src + e]);
+        }
+        float ks = gk[0], kz = gk[1], kinv = ginv[0], vs = gv[0], vz = gv[1], vinv = ginv[1];
+        if constexpr (FMT == kInt8Token) {
+          float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            klo = fminf(klo, kx[e]); khi = fmaxf(khi, kx[e]);
+            vlo = fminf(vlo, vx[e]); vhi = fmaxf(vhi, vx[e]);
+          }
+          klo = min_contig<64>(klo); khi = max_contig<64>(khi);
+          vlo = min_contig<64>(vlo); vhi = max_contig<64>(vhi);
+          quant_params(klo, khi, ks, kinv);
+          quant_params(vlo, vhi, vs, vinv);
+          kz = klo;
+          vz = vlo;
+          if (lane == 0) *(float4*)(a.params + (tile + t % kPage) * 4) = make_float4(ks, kz, vs, vz);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint32_t kc = quant_code(kx[e], kz, kinv);
+          ((uint8_t*)a.k_pages)[dst + e] = (uint8_t)kc;
+          ((uint8_t*)a.v_pages)[dst + e] = (uint8_t)quant_code(vx[e], vz, vinv);
+          kdec[e] = __builtin_fmaf((float)kc, ks, kz);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        lo[e] = fminf(lo[e], kdec[e]);
+        hi[e] = fmaxf(hi[e], kdec[e]);
+      }
+    }
+
+    // the page's metadata: min row then max row
+    float* m = a.meta + ((size_t)phys * a.H + h) * 2 * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      m[e] = lo[e];
+      m[D + e] = hi[e];
+      if (sm_meta) {
+        sm_meta[pi][0][lane * E + e] = lo[e];
+        sm_meta[pi][1][lane * E + e] = hi[e];
+      }
+    }
+  }
+  if (sm_meta) __syncthreads();  // block-uniform: the LDS copy is complete
+}
+
+}  // namespace kvq

@@ -1,0 +1,91 @@
+// append_scores.hip -- the decode-time append fused into page scoring.
+//
+// The scoring of page_scores.hip, with one change per (sequence, KV head)
+// row that received rows: the scoring blocks skip the pages the rows touch,
+// and one extra block per row appends the rows and rebuilds those pages'
+// metadata (append_body.h), then scores them from the metadata it still holds
+// in LDS with the same per-page arithmetic as the scorer (score_body.h), so
+// every score equals what kvq_append_decode followed by kvq_page_scores gives.
+// The append blocks come first in the grid, so they are dispatched first and
+// their dependent loads run while the scoring blocks stream metadata.
+#include "append_body.h"
+#include "kvq_internal.h"
+#include "score_body.h"
+
+namespace kvq {
+namespace {
+
+struct AppendScoreArgs {
+  AppendView ap;
+  ScoreView sc;
+  const int32_t* seq_lens;
+};
+
+// 1-D grid of (1 + ceil(max_pages / 32)) * B * H_kv blocks of 256 threads:
+// block L < B * H_kv appends for row L; the others score 32 pages each.
+template <int FMT, int D, int G>
+__global__ __launch_bounds__(256) KVQ_SCORE_OCC_ATTR void append_scores_kernel(AppendScoreArgs a, int rows) {
+  constexpr int kPerBlock = kScoreWaves * kScorePagesPerWave;
+  __shared__ float sm_meta[kMaxTouched][2][D];
+  const int L = blockIdx.x;
+  const int row = L % rows, c = L / rows - 1;  // c = -1: the row's append block
+  const int b = row / a.sc.H, g = row % a.sc.H;
+  const int P = (a.seq_lens[b] + kPage - 1) / kPage;
+  int first, count;
+  touched_pages(a.ap, b, first, count);
+  ScoreQuery<D, G> q;
+  q.load(a.sc, b, g);
+  if (c < 0) {  // block-uniform
+    if (count == 0 || P == 0) return;
+    append_rows_and_meta<FMT, D>(a.ap, b, g, sm_meta);
+    if (wave_id() == 0) {
+      constexpr int E = ScoreQuery<D, G>::E;
+      float* out = a.sc.scores + ((size_t)b * a.sc.H + g) * a.sc.max_pages;
+      for (int p = 0; p < count && first + p < P; ++p) {
+        const float best = score_from_values<D, G>(q, &sm_meta[p][0][0] + lane_id() * E);
+        if (lane_id() == 0) out[first + p] = best;
+      }
+    }
+    return;
+  }
+  const int touched = count > 0 ? first : P;  // the rows touch pages [touched, P)
+  score_pages<D, G>(a.sc, q, b, g, P, (c * kScoreWaves + wave_id()) * kScorePagesPerWave, touched);
+}
+
+template <int FMT, int D>
+hipError_t launch_g(const AppendScoreArgs& a, int rows, int G, dim3 grid, hipStream_t st) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((append_scores_kernel<FMT, D, 1>), grid, dim3(256), 0, st, a, rows); break;
+    case 2: hipLaunchKernelGGL((append_scores_kernel<FMT, D, 2>), grid, dim3(256), 0, st, a, rows); break;
+    case 4: hipLaunchKernelGGL((append_scores_kernel<FMT, D, 4>), grid, dim3(256), 0, st, a, rows); break;
+    default: hipLaunchKernelGGL((append_scores_kernel<FMT, D, 8>), grid, dim3(256), 0, st, a, rows); break;
+  }
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_d(const AppendScoreArgs& a, int d, int rows, int G, dim3 grid, hipStream_t st) {
+  return d == 64 ? launch_g<FMT, 64>(a, rows, G, grid, st) : launch_g<FMT, 128>(a, rows, G, grid, st);
+}
+
+}  // namespace
+
+hipError_t launch_append_scores(const kvq_cache& c, const kvq_seqs& s, const int32_t* start_pos,
+                                const int32_t* new_off, const uint16_t* k_new, const uint16_t* v_new,
+                                const uint16_t* q, int num_q_heads, float* scores, hipStream_t st) {
+  AppendScoreArgs a{{c.k_pages, c.v_pages, c.kv_params, c.page_meta, s.block_table, start_pos, new_off, k_new,
+                     v_new, c.num_kv_heads, s.max_pages},
+                    {c.page_meta, s.block_table, q, scores, c.num_kv_heads, num_q_heads, s.max_pages},
+                    s.seq_lens};
+  const int per_block = kScoreWaves * kScorePagesPerWave;
+  const int rows = s.batch * c.num_kv_heads;
+  const long long blocks = (1LL + (s.max_pages + per_block - 1) / per_block) * rows;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)blocks);
+  const int G = num_q_heads / c.num_kv_heads;
+  if (c.format == KVQ_FP16) return launch_d<kFp16>(a, c.head_dim, rows, G, grid, st);
+  if (c.format == KVQ_INT8_TOKEN) return launch_d<kInt8Token>(a, c.head_dim, rows, G, grid, st);
+  return launch_d<kInt8Group>(a, c.head_dim, rows, G, grid, st);
+}
+
+}  // namespace kvq

@@ -77,6 +77,22 @@ kvq_status kvq_append_decode(const kvq_cache* cache, const kvq_seqs* seqs, const
   return from_hip(kvq::launch_append_decode(*cache, *seqs, start_pos, new_off, k_new, v_new, (hipStream_t)stream));
 }
 
+kvq_status kvq_append_decode_scores(const kvq_cache* cache, const kvq_seqs* seqs, const int32_t* start_pos,
+                                    const int32_t* new_off, int32_t max_new, const uint16_t* k_new,
+                                    const uint16_t* v_new, const uint16_t* q, int32_t num_q_heads, float* scores,
+                                    void* stream) {
+  kvq_status st = check_cache(cache, true);
+  if (st != KVQ_OK) return st;
+  if ((st = check_seqs(seqs)) != KVQ_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != KVQ_OK) return st;
+  if (!q || !scores || !aligned16(q)) return KVQ_ERR_INVALID_ARG;
+  if (!start_pos || !new_off || max_new < 0) return KVQ_ERR_INVALID_ARG;
+  if (max_new > KVQ_DECODE_MAX_ROWS) return KVQ_ERR_UNSUPPORTED;
+  if (max_new > 0 && (!k_new || !v_new)) return KVQ_ERR_INVALID_ARG;
+  return from_hip(kvq::launch_append_scores(*cache, *seqs, start_pos, new_off, k_new, v_new, q, num_q_heads, scores,
+                                            (hipStream_t)stream));
+}
+
 kvq_status kvq_build_page_meta(const kvq_cache* cache, const kvq_seqs* seqs, const int32_t* page_begin,
                                int32_t max_span, void* stream) {
   kvq_status st = check_cache(cache, true);

@@ -19,6 +19,10 @@ hipError_t launch_append_decode(const kvq_cache& c, const kvq_seqs& s, const int
                                 const int32_t* new_off, const uint16_t* k_new, const uint16_t* v_new,
                                 hipStream_t st);
 
+hipError_t launch_append_scores(const kvq_cache& c, const kvq_seqs& s, const int32_t* start_pos,
+                                const int32_t* new_off, const uint16_t* k_new, const uint16_t* v_new,
+                                const uint16_t* q, int num_q_heads, float* scores, hipStream_t st);
+
 hipError_t launch_page_meta(const kvq_cache& c, const kvq_seqs& s, const int32_t* page_begin,
                             int max_span, hipStream_t st);
 

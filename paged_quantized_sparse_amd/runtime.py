@@ -14,7 +14,8 @@ from typing import Callable
 import numpy as np
 import torch
 
-from . import (KVQ_INT8_GROUP64, PAGE_SIZE, PagedCache, Seqs, kvq_append_decode, kvq_append_quant,
+from . import (KVQ_INT8_GROUP64, PAGE_SIZE, PagedCache, Seqs, kvq_append_decode, kvq_append_decode_scores,
+               kvq_append_quant,
                kvq_attn_workspace_bytes, kvq_build_page_meta, kvq_default_pages_per_split, kvq_page_scores,
                kvq_sparse_decode_attn, kvq_topk_pages, num_selected)
 
@@ -149,4 +150,17 @@ class DecodeStep:
         if self.dense:
             return self.attend(q, None, None, stream)
         self.select(q, stream)
+        return self.attend(q, self.sel_pages, self.sel_count, stream)
+
+    def run_with_append(self, app: "DecodeAppend", q, stream=None) -> torch.Tensor:
+        """The whole decode step: append the newest rows (app) and score in
+        one kernel, then top-K and attention."""
+        if self.dense:
+            app.run(stream)
+            return self.attend(q, None, None, stream)
+        kvq_append_decode_scores(self.cache, self.seqs, app.start, app.off, app.max_new, app.k_new, app.v_new, q,
+                                 self.scores, stream)
+        rn, rd, kf = self.ratio
+        kvq_topk_pages(self.scores, self.seqs, self.cache.num_kv_heads, rn, rd, kf, self.sel_pages,
+                       self.sel_count, stream)
         return self.attend(q, self.sel_pages, self.sel_count, stream)

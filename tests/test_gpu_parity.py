@@ -424,3 +424,53 @@ def test_append_decode_equals_separate_calls_and_oracle(fmt, rows):
     if fmt != workloads.FMT_FP16:
         assert np.array_equal(to_np(a.kv_params).view(np.uint32), oc.params.view(np.uint32))
     assert np.array_equal(to_np(a.page_meta), oc.meta)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_append_decode_scores_equals_separate_calls(n):
+    """kvq_append_decode_scores (append + metadata of the touched pages fused
+    into scoring) leaves the same cache and writes the same scores, bit for
+    bit, as kvq_append_decode followed by kvq_page_scores; the step built on it
+    matches the oracle."""
+    kvq, runtime = kvq_mod()
+    w = workloads.small(n)
+    table, n_phys = w.block_table()
+    lens = w.seq_lens()
+    src = lambda b: (w.keys(b), w.values(b))  # noqa: E731
+    q = torch.from_numpy(w.query().view(np.int16)).cuda()
+    runs = []
+    for fused in (True, False):
+        cache, seqs = runtime.build_cache(w.fmt, n_phys, w.num_kv_heads, w.head_dim, table, lens, src,
+                                          prefill_lens=lens - 1)
+        app = runtime.DecodeAppend(cache, seqs, lens, src)
+        st = runtime.DecodeStep(cache, seqs, w.num_q_heads, w.ratio_num, w.ratio_den, w.k_fixed)
+        if fused:
+            kvq.kvq_append_decode_scores(cache, seqs, app.start, app.off, app.max_new, app.k_new, app.v_new, q,
+                                         st.scores)
+        else:
+            app.run()
+            kvq.kvq_page_scores(cache, seqs, q, st.scores)
+        torch.cuda.synchronize()
+        runs.append((cache, st.scores.clone()))
+    (ca, sa), (cb, sb) = runs
+    assert torch.equal(sa, sb)
+    for x, y in [(ca.k_pages, cb.k_pages), (ca.v_pages, cb.v_pages), (ca.page_meta, cb.page_meta)]:
+        assert torch.equal(x, y)
+    if w.fmt != workloads.FMT_FP16:
+        assert torch.equal(ca.kv_params, cb.kv_params)
+    # the whole fused step against the oracle
+    cache, seqs = runtime.build_cache(w.fmt, n_phys, w.num_kv_heads, w.head_dim, table, lens, src,
+                                      prefill_lens=lens - 1)
+    app = runtime.DecodeAppend(cache, seqs, lens, src)
+    st = runtime.DecodeStep(cache, seqs, w.num_q_heads, w.ratio_num, w.ratio_den, w.k_fixed, dense=w.is_dense())
+    out = to_np(st.run_with_append(app, q)).astype(np.float64)
+    oc, _ = oracle.build_cache(w)
+    if w.is_dense():
+        want = oracle.attention(oc, table, lens, w.query())
+    else:
+        osc, osel, ocnt, _ = oracle.decode_step(oc, table, lens, w.query(), w.ratio_num, w.ratio_den, w.k_fixed,
+                                                st.k_cap)
+        gsel, gcnt = to_np(st.sel_pages), to_np(st.sel_count)
+        check_selection_near_ties(gsel, gcnt, osc, osel, ocnt)
+        want = oracle.attention(oc, table, lens, w.query(), gsel, gcnt)
+    assert np.abs(out - want).max() <= ATTN_ATOL
