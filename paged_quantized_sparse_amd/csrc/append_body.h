@@ -40,14 +40,6 @@ struct AppendView {
   int max_pages;
 };
 
-// Touched pages [first, first + count) of sequence b (count 0: no rows).
-__device__ __forceinline__ void touched_pages(const AppendView& a, int b, int& first, int& count) {
-  const int n = min(a.new_off[b + 1] - a.new_off[b], 64);
-  const int start = a.start_pos[b];
-  first = start / kPage;
-  count = n > 0 ? (start + n - 1) / kPage - first + 1 : 0;
-}
-
 template <int FMT, int D>
 __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b, int h,
                                                      float (*sm_meta)[2][D]) {

@@ -30,12 +30,27 @@ __global__ __launch_bounds__(256) KVQ_SCORE_OCC_ATTR void append_scores_kernel(A
   const int L = blockIdx.x;
   const int row = L % rows, c = L / rows - 1;  // c = -1: the row's append block
   const int b = row / a.sc.H, g = row % a.sc.H;
-  const int P = (a.seq_lens[b] + kPage - 1) / kPage;
-  int first, count;
-  touched_pages(a.ap, b, first, count);
+  const int j0 = (c * kScoreWaves + wave_id()) * kScorePagesPerWave;
+  const int bt_v = score_table_load(a.sc, b, j0);  // issued first; unused by the append block
+  // per-sequence values as pending vector loads (see vload_i32)
+  const int len_v = vload_i32(a.seq_lens, b);
+  const int off0_v = vload_i32(a.ap.new_off, b), off1_v = vload_i32(a.ap.new_off, b + 1);
+  const int start_v = vload_i32(a.ap.start_pos, b);
   ScoreQuery<D, G> q;
   q.load(a.sc, b, g);
+  __builtin_amdgcn_sched_barrier(0);
+  // the touched pages [first, first + count) of the rows (count 0: no rows); at most 64 rows,
+  // as the append itself clamps them
+  auto touched = [&](int& P, int& first, int& count) {
+    P = (__builtin_amdgcn_readfirstlane(len_v) + kPage - 1) / kPage;
+    const int n = min(__builtin_amdgcn_readfirstlane(off1_v) - __builtin_amdgcn_readfirstlane(off0_v), 64);
+    const int start = __builtin_amdgcn_readfirstlane(start_v);
+    first = start / kPage;
+    count = n > 0 ? (start + n - 1) / kPage - first + 1 : 0;
+  };
   if (c < 0) {  // block-uniform
+    int P, first, count;
+    touched(P, first, count);
     if (count == 0 || P == 0) return;
     append_rows_and_meta<FMT, D>(a.ap, b, g, sm_meta);
     if (wave_id() == 0) {
@@ -48,8 +63,11 @@ __global__ __launch_bounds__(256) KVQ_SCORE_OCC_ATTR void append_scores_kernel(A
     }
     return;
   }
-  const int touched = count > 0 ? first : P;  // the rows touch pages [touched, P)
-  score_pages<D, G>(a.sc, q, b, g, P, (c * kScoreWaves + wave_id()) * kScorePagesPerWave, touched);
+  score_pages<D, G>(a.sc, q, b, g, j0, bt_v, [&](int& P, int& skip_from) {
+    int first, count;
+    touched(P, first, count);
+    skip_from = count > 0 ? first : P;  // the rows touch pages [first, P)
+  });
 }
 
 template <int FMT, int D>

@@ -16,11 +16,15 @@ struct ScoreArgs {
 template <int D, int G>
 __global__ __launch_bounds__(256) KVQ_SCORE_OCC_ATTR void page_scores_kernel(ScoreArgs a) {
   const int b = blockIdx.z, g = blockIdx.y;
-  const int P = (a.seq_lens[b] + kPage - 1) / kPage;
   const int j0 = (blockIdx.x * kScoreWaves + wave_id()) * kScorePagesPerWave;
+  const int bt_v = score_table_load(a.v, b, j0);
+  const int len_v = vload_i32(a.seq_lens, b);
   ScoreQuery<D, G> q;
   q.load(a.v, b, g);
-  score_pages<D, G>(a.v, q, b, g, P, j0, P);
+  score_pages<D, G>(a.v, q, b, g, j0, bt_v, [&](int& P, int& skip_from) {
+    P = (__builtin_amdgcn_readfirstlane(len_v) + kPage - 1) / kPage;
+    skip_from = P;
+  });
 }
 
 template <int D>

@@ -34,6 +34,18 @@ struct ScoreView {
   int max_pages;
 };
 
+// A per-sequence value read with a vector load and left pending: the caller
+// turns it into a uniform value (readfirstlane) only after the scorer has
+// issued its block-table load.  A scalar load would not do: scalar loads
+// return out of order, so the compiler waits for all of them (kernel
+// arguments included) before using any, which would put this load in front
+// of the table load instead of beside it.
+__device__ __forceinline__ int vload_i32(const int32_t* p, int i) {
+  int zero;  // a zero the compiler cannot see as uniform, so the load stays a vector load
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  return p[i + zero];
+}
+
 // This lane's query coefficients: max(q, 0) on the max row, min(q, 0) on the min row.
 template <int D, int G>
 struct ScoreQuery {
@@ -72,31 +84,42 @@ __device__ __forceinline__ float score_from_values(const ScoreQuery<D, G>& q, co
   return best;
 }
 
-// The calling wave scores pages j0 .. j0+7 of row (b, g): pages below
-// min(P, skip_from) get their score, pages at or past P (and below max_pages)
-// get -inf, pages in [skip_from, P) are left to another writer.  All loads
-// are issued before any page is reduced.
-template <int D, int G>
-__device__ __forceinline__ void score_pages(const ScoreView& a, const ScoreQuery<D, G>& q, int b, int g, int P,
-                                            int j0, int skip_from) {
+// Block-table entries of pages j0 .. j0+7 of sequence b in one vector load:
+// lane k (mod 8) holds page j0 + k's entry (the index clamped into the row).
+__device__ __forceinline__ int score_table_load(const ScoreView& a, int b, int j0) {
+  const int j = min(max(j0 + (lane_id() & 7), 0), a.max_pages - 1);
+  return a.block_table[(size_t)b * a.max_pages + j];
+}
+
+// The calling wave scores pages j0 .. j0+7 of row (b, g), given their table
+// entries bt_v from score_table_load: pages below min(P, skip_from) get their
+// score, pages at or past P (and below max_pages) get -inf, pages in
+// [skip_from, P) are left to another writer.  P and skip_from come from
+// `bounds(P, skip_from)`, called only here, so the caller's loads of them and
+// the table load are in flight together.  A page that is not scored reads
+// physical page 0's metadata instead of its own, so every load is
+// unconditional.  All loads are issued before any page is reduced.
+template <int D, int G, typename Bounds>
+__device__ __forceinline__ void score_pages(const ScoreView& a, const ScoreQuery<D, G>& q, int b, int g, int j0,
+                                            int bt_v, Bounds bounds) {
   constexpr int E = ScoreQuery<D, G>::E;
   const int lane = lane_id();
-  const int live = min(P, skip_from);
   float* out = a.scores + ((size_t)b * a.H + g) * a.max_pages;
+  __builtin_amdgcn_sched_barrier(0);
+  int P, skip_from;
+  bounds(P, skip_from);
+  const int live = min(P, skip_from);
   float vals[kScorePagesPerWave][E];
 #pragma unroll
   for (int k = 0; k < kScorePagesPerWave; ++k) {
-    const int j = j0 + k;
-    if (j < live) {
-      const int phys = a.block_table[(size_t)b * a.max_pages + j];
-      const float* m = a.meta + ((size_t)phys * a.H + g) * 2 * D + lane * E;
-      if constexpr (E == 4) {
-        const float4 v = *(const float4*)m;
-        vals[k][0] = v.x; vals[k][1] = v.y; vals[k][2] = v.z; vals[k][3] = v.w;
-      } else {
-        const float2 v = *(const float2*)m;
-        vals[k][0] = v.x; vals[k][1] = v.y;
-      }
+    const int ph = j0 + k < live ? __builtin_amdgcn_readlane(bt_v, k) : 0;
+    const float* m = a.meta + ((size_t)ph * a.H + g) * 2 * D + lane * E;
+    if constexpr (E == 4) {
+      const float4 v = *(const float4*)m;
+      vals[k][0] = v.x; vals[k][1] = v.y; vals[k][2] = v.z; vals[k][3] = v.w;
+    } else {
+      const float2 v = *(const float2*)m;
+      vals[k][0] = v.x; vals[k][1] = v.y;
     }
   }
 #pragma unroll
