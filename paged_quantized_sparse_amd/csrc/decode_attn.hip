@@ -129,23 +129,20 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
   const int first = s * a.pps;
   const int w = wave_id();
   const int lane = lane_id();
-  // Speculative gather of this wave's first 64 selected page ids, issued
-  // together with the count loads (any index below k_cap is in bounds), so
-  // the tile loads wait on two dependent loads (selection, block table)
-  // instead of three.
-  int jlog_spec = 0;
+  // Prologue, three levels of dependent loads.  Level 1, issued together and
+  // unconditionally: this lane's selection slot (first + w + lane * NW, the
+  // wave's first 64 pages), the sequence length, the selected count and the
+  // query.  Level 2: the block-table entry of the slot's page.  Level 3: the
+  // first tiles.  Indices are clamped into their arrays, so a slot past the
+  // row's count reads some entry of the row and is never used; with no
+  // selection (all pages) the slot load reads the block table and is replaced
+  // by the slot index itself.
+  const bool sparse = a.sel_pages != nullptr;
   const int idx0 = first + w + lane * NW;
-  if (a.sel_pages) {
-    if (idx0 < a.k_cap && lane * NW < a.pps) jlog_spec = a.sel_pages[(size_t)row * a.k_cap + idx0];
-  } else {
-    jlog_spec = idx0;
-  }
-  const int L = a.seq_lens[b];
-  const int P = (L + kPage - 1) / kPage;
-  const int K = a.sel_pages ? a.sel_count[row] : P;
-  if (first >= K) return;
-  const int n = min(a.pps, K - first);
-
+  const int slot_raw = sparse ? vload_i32(a.sel_pages, (size_t)row * a.k_cap + min(idx0, a.k_cap - 1))
+                              : vload_i32(a.block_table, (size_t)b * a.max_pages + min(idx0, a.max_pages - 1));
+  const int len_v = vload_i32(a.seq_lens, b);
+  const int cnt_v = vload_i32(sparse ? a.sel_count : a.seq_lens, sparse ? row : b);
   const int tg = lane / LPT;  // token group
   const int cc = lane % LPT;  // channel chunk
   const int ch0 = cc * CH;
@@ -169,6 +166,16 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
     }
     qsum[hh] = acc;
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep every level-1 load ahead of the first use below
+
+  const int L = __builtin_amdgcn_readfirstlane(len_v);
+  const int P = (L + kPage - 1) / kPage;
+  const int K = sparse ? __builtin_amdgcn_readfirstlane(cnt_v) : P;
+  if (first >= K) return;
+  const int n = min(a.pps, K - first);
+  // level 2 for the wave's first 64 pages
+  const int jlog0 = sparse ? min(max(slot_raw, 0), a.max_pages - 1) : min(idx0, a.max_pages - 1);
+  const int phys0 = vload_i32(a.block_table, (size_t)b * a.max_pages + jlog0);
 
   // ---- per-lane online softmax state
   const int nw = n > w ? (n - w + NW - 1) / NW : 0;
@@ -305,11 +312,11 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
   };
 
   for (int k0 = 0; k0 < nw; k0 += 64) {
-    // page ids with one lane each (the first 64 were gathered speculatively)
-    int jlog_v = 0, phys_v = 0;
-    if (k0 + lane < nw) {
-      const int idx = first + w + (k0 + lane) * NW;
-      jlog_v = k0 == 0 ? jlog_spec : (a.sel_pages ? a.sel_pages[(size_t)row * a.k_cap + idx] : idx);
+    // page ids with one lane each (the first 64 come from the prologue)
+    int jlog_v = jlog0, phys_v = phys0;
+    if (k0 > 0) {  // wave-uniform; only when a split gives a wave more than 64 pages
+      const int idx = min(first + w + (k0 + lane) * NW, K - 1);
+      jlog_v = sparse ? min(max(a.sel_pages[(size_t)row * a.k_cap + idx], 0), a.max_pages - 1) : idx;
       phys_v = a.block_table[(size_t)b * a.max_pages + jlog_v];
     }
     const int cnt = min(64, nw - k0);

@@ -120,6 +120,17 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// A per-sequence (uniform) value read with a vector load, to be made uniform
+// with readfirstlane where it is first needed.  A scalar load would do, but
+// scalar loads return out of order, so the compiler waits for all of them
+// (kernel arguments included) before using any; as a vector load it stays in
+// flight beside the other vector loads issued with it.
+__device__ __forceinline__ int vload_i32(const int32_t* p, size_t i) {
+  int zero;  // a zero the compiler cannot see as uniform, so the load stays a vector load
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  return p[i + zero];
+}
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 

@@ -34,18 +34,6 @@ struct ScoreView {
   int max_pages;
 };
 
-// A per-sequence value read with a vector load and left pending: the caller
-// turns it into a uniform value (readfirstlane) only after the scorer has
-// issued its block-table load.  A scalar load would not do: scalar loads
-// return out of order, so the compiler waits for all of them (kernel
-// arguments included) before using any, which would put this load in front
-// of the table load instead of beside it.
-__device__ __forceinline__ int vload_i32(const int32_t* p, int i) {
-  int zero;  // a zero the compiler cannot see as uniform, so the load stays a vector load
-  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-  return p[i + zero];
-}
-
 // This lane's query coefficients: max(q, 0) on the max row, min(q, 0) on the min row.
 template <int D, int G>
 struct ScoreQuery {
