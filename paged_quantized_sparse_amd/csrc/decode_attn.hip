@@ -74,47 +74,74 @@ __device__ __forceinline__ float byte_to_float(uint32_t w, int i) { return (floa
 __device__ __forceinline__ half2v as_half2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 
 // grid (B * Hq), 256 threads: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
-// with M = max_s m_s.  Threads split the splits; loads are unrolled so a
-// thread keeps several partials in flight.
+// with M = max_s m_s.  Thread (part, c) takes channel c of splits part,
+// part + PARTS, ...: it loads eight splits' (m, l, acc) at once (indices past
+// the row's splits re-read its last split and are masked), together with the
+// split count, and merges them online; the PARTS partial merges then meet in
+// LDS.  So the block waits on one round of loads, not two.
 template <int D, int G>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   constexpr int PARTS = 256 / D;
-  __shared__ float red[4];
-  __shared__ float sm_num[PARTS][D];
-  __shared__ float sm_den[PARTS];
+  constexpr int U = 8;  // splits in flight per thread
+  __shared__ float sm_m[PARTS][D], sm_num[PARTS][D], sm_den[PARTS][D];
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int row = b * a.H + h / G;
   const int tid = threadIdx.x;
+  const int c = tid % D, part = tid / D;
   const float* ml = a.part_ml + (size_t)bh * a.max_splits * 2;
   const float* pa = a.part_acc + (size_t)bh * a.max_splits * D;
-  // the first 256 split maxima are loaded alongside the split count
-  const float m_spec = tid < a.max_splits ? ml[2 * tid] : -INFINITY;
-  const int P = (a.seq_lens[b] + kPage - 1) / kPage;
-  const int K = a.sel_pages ? a.sel_count[row] : P;
-  const int ns = (K + a.pps - 1) / a.pps;
-  float M = tid < ns ? m_spec : -INFINITY;
-  for (int s = tid + 256; s < ns; s += 256) M = fmaxf(M, ml[2 * s]);
-  M = max_contig<64>(M);
-  if (lane_id() == 0) red[wave_id()] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const int c = tid % D, part = tid / D;
-  float num = 0.0f, den = 0.0f;
-#pragma unroll 4
-  for (int s = part; s < ns; s += PARTS) {
-    const float2 mls = *(const float2*)(ml + 2 * s);
-    const float f = mls.x == -INFINITY ? 0.0f : exp2f(mls.x - M);
-    num = __builtin_fmaf(f, pa[(size_t)s * D + c], num);
-    den = __builtin_fmaf(f, mls.y, den);
+  const int32_t* cnt_p = a.sel_pages ? a.sel_count + row : a.seq_lens + b;  // a select, not a branch
+  const int cnt_v = vload_i32(cnt_p, 0);
+  float2 mlv[U];
+  float av[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {  // speculative: the first U splits of this part
+    const int sp = min(part + u * PARTS, a.max_splits - 1);
+    mlv[u] = *(const float2*)(ml + 2 * sp);
+    av[u] = pa[(size_t)sp * D + c];
   }
+  __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the count is waited for
+  // with every page selected cnt_p points at the length, so K = P either way
+  // (using the value on both paths keeps the load where it is issued)
+  const int cnt = __builtin_amdgcn_readfirstlane(cnt_v);
+  const int K = a.sel_pages ? cnt : (cnt + kPage - 1) / kPage;
+  const int ns = (K + a.pps - 1) / a.pps;
+  float M = -INFINITY, num = 0.0f, den = 0.0f;
+  for (int s0 = 0;; s0 += U * PARTS) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float ms = s0 + part + u * PARTS < ns ? mlv[u].x : -INFINITY;
+      const float Mn = fmaxf(M, ms);
+      const float fo = M == -INFINITY ? 0.0f : exp2f(M - Mn);
+      const float fs = ms == -INFINITY ? 0.0f : exp2f(ms - Mn);
+      num = __builtin_fmaf(fs, av[u], num * fo);
+      den = __builtin_fmaf(fs, mlv[u].y, den * fo);
+      M = Mn;
+    }
+    if (s0 + U * PARTS >= ns) break;  // block-uniform
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sp = min(s0 + U * PARTS + part + u * PARTS, a.max_splits - 1);
+      mlv[u] = *(const float2*)(ml + 2 * sp);
+      av[u] = pa[(size_t)sp * D + c];
+    }
+  }
+  sm_m[part][c] = M;
   sm_num[part][c] = num;
-  if (c == 0) sm_den[part] = den;
+  sm_den[part][c] = den;
   __syncthreads();
   if (part == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < PARTS; ++p) Mt = fmaxf(Mt, sm_m[p][c]);
     float n = 0.0f, dd = 0.0f;
 #pragma unroll
-    for (int p = 0; p < PARTS; ++p) { n += sm_num[p][c]; dd += sm_den[p]; }
+    for (int p = 0; p < PARTS; ++p) {
+      const float f = sm_m[p][c] == -INFINITY ? 0.0f : exp2f(sm_m[p][c] - Mt);
+      n = __builtin_fmaf(f, sm_num[p][c], n);
+      dd = __builtin_fmaf(f, sm_den[p][c], dd);
+    }
     a.out[(size_t)bh * D + c] = dd > 0.0f ? n / dd : 0.0f;
   }
 }
@@ -142,7 +169,8 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
   const int slot_raw = sparse ? vload_i32(a.sel_pages, (size_t)row * a.k_cap + min(idx0, a.k_cap - 1))
                               : vload_i32(a.block_table, (size_t)b * a.max_pages + min(idx0, a.max_pages - 1));
   const int len_v = vload_i32(a.seq_lens, b);
-  const int cnt_v = vload_i32(sparse ? a.sel_count : a.seq_lens, sparse ? row : b);
+  const int32_t* cnt_p = sparse ? a.sel_count + row : a.seq_lens + b;  // a select, not a branch
+  const int cnt_v = vload_i32(cnt_p, 0);
   const int tg = lane / LPT;  // token group
   const int cc = lane % LPT;  // channel chunk
   const int ch0 = cc * CH;
@@ -170,7 +198,10 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
 
   const int L = __builtin_amdgcn_readfirstlane(len_v);
   const int P = (L + kPage - 1) / kPage;
-  const int K = sparse ? __builtin_amdgcn_readfirstlane(cnt_v) : P;
+  // with every page selected cnt_p points at the length, so K = P either way
+  // (using the value on both paths keeps the load where it is issued)
+  const int cnt = __builtin_amdgcn_readfirstlane(cnt_v);
+  const int K = sparse ? cnt : (cnt + kPage - 1) / kPage;
   if (first >= K) return;
   const int n = min(a.pps, K - first);
   // level 2 for the wave's first 64 pages
