@@ -12,9 +12,12 @@
 // dependent steps, so the block is built for latency: cross-lane work is DPP
 // and ballots (no LDS shuffles), histograms are double-buffered so zeroing the
 // next one overlaps the current pass, and every wave finds the chosen bin
-// itself instead of waiting for a broadcast -- two barriers per pass.  Rounds
-// of 1024 pages in page order then write every key > T and the first `need`
-// keys == T, ascending.
+// itself instead of waiting for a broadcast -- two barriers per pass.  The
+// passes stop early once the chosen bin holds exactly the keys still needed:
+// then every key of that bin is taken, whatever its unresolved low bits.
+// Rounds of 1024 pages in page order then write every key above the chosen
+// prefix (compared on the resolved bits) and the first `need` keys on it,
+// ascending.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -175,20 +178,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     const int src = m0 ? (int)__builtin_ctzll(m0) : (int)__builtin_ctzll(m1);
     const int src_above = __builtin_amdgcn_readlane(above, src);
     const int src_d0 = __builtin_amdgcn_readlane(d0, src);
+    const int src_d1 = __builtin_amdgcn_readlane(d1, src);
     const int digit = m0 ? kHistBins - 1 - 2 * (64 * wv + src) : kHistBins - 2 - 2 * (64 * wv + src);
     need = m0 ? need - src_above : need - src_above - src_d0;
     prefix |= (uint32_t)digit << shift;
     mask |= (uint32_t)(nbins - 1) << shift;
     hi_bit = shift - 1;
     cur ^= 1;
+    if ((m0 ? src_d0 : src_d1) == need) break;  // uniform: the whole bin is taken
   }
+  // selected: every key whose resolved bits exceed the prefix, and the first
+  // `need` keys whose resolved bits equal it
   const uint32_t T = prefix;
 
   // rounds of 1024 consecutive pages, in page order
   int gt_base = 0, eq_base = 0, par = 0;
   for (int j0 = 0; j0 < P; j0 += kTopkThreads, par ^= 1) {
     const int j = j0 + tid;
-    const uint32_t k = j < P ? keys[j] : 0u;
+    const uint32_t k = j < P ? keys[j] & mask : 0u;
     const bool is_gt = j < P && k > T, is_eq = j < P && k == T;
     const uint64_t gm = __ballot(is_gt), em = __ballot(is_eq);
     if (lane == 0) ctot[par][w] = __builtin_popcountll(gm) | (__builtin_popcountll(em) << 16);
