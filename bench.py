@@ -220,7 +220,7 @@ def main() -> int:
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     attn_gbs = kv_b / (attn_us * 1e-6) / 1e9
 
-    # streaming-read ceiling of this GPU (2 GiB fp32 sum), for context
+    # for context: what torch's own reduction kernel reads per second (2 GiB fp32 sum)
     big = torch.empty(1 << 29, dtype=torch.float32, device=dev).fill_(1.0)
     big.sum()
     torch.cuda.synchronize()
@@ -270,7 +270,7 @@ def main() -> int:
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if args.config == 4 and not args.pages_per_split else None,
                      "algorithmic_bytes": kv_b, "us_per_launch": round(attn_us, 2)},
-        "stream_read_ceiling_gbs": round(read_gbs, 1),
+        "torch_sum_2gib_read_gbs": round(read_gbs, 1),
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
