@@ -54,8 +54,9 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 #define KVQ_PAGE_SIZE 16
+#define KVQ_SELECT_MAX_PAGES 2048 /* longest row (pages) kvq_select_decode_attn takes */
 
 typedef enum {
     KVQ_OK = 0,
@@ -215,6 +216,30 @@ kvq_status kvq_topk_pages(const float *scores, const kvq_seqs *seqs, int32_t num
 kvq_status kvq_sparse_decode_attn(const kvq_cache *cache, const kvq_seqs *seqs,
                                   const uint16_t *q, int32_t num_q_heads,
                                   const int32_t *sel_pages, const int32_t *sel_count, int32_t k_cap,
+                                  float sm_scale, int32_t pages_per_split,
+                                  float *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * kvq_select_decode_attn -- kvq_topk_pages and kvq_sparse_decode_attn in one
+ * call: every attention block selects the top-K pages of its (sequence, KV
+ * head) row from `scores` by exactly the rule of kvq_topk_pages and attends
+ * to its share of them, so the selection costs no launch of its own.  out
+ * equals, bit for bit, kvq_sparse_decode_attn over the selection
+ * kvq_topk_pages makes from the same scores, with the same pages_per_split.
+ *   scores    : [B][H_kv][max_pages] fp32 (as kvq_page_scores writes them)
+ *   sel_pages : [B][H_kv][k_cap] int32 out, or NULL: the selection, as
+ *               kvq_topk_pages writes it; sel_count [B][H_kv] out likewise
+ *               (both NULL or both given).
+ * k_cap must be >= K for P = max_pages (KVQ_ERR_INVALID_ARG); ws is sized by
+ * kvq_attn_workspace_bytes(..., k_cap, pages_per_split).  max_pages <=
+ * KVQ_SELECT_MAX_PAGES, and the block's LDS (pages_per_split * 4 bytes on top
+ * of its fixed use) must fit the device (else KVQ_ERR_UNSUPPORTED); longer
+ * rows take kvq_topk_pages and kvq_sparse_decode_attn.
+ */
+kvq_status kvq_select_decode_attn(const kvq_cache *cache, const kvq_seqs *seqs,
+                                  const uint16_t *q, int32_t num_q_heads, const float *scores,
+                                  int32_t ratio_num, int32_t ratio_den, int32_t k_fixed, int32_t k_cap,
+                                  int32_t *sel_pages, int32_t *sel_count,
                                   float sm_scale, int32_t pages_per_split,
                                   float *out, void *ws, size_t ws_bytes, void *stream);
 

@@ -9,7 +9,7 @@ entry points raises.
 Entry points keep the C names:
   kvq_append_quant, kvq_append_decode, kvq_append_decode_scores, kvq_build_page_meta,
   kvq_page_scores, kvq_topk_pages,
-  kvq_sparse_decode_attn, kvq_attn_workspace_bytes, kvq_default_pages_per_split
+  kvq_sparse_decode_attn, kvq_select_decode_attn, kvq_attn_workspace_bytes, kvq_default_pages_per_split
 """
 from __future__ import annotations
 
@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(HERE, "libkvq.so")
 
 KVQ_FP16, KVQ_INT8_TOKEN, KVQ_INT8_GROUP64 = 0, 1, 2
 PAGE_SIZE = 16
+SELECT_MAX_PAGES = 2048  # KVQ_SELECT_MAX_PAGES: longest row kvq_select_decode_attn takes
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
            3: "workspace missing or too small", 4: "HIP launch failed"}
 
@@ -65,8 +66,10 @@ def lib() -> ctypes.CDLL:
         L.kvq_page_scores.argtypes = [C, S, P, I, P, P]
         L.kvq_topk_pages.argtypes = [P, S, I, I, I, I, I, P, P, P]
         L.kvq_sparse_decode_attn.argtypes = [C, S, P, I, P, P, I, ctypes.c_float, I, P, P, ctypes.c_size_t, P]
+        L.kvq_select_decode_attn.argtypes = [C, S, P, I, P, I, I, I, I, P, P, ctypes.c_float, I, P, P,
+                                             ctypes.c_size_t, P]
         for f in ("kvq_append_quant", "kvq_append_decode", "kvq_append_decode_scores", "kvq_build_page_meta",
-                  "kvq_page_scores", "kvq_topk_pages", "kvq_sparse_decode_attn"):
+                  "kvq_page_scores", "kvq_topk_pages", "kvq_sparse_decode_attn", "kvq_select_decode_attn"):
             getattr(L, f).restype = ctypes.c_int
         L.kvq_attn_workspace_bytes.argtypes = [I, I, I, I, I, I]
         L.kvq_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -234,6 +237,17 @@ def kvq_sparse_decode_attn(cache: PagedCache, seqs: Seqs, q, sel_pages, sel_coun
         ctypes.byref(cache.struct()), ctypes.byref(seqs.struct()), _ptr(qb), int(qb.shape[1]),
         _ptr(sel_pages), _ptr(sel_count), k_cap, float(sm_scale), int(pages_per_split), _ptr(out),
         _ptr(workspace), int(workspace.numel() * workspace.element_size()), _stream(stream)))
+
+
+def kvq_select_decode_attn(cache: PagedCache, seqs: Seqs, q, scores, ratio_num: int, ratio_den: int, k_fixed: int,
+                           k_cap: int, out, workspace, sm_scale: float, pages_per_split: int = 0, stream=None, *,
+                           sel_pages=None, sel_count=None) -> None:
+    qb = _half_bits(q)
+    _check("kvq_select_decode_attn", lib().kvq_select_decode_attn(
+        ctypes.byref(cache.struct()), ctypes.byref(seqs.struct()), _ptr(qb), int(qb.shape[1]), _ptr(scores),
+        int(ratio_num), int(ratio_den), int(k_fixed), int(k_cap), _ptr(sel_pages), _ptr(sel_count),
+        float(sm_scale), int(pages_per_split), _ptr(out), _ptr(workspace),
+        int(workspace.numel() * workspace.element_size()), _stream(stream)))
 
 
 def num_selected(P: int, ratio_num: int, ratio_den: int, k_fixed: int) -> int:

@@ -25,7 +25,6 @@ struct AppendScoreArgs {
 // block L < B * H_kv appends for row L; the others score 32 pages each.
 template <int FMT, int D, int G>
 __global__ __launch_bounds__(256) KVQ_SCORE_OCC_ATTR void append_scores_kernel(AppendScoreArgs a, int rows) {
-  constexpr int kPerBlock = kScoreWaves * kScorePagesPerWave;
   __shared__ float sm_meta[kMaxTouched][2][D];
   const int L = blockIdx.x;
   const int row = L % rows, c = L / rows - 1;  // c = -1: the row's append block

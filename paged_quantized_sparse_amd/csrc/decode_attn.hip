@@ -27,6 +27,7 @@
 // invalidates the XCD's L2 each time and costs far more than a second launch.)
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "select_body.h"
 
 namespace kvq {
 namespace {
@@ -45,8 +46,12 @@ struct AttnArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   const uint16_t* q;
-  const int32_t* sel_pages;  // NULL: all pages
+  const int32_t* sel_pages;  // NULL: all pages (or selection in the kernel, below)
   const int32_t* sel_count;
+  const float* scores;       // [B][H][max_pages]: select in the kernel (the SEL instances)
+  int32_t* sel_out;          // optional copies of that selection, as kvq_topk_pages writes it
+  int32_t* cnt_out;
+  int rnum, rden, k_fixed;   // its selection rule
   float* part_acc;    // [B][Hq][max_splits][D]
   float* part_ml;     // [B][Hq][max_splits][2]
   float* out;         // [B][Hq][D]
@@ -105,7 +110,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   // with every page selected cnt_p points at the length, so K = P either way
   // (using the value on both paths keeps the load where it is issued)
   const int cnt = __builtin_amdgcn_readfirstlane(cnt_v);
-  const int K = a.sel_pages ? cnt : (cnt + kPage - 1) / kPage;
+  const int Pc = (cnt + kPage - 1) / kPage;
+  const int K = a.sel_pages ? cnt : (a.scores ? num_selected(Pc, a.rnum, a.rden, a.k_fixed) : Pc);
   const int ns = (K + a.pps - 1) / a.pps;
   float M = -INFINITY, num = 0.0f, den = 0.0f;
   for (int s0 = 0;; s0 += U * PARTS) {
@@ -146,7 +152,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   }
 }
 
-template <int FMT, int D, int G, int NW>
+// SEL: the block selects its pages itself (select_body.h) from a.scores.
+template <int FMT, int D, int G, int NW, bool SEL>
 __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
   static_assert(NW == 4, "the split merge and the combine assume 4 waves");
   using T = Tile<FMT, D>;
@@ -164,10 +171,16 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
   // row's count reads some entry of the row and is never used; with no
   // selection (all pages) the slot load reads the block table and is replaced
   // by the slot index itself.
-  const bool sparse = a.sel_pages != nullptr;
+  // With in-kernel selection, level 1 carries the row's first scores
+  // instead of the selection slot, and the slot comes from LDS after the
+  // selection.
+  const bool sparse = !SEL && a.sel_pages != nullptr;
   const int idx0 = first + w + lane * NW;
-  const int slot_raw = sparse ? vload_i32(a.sel_pages, (size_t)row * a.k_cap + min(idx0, a.k_cap - 1))
-                              : vload_i32(a.block_table, (size_t)b * a.max_pages + min(idx0, a.max_pages - 1));
+  SelPrefetch<NW * 64> pre;
+  if constexpr (SEL) pre.load(a.scores + (size_t)row * a.max_pages, a.max_pages);
+  const int slot_raw = SEL      ? 0
+                       : sparse ? vload_i32(a.sel_pages, (size_t)row * a.k_cap + min(idx0, a.k_cap - 1))
+                                : vload_i32(a.block_table, (size_t)b * a.max_pages + min(idx0, a.max_pages - 1));
   const int len_v = vload_i32(a.seq_lens, b);
   const int32_t* cnt_p = sparse ? a.sel_count + row : a.seq_lens + b;  // a select, not a branch
   const int cnt_v = vload_i32(cnt_p, 0);
@@ -201,11 +214,39 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
   // with every page selected cnt_p points at the length, so K = P either way
   // (using the value on both paths keeps the load where it is issued)
   const int cnt = __builtin_amdgcn_readfirstlane(cnt_v);
-  const int K = sparse ? cnt : (cnt + kPage - 1) / kPage;
+  const int Pc = (cnt + kPage - 1) / kPage;
+  const int K = SEL ? num_selected(Pc, a.rnum, a.rden, a.k_fixed) : (sparse ? cnt : Pc);
+  if constexpr (SEL) {  // the selection's count and padding, once per row
+    if (s == 0 && a.sel_out) {
+      if (threadIdx.x == 0) a.cnt_out[row] = K;
+      for (int i = K + threadIdx.x; i < a.k_cap; i += NW * 64) a.sel_out[(size_t)row * a.k_cap + i] = -1;
+    }
+  }
   if (first >= K) return;
   const int n = min(a.pps, K - first);
+  int* list = nullptr;  // SEL: this block's pages, ascending
+  int jlog0;
+  if constexpr (SEL) {
+    __shared__ int sm_hist[2 * kSelBins];
+    __shared__ int sm_wtot[2 * NW];
+    __shared__ uint32_t sm_wrange[2 * NW];
+    __shared__ int sm_rcnt[kSelRounds * NW];
+    extern __shared__ int sm_dyn[];  // the block's pages [pps]
+    list = sm_dyn;
+    if (K < P) {
+      select_chunk<NW>(pre, a.scores + (size_t)row * a.max_pages, P, K, first, n,
+                       SelShared{sm_hist, sm_wtot, sm_wrange, sm_rcnt}, list);
+    } else {
+      for (int i = threadIdx.x; i < n; i += NW * 64) list[i] = first + i;
+      __syncthreads();
+    }
+    if (a.sel_out)
+      for (int i = threadIdx.x; i < n; i += NW * 64) a.sel_out[(size_t)row * a.k_cap + first + i] = list[i];
+    jlog0 = list[min(w + lane * NW, n - 1)];
+  } else {
+    jlog0 = sparse ? min(max(slot_raw, 0), a.max_pages - 1) : min(idx0, a.max_pages - 1);
+  }
   // level 2 for the wave's first 64 pages
-  const int jlog0 = sparse ? min(max(slot_raw, 0), a.max_pages - 1) : min(idx0, a.max_pages - 1);
   const int phys0 = vload_i32(a.block_table, (size_t)b * a.max_pages + jlog0);
 
   // ---- per-lane online softmax state
@@ -347,7 +388,10 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
     int jlog_v = jlog0, phys_v = phys0;
     if (k0 > 0) {  // wave-uniform; only when a split gives a wave more than 64 pages
       const int idx = min(first + w + (k0 + lane) * NW, K - 1);
-      jlog_v = sparse ? min(max(a.sel_pages[(size_t)row * a.k_cap + idx], 0), a.max_pages - 1) : idx;
+      if constexpr (SEL)
+        jlog_v = list[idx - first];
+      else
+        jlog_v = sparse ? min(max(a.sel_pages[(size_t)row * a.k_cap + idx], 0), a.max_pages - 1) : idx;
       phys_v = a.block_table[(size_t)b * a.max_pages + jlog_v];
     }
     const int cnt = min(64, nw - k0);
@@ -428,10 +472,36 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
 
 }
 
+// LDS a launch of the SEL kernel would need beyond the device's per-block
+// limit: 0 if it fits.  Static LDS per instance and the limit are looked up
+// once.
+template <int FMT, int D, int G>
+size_t sel_lds_excess(size_t dyn) {
+  static size_t stat = 0, limit = 0;
+  if (limit == 0) {
+    hipFuncAttributes fa{};
+    int dev = 0, lim = 0;
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&decode_attn_kernel<FMT, D, G, kAttnWaves, true>)) !=
+            hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      return dyn;
+    stat = fa.sharedSizeBytes;
+    limit = (size_t)lim;
+  }
+  return stat + dyn > limit ? stat + dyn - limit : 0;
+}
+
 template <int FMT, int D, int G>
 hipError_t run(const AttnArgs& a, int B, hipStream_t st) {
   dim3 grid(a.max_splits, a.H, B);
-  hipLaunchKernelGGL((decode_attn_kernel<FMT, D, G, kAttnWaves>), grid, dim3(kAttnWaves * 64), 0, st, a);
+  if (a.scores) {
+    const size_t dyn = (size_t)a.pps * sizeof(int);
+    if (sel_lds_excess<FMT, D, G>(dyn)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_attn_kernel<FMT, D, G, kAttnWaves, true>), grid, dim3(kAttnWaves * 64), dyn, st, a);
+  } else {
+    hipLaunchKernelGGL((decode_attn_kernel<FMT, D, G, kAttnWaves, false>), grid, dim3(kAttnWaves * 64), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((combine_kernel<D, G>), dim3(B * a.Hq), dim3(256), 0, st, a);
@@ -456,12 +526,16 @@ hipError_t run_d(const AttnArgs& a, int B, int D, int G, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_decode_attn(const kvq_cache& c, const kvq_seqs& s, const uint16_t* q, int num_q_heads,
-                              const int32_t* sel_pages, const int32_t* sel_count, int k_cap, float sm_scale,
-                              int pages_per_split, int max_splits, float* out, void* ws, hipStream_t st) {
+                              const int32_t* sel_pages, const int32_t* sel_count, const InKernelSelect* ks,
+                              int k_cap, float sm_scale, int pages_per_split, int max_splits, float* out, void* ws,
+                              hipStream_t st) {
   const size_t n_part = (size_t)s.batch * num_q_heads * max_splits;
   float* part_ml = (float*)ws;
   float* part_acc = part_ml + n_part * 2;
-  AttnArgs a{c.k_pages, c.v_pages, c.kv_params, s.block_table, s.seq_lens, q, sel_pages, sel_count,
+  AttnArgs a{c.k_pages, c.v_pages, c.kv_params, s.block_table, s.seq_lens, q,
+             ks ? nullptr : sel_pages, ks ? nullptr : sel_count,
+             ks ? ks->scores : nullptr, ks ? ks->sel_out : nullptr, ks ? ks->cnt_out : nullptr,
+             ks ? ks->rnum : 0, ks ? ks->rden : 1, ks ? ks->k_fixed : 0,
              part_acc, part_ml, out, c.num_kv_heads, num_q_heads, s.max_pages, k_cap,
              pages_per_split, max_splits, sm_scale * 1.4426950408889634f};
   const int G = num_q_heads / c.num_kv_heads;

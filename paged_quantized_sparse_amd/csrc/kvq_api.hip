@@ -165,8 +165,39 @@ kvq_status kvq_sparse_decode_attn(const kvq_cache* cache, const kvq_seqs* seqs, 
   const int32_t max_splits = splits_for(seqs->max_pages, cap, pps);
   const size_t need = kvq_attn_workspace_bytes(seqs->batch, num_q_heads, cache->head_dim, seqs->max_pages, cap, pps);
   if (!ws || ws_bytes < need || !aligned16(ws)) return KVQ_ERR_WORKSPACE;
-  return from_hip(kvq::launch_decode_attn(*cache, *seqs, q, num_q_heads, sel_pages, sel_count, k_cap, sm_scale, pps,
+  return from_hip(kvq::launch_decode_attn(*cache, *seqs, q, num_q_heads, sel_pages, sel_count, nullptr, k_cap,
+                                          sm_scale, pps,
                                           max_splits, out, ws, (hipStream_t)stream));
+}
+
+kvq_status kvq_select_decode_attn(const kvq_cache* cache, const kvq_seqs* seqs, const uint16_t* q,
+                                  int32_t num_q_heads, const float* scores, int32_t ratio_num, int32_t ratio_den,
+                                  int32_t k_fixed, int32_t k_cap, int32_t* sel_pages, int32_t* sel_count,
+                                  float sm_scale, int32_t pages_per_split, float* out, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  kvq_status st = check_cache(cache, false);
+  if (st != KVQ_OK) return st;
+  if ((st = check_seqs(seqs)) != KVQ_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != KVQ_OK) return st;
+  if (!q || !out || !scores || !aligned16(q)) return KVQ_ERR_INVALID_ARG;
+  if (k_fixed < 0 || (k_fixed == 0 && (ratio_num < 1 || ratio_den < 1))) return KVQ_ERR_INVALID_ARG;
+  if ((sel_pages == nullptr) != (sel_count == nullptr)) return KVQ_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale)) return KVQ_ERR_INVALID_ARG;
+  if (pages_per_split < 0 || pages_per_split > 4096) return KVQ_ERR_INVALID_ARG;
+  if (seqs->max_pages > kvq::kSelMaxPages) return KVQ_ERR_UNSUPPORTED;
+  if (k_cap < kvq::num_selected(seqs->max_pages, ratio_num, ratio_den, k_fixed)) return KVQ_ERR_INVALID_ARG;
+  const int32_t pps = pages_per_split ? pages_per_split
+                                      : kvq_default_pages_per_split(seqs->batch, cache->num_kv_heads,
+                                                                    seqs->max_pages, k_cap);
+  const int32_t max_splits = splits_for(seqs->max_pages, k_cap, pps);
+  const size_t need = kvq_attn_workspace_bytes(seqs->batch, num_q_heads, cache->head_dim, seqs->max_pages, k_cap,
+                                               pps);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return KVQ_ERR_WORKSPACE;
+  const kvq::InKernelSelect ks{scores, ratio_num, ratio_den, k_fixed, sel_pages, sel_count};
+  const hipError_t e = kvq::launch_decode_attn(*cache, *seqs, q, num_q_heads, nullptr, nullptr, &ks, k_cap, sm_scale,
+                                               pps, max_splits, out, ws, (hipStream_t)stream);
+  if (e == hipErrorInvalidConfiguration) return KVQ_ERR_UNSUPPORTED;  // LDS of this row length and split
+  return from_hip(e);
 }
 
 const char* kvq_status_string(kvq_status status) {

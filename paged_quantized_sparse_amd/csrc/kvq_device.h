@@ -108,6 +108,42 @@ __device__ __forceinline__ int wave_incl_scan_add(int x) {
   return x;
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
+}
+
+// Min / max over the wave: DPP inside each row of 16, then the four row
+// results through readlane (wave-uniform result).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, dpp_u32<kDppXor1>(x));
+  x = min(x, dpp_u32<kDppXor2>(x));
+  x = min(x, dpp_u32<kDppHalfMirror>(x));
+  x = min(x, dpp_u32<kDppMirror>(x));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return min(min(a, b), min(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<kDppXor1>(x));
+  x = max(x, dpp_u32<kDppXor2>(x));
+  x = max(x, dpp_u32<kDppHalfMirror>(x));
+  x = max(x, dpp_u32<kDppMirror>(x));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Inclusive prefix sum inside each row of 16 lanes (DPP row_shr 1, 2, 4, 8).
+__device__ __forceinline__ int row16_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
+  return x;
+}
+
 // Lanes below this one whose bit is set in a 64-bit lane mask.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));

@@ -33,8 +33,23 @@ constexpr int kTopkMaxPages = 12000;  // keys in LDS beside 16.9 KB of histogram
 hipError_t launch_topk(const float* scores, const kvq_seqs& s, int num_kv_heads, int rnum, int rden,
                        int k_fixed, int k_cap, int32_t* sel_pages, int32_t* sel_count, hipStream_t st);
 
+// Longest row (pages) the attention kernel selects in itself: each of its
+// 256 threads holds 8 keys in registers.  (More rounds of keys would make the
+// fully unrolled selection code, fetched at every launch, slower for all rows.)
+constexpr int kSelMaxPages = KVQ_SELECT_MAX_PAGES;
+
+// Selection done inside the attention kernel: the scores, the rule, and
+// optional copies of the selection (NULL: not wanted).
+struct InKernelSelect {
+  const float* scores;
+  int rnum, rden, k_fixed;
+  int32_t* sel_out;
+  int32_t* cnt_out;
+};
+
 hipError_t launch_decode_attn(const kvq_cache& c, const kvq_seqs& s, const uint16_t* q, int num_q_heads,
-                              const int32_t* sel_pages, const int32_t* sel_count, int k_cap, float sm_scale,
+                              const int32_t* sel_pages, const int32_t* sel_count, const InKernelSelect* ks,
+                              int k_cap, float sm_scale,
                               int pages_per_split, int max_splits, float* out, void* ws, hipStream_t st);
 
 }  // namespace kvq

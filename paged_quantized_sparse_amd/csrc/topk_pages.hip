@@ -38,42 +38,6 @@ struct TopkArgs {
   int rnum, rden, k_fixed, k_cap;
 };
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
-}
-
-// Min / max over the wave: DPP inside each row of 16, then the four row
-// results through readlane (wave-uniform result).
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-  x = min(x, dpp_u32<kDppXor1>(x));
-  x = min(x, dpp_u32<kDppXor2>(x));
-  x = min(x, dpp_u32<kDppHalfMirror>(x));
-  x = min(x, dpp_u32<kDppMirror>(x));
-  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
-  return min(min(a, b), min(c, d));
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-  x = max(x, dpp_u32<kDppXor1>(x));
-  x = max(x, dpp_u32<kDppXor2>(x));
-  x = max(x, dpp_u32<kDppHalfMirror>(x));
-  x = max(x, dpp_u32<kDppMirror>(x));
-  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
-  return max(max(a, b), max(c, d));
-}
-
-// Inclusive prefix sum inside each row of 16 lanes (DPP row_shr 1, 2, 4, 8).
-__device__ __forceinline__ int row16_incl_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
-  return x;
-}
-
 // The 16 per-wave values of an LDS array, one per lane of row 0 (lanes
 // 16..63 read a copy of row 0 and are not used): a single LDS read instead of
 // sixteen serialized ones.

@@ -6,6 +6,9 @@ A decode step, as the TinyServe page (lpnh.cn, section 3.1) orders it:
   append the new token (and re-quantize its open group) -> refresh the
   metadata of the pages that changed -> score every page -> top-K ->
   attention over the selected pages (split-K + combine).
+DecodeStep.run_with_append does it in four launches: append + metadata +
+scores (kvq_append_decode_scores), then top-K inside the attention kernel
+(kvq_select_decode_attn), then the split combine.
 """
 from __future__ import annotations
 
@@ -14,10 +17,10 @@ from typing import Callable
 import numpy as np
 import torch
 
-from . import (KVQ_INT8_GROUP64, PAGE_SIZE, PagedCache, Seqs, kvq_append_decode, kvq_append_decode_scores,
+from . import (KVQ_INT8_GROUP64, PAGE_SIZE, SELECT_MAX_PAGES, PagedCache, Seqs, kvq_append_decode, kvq_append_decode_scores,
                kvq_append_quant,
                kvq_attn_workspace_bytes, kvq_build_page_meta, kvq_default_pages_per_split, kvq_page_scores,
-               kvq_sparse_decode_attn, kvq_topk_pages, num_selected)
+               kvq_select_decode_attn, kvq_sparse_decode_attn, kvq_topk_pages, num_selected)
 
 KVSource = Callable[[int], "tuple[np.ndarray, np.ndarray]"]  # b -> (K [L][H][d], V [L][H][d]) fp16
 
@@ -117,13 +120,20 @@ class DecodeAppend:
 
 class DecodeStep:
     """Device buffers for score -> top-K -> sparse attention of one step.
-    dense=True skips scoring and selection and attends to every page."""
+    dense=True skips scoring and selection and attends to every page.
+    fused_select=True (the default) selects inside the attention kernel
+    (kvq_select_decode_attn) when rows have at most SELECT_MAX_PAGES pages;
+    otherwise, or with False, it runs kvq_topk_pages, then
+    kvq_sparse_decode_attn.  Either way sel_pages / sel_count end up holding
+    the selection."""
 
     def __init__(self, cache: PagedCache, seqs: Seqs, num_q_heads: int, ratio_num: int, ratio_den: int,
-                 k_fixed: int, dense: bool = False, pages_per_split: int = 0, device="cuda"):
+                 k_fixed: int, dense: bool = False, pages_per_split: int = 0, device="cuda",
+                 fused_select: bool = True):
         self.cache, self.seqs, self.Hq = cache, seqs, num_q_heads
         self.ratio = (ratio_num, ratio_den, k_fixed)
         self.dense = dense
+        self.fused_select = fused_select and seqs.max_pages <= SELECT_MAX_PAGES
         B, H, d, maxp = seqs.batch, cache.num_kv_heads, cache.head_dim, seqs.max_pages
         self.k_cap = 0 if dense else num_selected(maxp, ratio_num, ratio_den, k_fixed)
         self.pps = pages_per_split or kvq_default_pages_per_split(B, H, maxp, self.k_cap)
@@ -146,9 +156,20 @@ class DecodeStep:
                                self.sm_scale, self.pps, stream)
         return self.out
 
+    def select_attend(self, q, stream=None) -> torch.Tensor:
+        """Top-K of self.scores and attention in one call (kvq_select_decode_attn)."""
+        rn, rd, kf = self.ratio
+        kvq_select_decode_attn(self.cache, self.seqs, q, self.scores, rn, rd, kf, self.k_cap, self.out,
+                               self.workspace, self.sm_scale, self.pps, stream, sel_pages=self.sel_pages,
+                               sel_count=self.sel_count)
+        return self.out
+
     def run(self, q, stream=None) -> torch.Tensor:
         if self.dense:
             return self.attend(q, None, None, stream)
+        if self.fused_select:
+            kvq_page_scores(self.cache, self.seqs, q, self.scores, stream)
+            return self.select_attend(q, stream)
         self.select(q, stream)
         return self.attend(q, self.sel_pages, self.sel_count, stream)
 
@@ -160,6 +181,8 @@ class DecodeStep:
             return self.attend(q, None, None, stream)
         kvq_append_decode_scores(self.cache, self.seqs, app.start, app.off, app.max_new, app.k_new, app.v_new, q,
                                  self.scores, stream)
+        if self.fused_select:
+            return self.select_attend(q, stream)
         rn, rd, kf = self.ratio
         kvq_topk_pages(self.scores, self.seqs, self.cache.num_kv_heads, rn, rd, kf, self.sel_pages,
                        self.sel_count, stream)

@@ -58,8 +58,8 @@ def test_library_never_allocates_or_synchronizes():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == 1
-    assert "#define KVQ_ABI_VERSION 1" in open(HEADER).read()
+    assert lib.kvq_abi_version() == 2
+    assert "#define KVQ_ABI_VERSION 2" in open(HEADER).read()
     for s, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP"), (99, b"unknown")]:
         assert word in lib.kvq_status_string(s)
 
@@ -141,3 +141,30 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(kvq, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="libkvq.so not found"):
         kvq.lib()
+
+
+def _sel_attn(lib, c, s, hq=4, scores=FAKE, rn=3, rd=10, kf=0, k_cap=3, sel=None, cnt=None, pps=8, ws=FAKE,
+              ws_bytes=1 << 30, q=FAKE, scale=0.1):
+    return lib.kvq_select_decode_attn(ctypes.byref(c), ctypes.byref(s), q, hq, scores, rn, rd, kf, k_cap, sel, cnt,
+                                      scale, pps, FAKE, ws, ws_bytes, None)
+
+
+def test_select_attention_argument_errors(lib):
+    c, s = _structs()                                        # max_pages 8: K(8) = 3 at 3/10
+    assert _sel_attn(lib, c, s, scores=None) == INVALID
+    assert _sel_attn(lib, c, s, k_cap=2) == INVALID          # below K(max_pages)
+    assert _sel_attn(lib, c, s, rn=0) == INVALID
+    assert _sel_attn(lib, c, s, kf=-1) == INVALID
+    assert _sel_attn(lib, c, s, sel=FAKE) == INVALID         # selection copy without its counts
+    assert _sel_attn(lib, c, s, hq=12) == UNSUPPORTED        # group size 3
+    assert _sel_attn(lib, c, s, pps=5000) == INVALID
+    assert _sel_attn(lib, c, s, q=FAKE + 2) == INVALID
+    assert _sel_attn(lib, c, s, ws=None) == WORKSPACE
+    assert _sel_attn(lib, c, s, ws_bytes=16) == WORKSPACE
+    _, s_long = _structs(maxp=2049)
+    assert _sel_attn(lib, c, s_long, k_cap=2049) == UNSUPPORTED  # rows over KVQ_SELECT_MAX_PAGES
+
+
+def test_select_limit_matches_header():
+    import paged_quantized_sparse_amd as kvq
+    assert f"#define KVQ_SELECT_MAX_PAGES {kvq.SELECT_MAX_PAGES} " in open(HEADER).read()

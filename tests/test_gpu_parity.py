@@ -260,6 +260,110 @@ def test_attention_independent_of_split_size(n, pps):
     assert np.abs(dense - oracle.attention(bt.ocache, bt.table, bt.lens, bt.q)).max() <= ATTN_ATOL
 
 
+def _select_vs_separate(st_sep, st_fus, q_dev, scores=None):
+    """Run top-K then attention (st_sep) and the one-call select + attention
+    (st_fus) on the same scores; return both outputs and selections."""
+    kvq, _ = kvq_mod()
+    if scores is not None:
+        st_sep.scores.copy_(scores)
+    rn, rd, kf = st_sep.ratio
+    kvq.kvq_topk_pages(st_sep.scores, st_sep.seqs, st_sep.cache.num_kv_heads, rn, rd, kf, st_sep.sel_pages,
+                       st_sep.sel_count)
+    out_sep = st_sep.attend(q_dev, st_sep.sel_pages, st_sep.sel_count).clone()
+    st_fus.scores.copy_(st_sep.scores)
+    st_fus.sel_pages.fill_(-7)
+    st_fus.sel_count.fill_(-7)
+    out_fus = st_fus.select_attend(q_dev)
+    torch.cuda.synchronize()
+    return out_sep, out_fus
+
+
+@pytest.mark.parametrize("kind,n", CASES, ids=IDS)
+def test_select_attention_equals_topk_then_attention(kind, n):
+    """kvq_select_decode_attn (top-K inside the attention kernel) writes the
+    selection kvq_topk_pages writes and, bit for bit, the output of
+    kvq_sparse_decode_attn over it, at the default split and at others."""
+    kvq, _ = kvq_mod()
+    bt = built((kind, n), workload(kind, n))
+    if bt.w.is_dense():
+        pytest.skip("selection bypassed for ratio 1")
+    for pps in ([0, 1, 3, 16, 64] if kind == "small" else [0, 16]):
+        sep = bt.step(pages_per_split=pps, fused_select=False)
+        kvq.kvq_page_scores(bt.cache, bt.seqs, bt.q_dev, sep.scores)
+        fus = bt.step(pages_per_split=pps)
+        out_sep, out_fus = _select_vs_separate(sep, fus, bt.q_dev)
+        assert torch.equal(fus.sel_count, sep.sel_count), pps
+        assert torch.equal(fus.sel_pages, sep.sel_pages), pps
+        assert torch.equal(out_fus, out_sep), pps
+
+
+def test_select_attention_on_tied_scores():
+    """Heavily tied scores (small integers, -0 and +0, plateaus) on a ragged
+    GQA batch: the in-kernel selection equals the oracle's top-K exactly and
+    the output equals top-K then attention bit for bit."""
+    _, runtime = kvq_mod()
+    bt = built(("small", 5), workloads.small(5))
+    w = bt.w
+    B, maxp, H = bt.table.shape[0], bt.table.shape[1], w.num_kv_heads
+    rng = np.random.default_rng(33)
+    sc = rng.integers(-3, 4, size=(B, H, maxp)).astype(np.float32)
+    sc[0, 0] = 0.0
+    sc[0, 0, ::2] = -0.0
+    sc[1 % B, H - 1, 5:60] = 2.5
+    P = (bt.lens + PAGE - 1) // PAGE
+    for b in range(B):
+        sc[b, :, P[b]:] = -np.inf
+    for rn, rd, kf in [(3, 10, 0), (1, 7, 0), (0, 1, 5), (1, 1, 0)]:
+        mk = lambda fused: runtime.DecodeStep(bt.cache, bt.seqs, w.num_q_heads, rn, rd, kf,  # noqa: E731
+                                              fused_select=fused)
+        sep, fus = mk(False), mk(True)
+        out_sep, out_fus = _select_vs_separate(sep, fus, bt.q_dev, torch.from_numpy(sc).cuda())
+        osel, ocnt = oracle.topk(sc.astype(np.float64), bt.lens, rn, rd, kf, fus.k_cap)
+        assert np.array_equal(to_np(fus.sel_count), ocnt), (rn, rd, kf)
+        assert np.array_equal(to_np(fus.sel_pages), osel), (rn, rd, kf)
+        assert torch.equal(out_fus, out_sep), (rn, rd, kf)
+
+
+def test_select_attention_rows_at_the_limit():
+    """Rows of up to KVQ_SELECT_MAX_PAGES pages (every thread holding all 8 of
+    its keys): selection and output equal top-K then attention, at several
+    splits, and the selection equals the oracle's top-K of the same scores.
+    Longer rows are refused, and the runtime then takes the two-call path."""
+    kvq, runtime = kvq_mod()
+    w = workloads.small(4).with_(seq_len=kvq.SELECT_MAX_PAGES * PAGE - 3, batch=2)  # last page partial
+    bt = Built(w, with_oracle=False)
+    assert bt.seqs.max_pages == kvq.SELECT_MAX_PAGES
+    for pps in (0, 7, 64):
+        sep = bt.step(pages_per_split=pps, fused_select=False)
+        kvq.kvq_page_scores(bt.cache, bt.seqs, bt.q_dev, sep.scores)
+        fus = bt.step(pages_per_split=pps)
+        assert fus.fused_select
+        out_sep, out_fus = _select_vs_separate(sep, fus, bt.q_dev)
+        osel, ocnt = oracle.topk(to_np(sep.scores).astype(np.float64), bt.lens, w.ratio_num, w.ratio_den,
+                                 w.k_fixed, fus.k_cap)
+        assert np.array_equal(to_np(fus.sel_count), ocnt), pps
+        assert np.array_equal(to_np(fus.sel_pages), osel), pps
+        assert torch.equal(out_fus, out_sep), pps
+    # one page more per row: refused by the fused call, run in two calls by the runtime
+    lens = torch.from_numpy(bt.lens.astype(np.int32)).cuda()
+    table = torch.zeros((w.batch, kvq.SELECT_MAX_PAGES + 1), dtype=torch.int32, device="cuda")
+    table[:, :-1] = bt.seqs.block_table
+    seqs = kvq.Seqs(lens, table)
+    st = runtime.DecodeStep(bt.cache, seqs, w.num_q_heads, w.ratio_num, w.ratio_den, w.k_fixed, pages_per_split=16)
+    assert not st.fused_select
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_select_decode_attn(bt.cache, seqs, bt.q_dev, st.scores, w.ratio_num, w.ratio_den, w.k_fixed,
+                                   st.k_cap, st.out, st.workspace, st.sm_scale)
+    assert e.value.status == 2
+    out = st.run(bt.q_dev).clone()
+    fus = bt.step(pages_per_split=16)
+    want = fus.run(bt.q_dev)
+    torch.cuda.synchronize()
+    assert st.k_cap == fus.k_cap
+    assert torch.equal(st.sel_pages, fus.sel_pages)   # the extra column is never a live page
+    assert torch.equal(out, want)                     # same splits, same pages: same bits
+
+
 @pytest.mark.parametrize("kind,n", CASES, ids=IDS)
 def test_end_to_end_step(kind, n):
     bt = built((kind, n), workload(kind, n))
