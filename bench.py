@@ -4,17 +4,20 @@ One step = the whole hot path for one layer of the Llama-2-7B-shaped workload
 (1 sequence, 32 heads, head_dim 128, 32768 tokens in 16-token pages, INT8 per
 token, selection ratio 0.3 -> 615 of 2048 pages per head):
   append the newest token (quantize into its page) and refresh that page's
-  metadata, fused into scoring all pages -> top-K -> split-K attention +
-  combine.
+  metadata, fused into scoring all pages -> top-K inside the split-K
+  attention kernel -> split combine.
 Steps rotate over `--layers` independent copies of the layer cache (distinct
 device buffers), so a step never finds the previous step's working set in the
 256 MB Infinity Cache, as in a real decode pass over many layers.
 
 Prints one JSON line: achieved GB/s of the whole step (metadata of every page
 + the selected KV tiles with their scale/zero, i.e. the bytes the method must
-read), microseconds per step, the sparse attention kernels' own GB/s against
-the 8 TB/s HBM peak (timed with HIP events on the launch stream), and the CPU
-oracle timed on the host on the same workload.
+read), microseconds per step (and its p10/p50/p90 over rotations), the sparse
+attention call's own GB/s against the 8 TB/s HBM peak (kvq_sparse_decode_attn
+over the step's selection, timed with HIP events on the launch stream), what a
+plain streaming-read kernel reaches over 2 GiB on the same GPU, the decode-time
+append alone, and the CPU oracle timed on the host on the same workload (all
+threads this process may use, up to 16, and one thread).
 """
 from __future__ import annotations
 
@@ -69,17 +72,19 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(w, seconds: float):
-    """The oracle's decode step (scores -> top-K -> attention) on host threads."""
+def cpu_baseline(w, seconds: float, threads: int = 0, built=None):
+    """The oracle's decode step (scores -> top-K -> attention) on host threads
+    (0: all this process may use, at most 16)."""
     import oracle
-    cache, table = oracle.build_cache(w)
+    cache, table = built if built is not None else oracle.build_cache(w)
     lens, q = w.seq_lens(), w.query()
     k_cap = oracle.num_selected(int(table.shape[1]), w.ratio_num, w.ratio_den, w.k_fixed)
-    try:
-        threads = len(os.sched_getaffinity(0))
-    except AttributeError:
-        threads = os.cpu_count() or 1
-    threads = max(1, min(16, threads))
+    if threads <= 0:
+        try:
+            threads = len(os.sched_getaffinity(0))
+        except AttributeError:
+            threads = os.cpu_count() or 1
+        threads = max(1, min(16, threads))
     times = []
     t_end = time.perf_counter() + seconds
     while True:
@@ -88,7 +93,7 @@ def cpu_baseline(w, seconds: float):
         times.append(time.perf_counter() - t0)
         if time.perf_counter() > t_end or len(times) >= 20:
             break
-    return float(np.median(times)), threads, len(times)
+    return float(np.median(times)), threads, len(times), (cache, table)
 
 
 def main() -> int:
@@ -198,6 +203,32 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / args.steps * 1e3
 
+    # ---- per-step spread (outside the timed region): HIP events around each
+    # replay of the rotation graph, or around each eager step
+    per_step_us = []
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * 50)]
+    for r in range(50):
+        ev[2 * r].record(stream)
+        if rotation is not None:
+            rotation.replay()
+        else:
+            for i in range(len(layers)):
+                one_step(i)
+        ev[2 * r + 1].record(stream)
+    torch.cuda.synchronize()
+    for r in range(50):
+        per_step_us.append(ev[2 * r].elapsed_time(ev[2 * r + 1]) * 1e3 / len(layers))
+    p10, p50, p90 = (float(np.percentile(per_step_us, x)) for x in (10, 50, 90))
+
+    # ---- the decode-time append alone (kvq_append_decode), rotating layers
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        appends[i % len(layers)].run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    append_us = e0.elapsed_time(e1) * 1e3 / args.steps
+
     # ---- the sparse attention call alone (split kernel + combine), HIP events
     # on the stream it is launched on, rotating over the same layers
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -220,27 +251,30 @@ def main() -> int:
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     attn_gbs = kv_b / (attn_us * 1e-6) / 1e9
 
-    # for context: what torch's own reduction kernel reads per second (2 GiB fp32 sum)
-    big = torch.empty(1 << 29, dtype=torch.float32, device=dev).fill_(1.0)
-    big.sum()
+    # the attainable streaming read on this GPU: a plain read kernel over 2 GiB
+    big = torch.empty(2 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    kvq.kvq_read_probe(big, sink)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    e0.record(stream)
     for _ in range(5):
-        big.sum()
-    e1.record()
+        kvq.kvq_read_probe(big, sink)
+    e1.record(stream)
     torch.cuda.synchronize()
-    read_gbs = 5 * big.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    read_gbs = 5 * big.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del big
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
-        t_cpu, threads, reps = cpu_baseline(w, args.cpu_seconds)
+        t_cpu, threads, reps, built = cpu_baseline(w, args.cpu_seconds)
         cpu = {"value": round(step_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": f"full decode step (scores, top-K, attention) of this workload, median of {reps} runs, "
                          f"{t_cpu * 1e3:.1f} ms each",
                "us_per_step": round(t_cpu * 1e6, 1)}
+        t1, _, reps1, _ = cpu_baseline(w, args.cpu_seconds / 2, threads=1, built=built)
+        cpu1 = {"value": round(step_bytes / t1 / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"the same step on one thread, median of {reps1} runs", "us_per_step": round(t1 * 1e6, 1)}
 
     ratio = f"{w.ratio_num}/{w.ratio_den}" if not w.k_fixed else f"k={w.k_fixed}"
     rec = {
@@ -270,8 +304,12 @@ def main() -> int:
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if args.config == 4 and not args.pages_per_split else None,
                      "algorithmic_bytes": kv_b, "us_per_launch": round(attn_us, 2)},
-        "torch_sum_2gib_read_gbs": round(read_gbs, 1),
+        "us_per_step_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
+        "append_decode_us": round(append_us, 2),
+        "read_probe_2gib_gbs": round(read_gbs, 1),
+        "attention_vs_read_probe": round(attn_gbs / read_gbs, 4),
         "cpu_baseline": cpu,
+        "cpu_baseline_1thread": cpu1,
     }
     print(json.dumps(rec), flush=True)
     return 0

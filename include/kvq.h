@@ -251,6 +251,15 @@ size_t kvq_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head
 /* The pages_per_split kvq_sparse_decode_attn uses when given 0. */
 int32_t kvq_default_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t max_pages, int32_t k_cap);
 
+/*
+ * kvq_read_probe -- measurement helper, not a step of the method: reads
+ * `bytes` of device memory at `buf` once with a plain streaming kernel, so a
+ * caller can time the bandwidth an HBM-bound kernel can reach on this GPU.
+ * buf 16-byte aligned, bytes a multiple of 16 (else KVQ_ERR_INVALID_ARG);
+ * sink is one device uint32 the kernel may write (in practice never does).
+ */
+kvq_status kvq_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *kvq_status_string(kvq_status status);
 

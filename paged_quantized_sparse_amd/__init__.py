@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         for f in ("kvq_append_quant", "kvq_append_decode", "kvq_append_decode_scores", "kvq_build_page_meta",
                   "kvq_page_scores", "kvq_topk_pages", "kvq_sparse_decode_attn", "kvq_select_decode_attn"):
             getattr(L, f).restype = ctypes.c_int
+        L.kvq_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
+        L.kvq_read_probe.restype = ctypes.c_int
         L.kvq_attn_workspace_bytes.argtypes = [I, I, I, I, I, I]
         L.kvq_attn_workspace_bytes.restype = ctypes.c_size_t
         L.kvq_default_pages_per_split.argtypes = [I, I, I, I]
@@ -248,6 +250,12 @@ def kvq_select_decode_attn(cache: PagedCache, seqs: Seqs, q, scores, ratio_num: 
         int(ratio_num), int(ratio_den), int(k_fixed), int(k_cap), _ptr(sel_pages), _ptr(sel_count),
         float(sm_scale), int(pages_per_split), _ptr(out), _ptr(workspace),
         int(workspace.numel() * workspace.element_size()), _stream(stream)))
+
+
+def kvq_read_probe(buf, sink, stream=None) -> None:
+    """Measurement helper: one plain streaming read of `buf` (a device tensor)."""
+    _check("kvq_read_probe", lib().kvq_read_probe(_ptr(buf), int(buf.numel() * buf.element_size()), _ptr(sink),
+                                                  _stream(stream)))
 
 
 def num_selected(P: int, ratio_num: int, ratio_den: int, k_fixed: int) -> int:

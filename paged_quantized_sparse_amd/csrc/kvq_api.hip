@@ -200,6 +200,11 @@ kvq_status kvq_select_decode_attn(const kvq_cache* cache, const kvq_seqs* seqs, 
   return from_hip(e);
 }
 
+kvq_status kvq_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || !aligned16(buf) || bytes % 16 != 0) return KVQ_ERR_INVALID_ARG;
+  return from_hip(kvq::launch_read_probe(buf, bytes, sink, (hipStream_t)stream));
+}
+
 const char* kvq_status_string(kvq_status status) {
   switch (status) {
     case KVQ_OK: return "ok";

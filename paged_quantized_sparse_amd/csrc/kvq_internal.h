@@ -33,6 +33,8 @@ constexpr int kTopkMaxPages = 12000;  // keys in LDS beside 16.9 KB of histogram
 hipError_t launch_topk(const float* scores, const kvq_seqs& s, int num_kv_heads, int rnum, int rden,
                        int k_fixed, int k_cap, int32_t* sel_pages, int32_t* sel_count, hipStream_t st);
 
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
+
 // Longest row (pages) the attention kernel selects in itself: each of its
 // 256 threads holds 8 keys in registers.  (More rounds of keys would make the
 // fully unrolled selection code, fetched at every launch, slower for all rows.)
