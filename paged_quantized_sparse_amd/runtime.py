@@ -22,6 +22,8 @@ from . import (KVQ_INT8_GROUP64, PAGE_SIZE, SELECT_MAX_PAGES, PagedCache, Seqs, 
                kvq_attn_workspace_bytes, kvq_build_page_meta, kvq_default_pages_per_split, kvq_page_scores,
                kvq_select_decode_attn, kvq_sparse_decode_attn, kvq_topk_pages, num_selected)
 
+FUSED_SELECT_MAX_BLOCKS = 512  # one round of attention blocks on 256 CUs (2 per CU)
+
 KVSource = Callable[[int], "tuple[np.ndarray, np.ndarray]"]  # b -> (K [L][H][d], V [L][H][d]) fp16
 
 
@@ -122,10 +124,12 @@ class DecodeStep:
     """Device buffers for score -> top-K -> sparse attention of one step.
     dense=True skips scoring and selection and attends to every page.
     fused_select=True (the default) selects inside the attention kernel
-    (kvq_select_decode_attn) when rows have at most SELECT_MAX_PAGES pages;
-    otherwise, or with False, it runs kvq_topk_pages, then
-    kvq_sparse_decode_attn.  Either way sel_pages / sel_count end up holding
-    the selection."""
+    (kvq_select_decode_attn) when rows have at most SELECT_MAX_PAGES pages and
+    the attention grid fits in one round of resident blocks (about 2 per CU,
+    FUSED_SELECT_MAX_BLOCKS): every attention block repeats its row's
+    selection, which pays off only while all blocks run at once.  Otherwise,
+    or with False, it runs kvq_topk_pages, then kvq_sparse_decode_attn.
+    Either way sel_pages / sel_count end up holding the selection."""
 
     def __init__(self, cache: PagedCache, seqs: Seqs, num_q_heads: int, ratio_num: int, ratio_den: int,
                  k_fixed: int, dense: bool = False, pages_per_split: int = 0, device="cuda",
@@ -133,10 +137,12 @@ class DecodeStep:
         self.cache, self.seqs, self.Hq = cache, seqs, num_q_heads
         self.ratio = (ratio_num, ratio_den, k_fixed)
         self.dense = dense
-        self.fused_select = fused_select and seqs.max_pages <= SELECT_MAX_PAGES
         B, H, d, maxp = seqs.batch, cache.num_kv_heads, cache.head_dim, seqs.max_pages
         self.k_cap = 0 if dense else num_selected(maxp, ratio_num, ratio_den, k_fixed)
         self.pps = pages_per_split or kvq_default_pages_per_split(B, H, maxp, self.k_cap)
+        blocks = B * H * -(-max(self.k_cap, 1) // self.pps)
+        self.fused_select = (fused_select and not dense and maxp <= SELECT_MAX_PAGES
+                             and blocks <= FUSED_SELECT_MAX_BLOCKS)
         self.scores = torch.empty((B, H, maxp), dtype=torch.float32, device=device)
         self.sel_pages = torch.empty((B, H, max(self.k_cap, 1)), dtype=torch.int32, device=device)
         self.sel_count = torch.empty((B, H), dtype=torch.int32, device=device)
