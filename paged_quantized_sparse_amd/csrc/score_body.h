@@ -17,10 +17,6 @@
 
 namespace kvq {
 
-// Scoring kernels run at 8 waves per SIMD (at most 64 VGPRs), so a launch of
-// 256 CUs x 8 blocks streams the metadata in a single round of blocks.
-#define KVQ_SCORE_OCC_ATTR __attribute__((amdgpu_waves_per_eu(8, 8)))
-
 constexpr int kScoreWaves = 4;
 constexpr int kScorePagesPerWave = 8;
 
@@ -72,52 +68,162 @@ __device__ __forceinline__ float score_from_values(const ScoreQuery<D, G>& q, co
   return best;
 }
 
-// Block-table entries of pages j0 .. j0+7 of sequence b in one vector load:
-// lane k (mod 8) holds page j0 + k's entry (the index clamped into the row).
-__device__ __forceinline__ int score_table_load(const ScoreView& a, int b, int j0) {
-  const int j = min(max(j0 + (lane_id() & 7), 0), a.max_pages - 1);
-  return a.block_table[(size_t)b * a.max_pages + j];
-}
+// What one scoring item needs before its metadata can be loaded: the block-
+// table entries of its 8 pages (lane k mod 8: page j0 + k, index clamped into
+// the row), the sequence length, the append offsets and start (when rows are
+// being appended) and this lane's raw fp16 query pairs.  All are vector loads
+// left pending: a wave issues the next item's head while the current item's
+// metadata loads are in flight.
+template <int D, int G>
+struct ScoreHead {
+  static constexpr int E = ScoreQuery<D, G>::E;
+  static constexpr int QW = G * E / 2;  // query dwords per lane
+  int bt, len, o0, o1, start;
+  uint32_t q[QW];
+};
 
-// The calling wave scores pages j0 .. j0+7 of row (b, g), given their table
-// entries bt_v from score_table_load: pages below min(P, skip_from) get their
-// score, pages at or past P (and below max_pages) get -inf, pages in
-// [skip_from, P) are left to another writer.  P and skip_from come from
-// `bounds(P, skip_from)`, called only here, so the caller's loads of them and
-// the table load are in flight together.  A page that is not scored reads
-// physical page 0's metadata instead of its own, so every load is
-// unconditional.  All loads are issued before any page is reduced.
-template <int D, int G, typename Bounds>
-__device__ __forceinline__ void score_pages(const ScoreView& a, const ScoreQuery<D, G>& q, int b, int g, int j0,
-                                            int bt_v, Bounds bounds) {
+// Per-sequence arrays the scoring items read (new_off and start_pos only
+// when rows are appended in the same launch).
+struct ScoreSeqs {
+  const int32_t* seq_lens;
+  const int32_t* new_off;
+  const int32_t* start_pos;
+  int rows;  // B * H
+};
+
+template <int D, int G, bool APPEND>
+__device__ __forceinline__ ScoreHead<D, G> score_head_load(const ScoreView& a, const ScoreSeqs& ss, int b, int g,
+                                                           int j0) {
   constexpr int E = ScoreQuery<D, G>::E;
+  ScoreHead<D, G> h;
   const int lane = lane_id();
-  float* out = a.scores + ((size_t)b * a.H + g) * a.max_pages;
-  __builtin_amdgcn_sched_barrier(0);
-  int P, skip_from;
-  bounds(P, skip_from);
-  const int live = min(P, skip_from);
-  float vals[kScorePagesPerWave][E];
+  h.bt = a.block_table[(size_t)b * a.max_pages + min(j0 + (lane & 7), a.max_pages - 1)];
+  h.len = vload_i32(ss.seq_lens, b);
+  if constexpr (APPEND) {
+    h.o0 = vload_i32(ss.new_off, b);
+    h.o1 = vload_i32(ss.new_off, b + 1);
+    h.start = vload_i32(ss.start_pos, b);
+  } else {
+    h.o0 = h.o1 = h.start = 0;
+  }
+  const int ch0 = (lane & 31) * E;
 #pragma unroll
-  for (int k = 0; k < kScorePagesPerWave; ++k) {
-    const int ph = j0 + k < live ? __builtin_amdgcn_readlane(bt_v, k) : 0;
-    const float* m = a.meta + ((size_t)ph * a.H + g) * 2 * D + lane * E;
+  for (int hh = 0; hh < G; ++hh) {
+    const uint16_t* qh = a.q + ((size_t)b * a.Hq + g * G + hh) * D + ch0;
     if constexpr (E == 4) {
-      const float4 v = *(const float4*)m;
-      vals[k][0] = v.x; vals[k][1] = v.y; vals[k][2] = v.z; vals[k][3] = v.w;
+      const uint2 v = *(const uint2*)qh;
+      h.q[2 * hh] = v.x;
+      h.q[2 * hh + 1] = v.y;
     } else {
-      const float2 v = *(const float2*)m;
-      vals[k][0] = v.x; vals[k][1] = v.y;
+      h.q[hh] = *(const uint32_t*)qh;
     }
   }
+  return h;
+}
+
+// The query coefficients from a head's raw query, exactly as ScoreQuery::load.
+template <int D, int G>
+__device__ __forceinline__ ScoreQuery<D, G> score_query_of(const ScoreHead<D, G>& h) {
+  constexpr int E = ScoreQuery<D, G>::E;
+  ScoreQuery<D, G> q;
+  const bool max_row = lane_id() >= 32;
 #pragma unroll
-  for (int k = 0; k < kScorePagesPerWave; ++k) {
-    const int j = j0 + k;
-    if (j >= a.max_pages) break;
-    if (j >= live && j < P) continue;
-    const float best = j < live ? score_from_values<D, G>(q, vals[k]) : -INFINITY;
-    if (lane == 0) out[j] = best;
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float x = half_bits_to_float((h.q[hh * E / 2 + e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+      q.qc[hh][e] = max_row ? fmaxf(x, 0.0f) : fminf(x, 0.0f);
+    }
+  return q;
+}
+
+// Persistent scoring: the calling wave takes items gw, gw + TW, ... of the
+// rows * ceil(max_pages / 8) items (row-major: row = b * H + g, then 8-page
+// chunks).  For each item it scores pages below min(P, skip) (skip = the
+// first page the appended rows touch, when APPEND), writes -inf for pages at
+// or past P, and leaves pages in [skip, P) to the append block.  The next
+// item's head is loaded while the current item's metadata is in flight, so a
+// wave's loads never wait on a new block's first loads.  An item with no live
+// page loads no metadata.
+template <int D, int G, bool APPEND>
+__device__ __forceinline__ void score_items(const ScoreView& a, const ScoreSeqs& ss, int gw, int TW) {
+  constexpr int E = ScoreQuery<D, G>::E;
+  const int nchunks = (a.max_pages + kScorePagesPerWave - 1) / kScorePagesPerWave;
+  const int n_items = ss.rows * nchunks;
+  if (gw >= n_items) return;
+  const int lane = lane_id();
+  auto head_of = [&](int item) {
+    const int row = item / nchunks;
+    return score_head_load<D, G, APPEND>(a, ss, row / a.H, row % a.H, (item % nchunks) * kScorePagesPerWave);
+  };
+  ScoreHead<D, G> nh = head_of(gw);
+#pragma unroll 1
+  for (int it = gw;;) {
+    const ScoreHead<D, G> h = nh;
+    const int row = it / nchunks, j0 = (it % nchunks) * kScorePagesPerWave;
+    const int g = row % a.H;
+    const int nxt = it + TW;
+    const int nxt_c = min(nxt, n_items - 1);  // the last item's head is re-read, unused
+    float* out = a.scores + (size_t)row * a.max_pages;
+    const int P = (__builtin_amdgcn_readfirstlane(h.len) + kPage - 1) / kPage;
+    int skip = P;
+    if constexpr (APPEND) {
+      const int n = min(__builtin_amdgcn_readfirstlane(h.o1) - __builtin_amdgcn_readfirstlane(h.o0), 64);
+      const int st = __builtin_amdgcn_readfirstlane(h.start);
+      skip = n > 0 ? min(st / kPage, P) : P;
+    }
+    const int live = skip;
+    if (j0 < live) {  // wave-uniform
+      float vals[kScorePagesPerWave][E];
+#pragma unroll
+      for (int k = 0; k < kScorePagesPerWave; ++k) {
+        const int ph = j0 + k < live ? __builtin_amdgcn_readlane(h.bt, k) : 0;
+        const float* m = a.meta + ((size_t)ph * a.H + g) * 2 * D + lane * E;
+        if constexpr (E == 4) {
+          const float4 v = *(const float4*)m;
+          vals[k][0] = v.x; vals[k][1] = v.y; vals[k][2] = v.z; vals[k][3] = v.w;
+        } else {
+          const float2 v = *(const float2*)m;
+          vals[k][0] = v.x; vals[k][1] = v.y;
+        }
+      }
+      nh = head_of(nxt_c);
+      const ScoreQuery<D, G> q = score_query_of<D, G>(h);
+#pragma unroll
+      for (int k = 0; k < kScorePagesPerWave; ++k) {
+        const int j = j0 + k;
+        if (j >= a.max_pages) break;
+        if (j >= live && j < P) continue;
+        const float best = j < live ? score_from_values<D, G>(q, vals[k]) : -INFINITY;
+        if (lane == 0) out[j] = best;
+      }
+    } else {
+      nh = head_of(nxt_c);
+      const int j = j0 + lane;
+      if (lane < kScorePagesPerWave && j >= P && j < a.max_pages) out[j] = -INFINITY;
+    }
+    if (nxt >= n_items) break;
+    it = nxt;
   }
+}
+
+// Blocks of a persistent scoring grid: the device's resident capacity for
+// `kernel` (cached in `capacity`, one per kernel instance), less `reserved`
+// blocks launched ahead of them (but at least half the capacity), and no
+// more than the items need.  0 if the capacity cannot be queried.
+inline int score_grid_blocks(const void* kernel, int& capacity, int items, int reserved) {
+  if (capacity == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kScoreWaves * 64, 0) != hipSuccess ||
+        cus < 1 || per_cu < 1)
+      return 0;
+    capacity = cus * per_cu;
+  }
+  const int want = (items + kScoreWaves - 1) / kScoreWaves;
+  const int avail = capacity - reserved > capacity / 2 ? capacity - reserved : capacity / 2;
+  return want < avail ? want : avail;
 }
 
 }  // namespace kvq
