@@ -230,12 +230,10 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
     __shared__ int sm_hist[2 * kSelBins];
     __shared__ int sm_wtot[2 * NW];
     __shared__ uint32_t sm_wrange[2 * NW];
-    __shared__ int sm_rcnt[kSelRounds * NW];
     extern __shared__ int sm_dyn[];  // the block's pages [pps]
     list = sm_dyn;
     if (K < P) {
-      select_chunk<NW>(pre, a.scores + (size_t)row * a.max_pages, P, K, first, n,
-                       SelShared{sm_hist, sm_wtot, sm_wrange, sm_rcnt}, list);
+      select_chunk<NW>(pre, P, K, first, n, SelShared{sm_hist, sm_wtot, sm_wrange}, list);
     } else {
       for (int i = threadIdx.x; i < n; i += NW * 64) list[i] = first + i;
       __syncthreads();

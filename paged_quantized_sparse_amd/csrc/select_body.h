@@ -11,15 +11,15 @@
 //
 // Method, as in topk_pages.hip but for a 256-thread block and with every key
 // in registers: scores become order-preserving uint32 keys, thread t holding
-// those of pages t, t + 256, ... (up to 8); all keys share the bits above the highest
-// bit where the row's minimum and maximum key differ; MSB-first radix passes
-// of up to 11 bits over the bits below (LDS histograms filled from the
+// those of pages 8t .. 8t+7; all keys share the bits above the highest bit
+// where the row's minimum and maximum key differ; MSB-first radix passes of
+// up to 11 bits over the bits below (LDS histograms filled from the
 // registers) find the K-th largest key's prefix and how many keys on it are
 // still needed, stopping early once the chosen bin holds exactly that many.
 // Every wave finds the chosen bin itself (two barriers per pass).  Ranks then
-// come from ballots: per 256-page round, each wave's count of keys above and
-// on the prefix goes through LDS once, and a page's rank is the counts of
-// earlier rounds, earlier waves and lower lanes.
+// come from each thread's counts of its 8 keys above and on the prefix, one
+// wave scan and one block scan.  The code is kept short on purpose: it runs
+// once per launch, so its instruction fetch is part of its latency.
 #pragma once
 
 #include "kvq_device.h"
@@ -30,25 +30,24 @@ namespace kvq {
 constexpr int kSelBins = 2048;
 static_assert(kSelMaxPages < 65536, "rank counts are packed in 16 bits");
 
-constexpr int kSelRounds = kSelMaxPages / 256;  // keys per thread, at most
+constexpr int kSelKeys = kSelMaxPages / 256;  // keys per thread (pages 8t .. 8t+7)
 
 // LDS of the selection (the caller allocates).
 struct SelShared {
   int* hist;         // [2][kSelBins]
   int* wtot;         // [2][waves]
   uint32_t* wrange;  // [2][waves]
-  int* rcnt;         // [kSelRounds][waves]
 };
 
-// The row's first 8 * threads scores, loaded before the row length is known
-// (indices clamped into the row of max_pages scores), so these loads are in
-// flight with the kernel's other first loads.
+// Thread t's 8 scores (pages 8t .. 8t+7), loaded before the row length is
+// known (indices clamped into the row of max_pages scores), so these loads
+// are in flight with the kernel's other first loads.
 template <int NT>
 struct SelPrefetch {
-  float v[8];
+  float v[kSelKeys];
   __device__ __forceinline__ void load(const float* sc, int max_pages) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = sc[min(u * NT + (int)threadIdx.x, max_pages - 1)];
+    for (int u = 0; u < kSelKeys; ++u) v[u] = sc[min(kSelKeys * (int)threadIdx.x + u, max_pages - 1)];
   }
 };
 
@@ -57,33 +56,24 @@ struct SelPrefetch {
 // the caller's).  Called by all NW * 64 threads of the block; ends with a
 // barrier.
 template <int NW>
-__device__ __forceinline__ void select_chunk(const SelPrefetch<NW * 64>& pre, const float* sc, int P, int K,
-                                             int first, int n, const SelShared& sm, int* out) {
+__device__ __forceinline__ void select_chunk(const SelPrefetch<NW * 64>& pre, int P, int K, int first, int n,
+                                             const SelShared& sm, int* out) {
   constexpr int NT = NW * 64;
   constexpr int BPT = kSelBins / NT;  // histogram bins per thread
-  constexpr int U = kSelRounds;
-  static_assert(BPT == 8 && NT == 256, "bins per thread and rounds assume 256 threads");
+  constexpr int U = kSelKeys;
+  static_assert(BPT == 8 && NT * U == kSelMaxPages, "bins and keys per thread assume 256 threads");
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
-  const int rounds = (P + NT - 1) / NT;  // uniform
+  const int j0 = U * tid;  // this thread's first page
 
-  // ---- keys into registers (page u * NT + tid), the key range, the first
-  // histogram zeroed
-  float v[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (u < 8) v[u] = pre.v[u];
-    else if (u < rounds) v[u] = sc[min(u * NT + tid, P - 1)];
-  }
+  // ---- keys into registers, the key range, the first histogram zeroed
   uint32_t kr[U];
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (u < rounds) {
-      const bool valid = u * NT + tid < P;
-      kr[u] = valid ? float_key(v[u]) : 0u;
-      kmin = valid ? min(kmin, kr[u]) : kmin;
-      kmax = valid ? max(kmax, kr[u]) : kmax;
-    }
+    const bool valid = j0 + u < P;
+    kr[u] = valid ? float_key(pre.v[u]) : 0u;
+    kmin = valid ? min(kmin, kr[u]) : kmin;
+    kmax = valid ? max(kmax, kr[u]) : kmax;
   }
   *(int4*)(sm.hist + BPT * tid) = make_int4(0, 0, 0, 0);
   *(int4*)(sm.hist + BPT * tid + 4) = make_int4(0, 0, 0, 0);
@@ -113,10 +103,8 @@ __device__ __forceinline__ void select_chunk(const SelPrefetch<NW * 64>& pre, co
     const int nbins = 1 << bits;
     int* h = sm.hist + cur * kSelBins;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (u < rounds && u * NT + tid < P && (kr[u] & mask) == prefix)
-        atomicAdd(&h[(kr[u] >> shift) & (nbins - 1)], 1);
-    }
+    for (int u = 0; u < U; ++u)
+      if (j0 + u < P && (kr[u] & mask) == prefix) atomicAdd(&h[(kr[u] >> shift) & (nbins - 1)], 1);
     __syncthreads();
     // thread t owns bins lo .. lo+7 with lo = 2048 - 8(t+1): thread 0 the top
     // ones (bins at or above nbins stay empty); the next histogram is zeroed now
@@ -172,42 +160,33 @@ __device__ __forceinline__ void select_chunk(const SelPrefetch<NW * 64>& pre, co
 
   // ---- ranks.  Selected: every key whose resolved bits exceed the prefix,
   // and the first `need` (in page order) whose resolved bits equal it.  Each
-  // wave publishes, per round, its counts of both kinds (packed in one int);
-  // one barrier, then every page's counts before it are the earlier rounds,
-  // the earlier waves of its round and its lower lanes.
+  // thread counts both kinds among its 8 pages (packed in one int), a wave
+  // scan and a block scan give the counts before its first page, and it walks
+  // its pages in order.
+  int gt = 0, eq = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (u < rounds) {
-      const bool valid = u * NT + tid < P;
-      const uint32_t k = kr[u] & mask;
-      const uint64_t gm = __ballot(valid && k > prefix), em = __ballot(valid && k == prefix);
-      if (lane == 0) sm.rcnt[u * NW + w] = __builtin_popcountll(gm) | (__builtin_popcountll(em) << 16);
-    }
+    const uint32_t k = kr[u] & mask;
+    gt += j0 + u < P && k > prefix;
+    eq += j0 + u < P && k == prefix;
   }
+  const int packed = gt | (eq << 16);
+  const int incl = wave_incl_scan_add(packed);
+  if (lane == 63) sm.wtot[cur * NW + w] = incl;  // the buffer the last pass did not use
   __syncthreads();
-  int base = 0;  // packed counts of the rounds before u
+  const int wt = lane < NW ? sm.wtot[cur * NW + lane] : 0;
+  const int wrun = row16_incl_scan(wt);
+  const int bef = __builtin_amdgcn_readlane(wrun, w) - __builtin_amdgcn_readlane(wt, w) + incl - packed;
+  int gt_b = bef & 0xFFFF, eq_b = bef >> 16;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (u < rounds) {
-      int wbefore = 0, total = 0;
-#pragma unroll
-      for (int x = 0; x < NW; ++x) {
-        const int c = sm.rcnt[u * NW + x];
-        wbefore += x < w ? c : 0;
-        total += c;
-      }
-      const int j = u * NT + tid;
-      const bool valid = j < P;
-      const uint32_t k = kr[u] & mask;
-      const bool is_gt = valid && k > prefix, is_eq = valid && k == prefix;
-      const uint64_t gm = __ballot(is_gt), em = __ballot(is_eq);
-      const int bef = base + wbefore;
-      const int gt_b = (bef & 0xFFFF) + lanes_below(gm);
-      const int eq_b = (bef >> 16) + lanes_below(em);
-      const int rank = is_gt ? gt_b + min(eq_b, need) : (is_eq && eq_b < need ? gt_b + eq_b : -1);
-      if (rank >= first && rank < first + n) out[rank - first] = j;
-      base += total;
-    }
+    const uint32_t k = kr[u] & mask;
+    const bool valid = j0 + u < P;
+    const bool is_gt = valid && k > prefix, is_eq = valid && k == prefix;
+    const int rank = is_gt ? gt_b + min(eq_b, need) : (is_eq && eq_b < need ? gt_b + eq_b : -1);
+    gt_b += is_gt;
+    eq_b += is_eq;
+    if (rank >= first && rank < first + n) out[rank - first] = j0 + u;
   }
   __syncthreads();
 }
