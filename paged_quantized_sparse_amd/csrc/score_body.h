@@ -139,7 +139,7 @@ __device__ __forceinline__ ScoreQuery<D, G> score_query_of(const ScoreHead<D, G>
 
 // Persistent scoring: the calling wave takes items gw, gw + TW, ... of the
 // rows * ceil(max_pages / 8) items (row-major: row = b * H + g, then 8-page
-// chunks).  For each item it scores pages below min(P, skip) (skip = the
+// chunks, so waves running at the same time read neighbouring pages).  For each item it scores pages below min(P, skip) (skip = the
 // first page the appended rows touch, when APPEND), writes -inf for pages at
 // or past P, and leaves pages in [skip, P) to the append block.  The next
 // item's head is loaded while the current item's metadata is in flight, so a
@@ -207,10 +207,11 @@ __device__ __forceinline__ void score_items(const ScoreView& a, const ScoreSeqs&
   }
 }
 
-// Blocks of a persistent scoring grid: the device's resident capacity for
-// `kernel` (cached in `capacity`, one per kernel instance), less `reserved`
-// blocks launched ahead of them (but at least half the capacity), and no
-// more than the items need.  0 if the capacity cannot be queried.
+// Blocks of a scoring grid: one wave per item when that fits in the device's
+// resident capacity for `kernel` (cached in `capacity`, one per kernel
+// instance); otherwise a persistent grid of the capacity less `reserved`
+// blocks launched ahead of it (but at least half the capacity).  0 if the
+// capacity cannot be queried.
 inline int score_grid_blocks(const void* kernel, int& capacity, int items, int reserved) {
   if (capacity == 0) {
     int dev = 0, cus = 0, per_cu = 0;
@@ -222,8 +223,8 @@ inline int score_grid_blocks(const void* kernel, int& capacity, int items, int r
     capacity = cus * per_cu;
   }
   const int want = (items + kScoreWaves - 1) / kScoreWaves;
-  const int avail = capacity - reserved > capacity / 2 ? capacity - reserved : capacity / 2;
-  return want < avail ? want : avail;
+  if (want <= capacity) return want;
+  return capacity - reserved > capacity / 2 ? capacity - reserved : capacity / 2;
 }
 
 }  // namespace kvq
