@@ -487,6 +487,54 @@ def test_graph_replay_matches_eager(n):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_decode_stream_many_steps(fmt, fused):
+    """A decode loop: 24 consecutive steps of DecodeStep.run_with_append on a
+    ragged batch, each appending every sequence's next token (INT8_GROUP64
+    re-supplies its open 64-token group), crossing page and group boundaries,
+    with a fresh query per step.  After every step the whole cache (codes,
+    scale/zero bits, metadata) equals the oracle's one-shot build of the same
+    tokens, the selection passes the near-tie rule and the output is within
+    tolerance of the oracle's attention over that selection."""
+    _, runtime = kvq_mod()
+    T = 24
+    w = workloads.small(5).with_(fmt=fmt)
+    lens_end = w.seq_lens().astype(np.int64)
+    table, n_phys = w.block_table()
+    L0 = lens_end - T
+    assert (L0 >= 1).all()
+    src = lambda b: (w.keys(b), w.values(b))  # noqa: E731
+    cache, seqs = runtime.build_cache(w.fmt, n_phys, w.num_kv_heads, w.head_dim, table, L0, src)
+    st = runtime.DecodeStep(cache, seqs, w.num_q_heads, w.ratio_num, w.ratio_den, w.k_fixed, fused_select=fused)
+    rng = np.random.default_rng(4242 + fmt)
+    crossed = 0
+    for t in range(T):
+        lens_t = L0 + t + 1
+        crossed += int(((lens_t - 1) % PAGE == 0).sum())
+        seqs.seq_lens.copy_(torch.from_numpy(lens_t.astype(np.int32)))
+        app = runtime.DecodeAppend(cache, seqs, lens_t, src)
+        q = rng.standard_normal((w.batch, w.num_q_heads, w.head_dim)).astype(np.float16)
+        out = to_np(st.run_with_append(app, torch.from_numpy(q.view(np.int16)).cuda())).astype(np.float64)
+        oc, _ = oracle.build_cache(w, upto=lens_t)
+        k, v = to_np(cache.k_pages), to_np(cache.v_pages)
+        if fmt == workloads.FMT_FP16:
+            k, v = k.view(np.uint16), v.view(np.uint16)
+        assert np.array_equal(k, oc.k_pages) and np.array_equal(v, oc.v_pages), f"step {t}: storage"
+        if fmt != workloads.FMT_FP16:
+            assert np.array_equal(to_np(cache.kv_params).view(np.uint32), oc.params.view(np.uint32)), f"step {t}"
+        assert np.array_equal(to_np(cache.page_meta), oc.meta), f"step {t}: metadata"
+        osc, osel, ocnt, _ = oracle.decode_step(oc, table, lens_t, q, w.ratio_num, w.ratio_den, w.k_fixed,
+                                                st.k_cap, nthreads=8)
+        gsel, gcnt = to_np(st.sel_pages), to_np(st.sel_count)
+        check_selection_near_ties(gsel, gcnt, osc, osel, ocnt)
+        want = oracle.attention(oc, table, lens_t, q, gsel, gcnt)
+        err = np.abs(out - want).max()
+        assert err <= ATTN_ATOL, f"step {t}: max abs err {err:.3g}"
+    log(f"[stream] fmt {fmt} fused {fused}: {T} steps, {crossed} new pages opened")
+    assert crossed >= w.batch  # every sequence opened at least one page
+
+
 @pytest.mark.parametrize("fmt", [0, 1, 2])
 @pytest.mark.parametrize("rows", [1, 17, 64])
 def test_append_decode_equals_separate_calls_and_oracle(fmt, rows):
