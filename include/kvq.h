@@ -20,7 +20,9 @@
  * Conventions shared by every entry point:
  *   - Every array pointer is DEVICE memory owned by the caller, unless a
  *     comment says otherwise.  The library never allocates or frees memory and
- *     keeps no state between calls; calls are reentrant.
+ *     keeps no state between calls beyond a one-time, read-only lookup of the
+ *     device's occupancy limits (the first device a kernel is launched on);
+ *     calls are reentrant.
  *   - Each call only enqueues kernels on `stream` (a hipStream_t; NULL is the
  *     default stream) and returns.  Nothing synchronizes.  The caller keeps the
  *     buffers alive until the stream has drained.

@@ -59,10 +59,9 @@ __global__ __launch_bounds__(256) void append_scores_kernel(AppendScoreArgs a, i
 
 template <int FMT, int D, int G>
 hipError_t launch_k(const AppendScoreArgs& a, int rows, hipStream_t st) {
-  static int capacity = 0;
+  static const int capacity = resident_blocks(reinterpret_cast<const void*>(&append_scores_kernel<FMT, D, G>));
   const int items = rows * ((a.sc.max_pages + kScorePagesPerWave - 1) / kScorePagesPerWave);
-  const int blocks =
-      score_grid_blocks(reinterpret_cast<const void*>(&append_scores_kernel<FMT, D, G>), capacity, items, rows);
+  const int blocks = score_grid_blocks(capacity, items, rows);
   if (blocks < 1 || (long long)blocks + rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((append_scores_kernel<FMT, D, G>), dim3(rows + blocks), dim3(256), 0, st, a, rows);
   return hipGetLastError();

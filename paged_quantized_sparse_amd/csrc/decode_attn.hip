@@ -23,8 +23,12 @@
 // max.  Lanes, then waves, merge with log-sum-exp weights; each block writes a
 // partial (m, l, acc) per query head and split, and combine_kernel merges a
 // row's splits.  (Merging in the last-arriving split block instead needs a
-// device-scope release/acquire per block, which on gfx950 writes back and
-// invalidates the XCD's L2 each time and costs far more than a second launch.)
+// device-scope release per block, which on gfx950 writes back the XCD's L2
+// each time and costs far more than a second launch.)
+//
+// The SEL instances select the block's pages themselves (select_body.h) from
+// the row's scores instead of reading a selection: every block of the row
+// repeats the row's top-K and keeps the pages of its split's ranks.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "select_body.h"
@@ -470,24 +474,23 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
 
 }
 
-// LDS a launch of the SEL kernel would need beyond the device's per-block
-// limit: 0 if it fits.  Static LDS per instance and the limit are looked up
-// once.
+// Room for dynamic LDS a launch of the SEL kernel has under the device's
+// per-block limit (its static LDS taken off), or 0 if that cannot be queried.
+// Looked up once per instance (a function-local static).
 template <int FMT, int D, int G>
-size_t sel_lds_excess(size_t dyn) {
-  static size_t stat = 0, limit = 0;
-  if (limit == 0) {
+size_t sel_lds_room() {
+  static const size_t room = [] {
     hipFuncAttributes fa{};
     int dev = 0, lim = 0;
     if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&decode_attn_kernel<FMT, D, G, kAttnWaves, true>)) !=
             hipSuccess ||
         hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-      return dyn;
-    stat = fa.sharedSizeBytes;
-    limit = (size_t)lim;
-  }
-  return stat + dyn > limit ? stat + dyn - limit : 0;
+        hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        (size_t)lim < fa.sharedSizeBytes)
+      return (size_t)0;
+    return (size_t)lim - fa.sharedSizeBytes;
+  }();
+  return room;
 }
 
 template <int FMT, int D, int G>
@@ -495,7 +498,7 @@ hipError_t run(const AttnArgs& a, int B, hipStream_t st) {
   dim3 grid(a.max_splits, a.H, B);
   if (a.scores) {
     const size_t dyn = (size_t)a.pps * sizeof(int);
-    if (sel_lds_excess<FMT, D, G>(dyn)) return hipErrorInvalidConfiguration;
+    if (dyn > sel_lds_room<FMT, D, G>()) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((decode_attn_kernel<FMT, D, G, kAttnWaves, true>), grid, dim3(kAttnWaves * 64), dyn, st, a);
   } else {
     hipLaunchKernelGGL((decode_attn_kernel<FMT, D, G, kAttnWaves, false>), grid, dim3(kAttnWaves * 64), 0, st, a);

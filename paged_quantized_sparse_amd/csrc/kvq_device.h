@@ -1,8 +1,9 @@
 // kvq_device.h -- device helpers shared by the gfx950 kernels of libkvq.
 //
 // Wave64 reductions use DPP row operations inside a row of 16 lanes and
-// ds_bpermute (__shfl_xor) across rows.  All helpers are all-reduce: every
-// participating lane ends with the result.
+// ds_bpermute (__shfl_xor) across rows; the sums and extrema are all-reduce
+// (every participating lane ends with the result).  Scans and min/max over a
+// whole wave stay in DPP and readlane.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -72,8 +73,8 @@ __device__ __forceinline__ float min_contig(float x) {
   return x;
 }
 
-// Sum over the lanes congruent modulo S (S = 1, 2, 4, 8, 16, 32, 64): the
-// 64/S lanes l, l+S, l+2S, ... all end with their total.
+// Sum over the lanes congruent modulo S (S = 4, 8, 16, 32, 64): the 64/S
+// lanes l, l+S, l+2S, ... all end with their total.
 template <int S>
 __device__ __forceinline__ float sum_strided(float x) {
   static_assert(S >= 4 && S <= 64, "strides 4..64");

@@ -36,8 +36,9 @@ hipError_t launch_topk(const float* scores, const kvq_seqs& s, int num_kv_heads,
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 
 // Longest row (pages) the attention kernel selects in itself: each of its
-// 256 threads holds 8 keys in registers.  (More rounds of keys would make the
-// fully unrolled selection code, fetched at every launch, slower for all rows.)
+// 256 threads holds the keys of 8 consecutive pages in registers.  (More keys
+// per thread would cost registers, and unrolled code that every launch
+// fetches again, for all rows.)
 constexpr int kSelMaxPages = KVQ_SELECT_MAX_PAGES;
 
 // Selection done inside the attention kernel: the scores, the rule, and

@@ -20,9 +20,9 @@ __global__ __launch_bounds__(256) void page_scores_kernel(ScoreArgs a) {
 
 template <int D, int G>
 hipError_t launch_g(const ScoreArgs& a, hipStream_t st) {
-  static int capacity = 0;
+  static const int capacity = resident_blocks(reinterpret_cast<const void*>(&page_scores_kernel<D, G>));
   const int items = a.ss.rows * ((a.v.max_pages + kScorePagesPerWave - 1) / kScorePagesPerWave);
-  const int blocks = score_grid_blocks(reinterpret_cast<const void*>(&page_scores_kernel<D, G>), capacity, items, 0);
+  const int blocks = score_grid_blocks(capacity, items, 0);
   if (blocks < 1) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((page_scores_kernel<D, G>), dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();

@@ -207,21 +207,25 @@ __device__ __forceinline__ void score_items(const ScoreView& a, const ScoreSeqs&
   }
 }
 
-// Blocks of a scoring grid: one wave per item when that fits in the device's
-// resident capacity for `kernel` (cached in `capacity`, one per kernel
-// instance); otherwise a persistent grid of the capacity less `reserved`
-// blocks launched ahead of it (but at least half the capacity).  0 if the
-// capacity cannot be queried.
-inline int score_grid_blocks(const void* kernel, int& capacity, int items, int reserved) {
-  if (capacity == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kScoreWaves * 64, 0) != hipSuccess ||
-        cus < 1 || per_cu < 1)
-      return 0;
-    capacity = cus * per_cu;
-  }
+// Blocks of `kernel` (256 threads) the current device keeps resident at
+// once, or 0 if that cannot be queried.  Launchers look it up once, into a
+// function-local static (initialized once even with concurrent callers).
+inline int resident_blocks(const void* kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kScoreWaves * 64, 0) != hipSuccess ||
+      cus < 1 || per_cu < 1)
+    return 0;
+  return cus * per_cu;
+}
+
+// Blocks of a scoring grid: one wave per item when that fits in `capacity`
+// resident blocks; otherwise a persistent grid of the capacity less
+// `reserved` blocks launched ahead of it (but at least half the capacity).
+// 0 if the capacity is unknown.
+inline int score_grid_blocks(int capacity, int items, int reserved) {
+  if (capacity < 1) return 0;
   const int want = (items + kScoreWaves - 1) / kScoreWaves;
   if (want <= capacity) return want;
   return capacity - reserved > capacity / 2 ? capacity - reserved : capacity / 2;
