@@ -73,7 +73,7 @@ def test_workspace_bytes(lib):
     pps = lib.kvq_default_pages_per_split(1, 32, 2048, 615)
     assert pps == 40   # ceil(32 * 615 / 512) = 39, rounded up to a multiple of 4
     assert lib.kvq_default_pages_per_split(1, 4, 64, 16) == 16
-    assert lib.kvq_default_pages_per_split(64, 8, 2048, 615) == 64
+    assert lib.kvq_default_pages_per_split(64, 8, 2048, 615) == 128
 
 
 def _structs(fmt=1, page=16, d=128, H=4, B=1, maxp=8, meta=True):
