@@ -364,6 +364,54 @@ def test_select_attention_rows_at_the_limit():
     assert torch.equal(out, want)                     # same splits, same pages: same bits
 
 
+@pytest.mark.parametrize("fused", [True, False])
+def test_empty_sequences_in_batch(fused):
+    """Sequences of length 0 inside a ragged GQA batch: all their scores are
+    -inf, nothing is selected, their output rows are zero, and the other
+    sequences still match the oracle."""
+    kvq, runtime = kvq_mod()
+    w = workloads.small(5)
+    bt = built(("small", 5), w)
+    lens = bt.lens.copy()
+    empty = [1, 3]
+    lens[empty] = 0
+    seqs = kvq.Seqs(torch.from_numpy(lens.astype(np.int32)).cuda(), bt.seqs.block_table)
+    st = runtime.DecodeStep(bt.cache, seqs, w.num_q_heads, w.ratio_num, w.ratio_den, w.k_fixed, fused_select=fused)
+    out = to_np(st.run(bt.q_dev)).astype(np.float64)
+    assert np.isneginf(to_np(st.scores)[empty]).all()
+    gsel, gcnt = to_np(st.sel_pages), to_np(st.sel_count)
+    assert (gcnt[empty] == 0).all() and (gsel[empty] == -1).all()
+    assert (out[empty] == 0).all()
+    osc, osel, ocnt, _ = oracle.decode_step(bt.ocache, bt.table, lens, bt.q, w.ratio_num, w.ratio_den, w.k_fixed,
+                                            st.k_cap, nthreads=8)
+    check_selection_near_ties(gsel, gcnt, osc, osel, ocnt)
+    want = oracle.attention(bt.ocache, bt.table, lens, bt.q, gsel, gcnt)
+    assert np.abs(out - want).max() <= ATTN_ATOL
+
+
+def test_topk_longest_rows():
+    """kvq_topk_pages at its longest supported row (12000 pages), on random
+    and on tied scores, against the oracle's top-K exactly."""
+    kvq, _ = kvq_mod()
+    rng = np.random.default_rng(77)
+    B, H, maxp = 2, 2, 12000
+    lens = np.array([maxp * PAGE, 7777 * PAGE - 5], np.int32)
+    sc = rng.standard_normal((B, H, maxp)).astype(np.float32)
+    sc[1, 1] = np.round(sc[1, 1] * 4) / 4  # heavy ties
+    P = (lens + PAGE - 1) // PAGE
+    for b in range(B):
+        sc[b, :, P[b]:] = -np.inf
+    seqs = kvq.Seqs(torch.from_numpy(lens).cuda(), torch.zeros((B, maxp), dtype=torch.int32, device="cuda"))
+    for rn, rd, kf in [(3, 10, 0), (1, 50, 0)]:
+        k_cap = kvq.num_selected(maxp, rn, rd, kf)
+        sel = torch.empty((B, H, k_cap), dtype=torch.int32, device="cuda")
+        cnt = torch.empty((B, H), dtype=torch.int32, device="cuda")
+        kvq.kvq_topk_pages(torch.from_numpy(sc).cuda(), seqs, H, rn, rd, kf, sel, cnt)
+        osel, ocnt = oracle.topk(sc.astype(np.float64), lens, rn, rd, kf, k_cap)
+        assert np.array_equal(to_np(cnt), ocnt), (rn, rd)
+        assert np.array_equal(to_np(sel), osel), (rn, rd)
+
+
 @pytest.mark.parametrize("kind,n", CASES, ids=IDS)
 def test_end_to_end_step(kind, n):
     bt = built((kind, n), workload(kind, n))
