@@ -255,8 +255,9 @@ int32_t kvq_default_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t
 
 /*
  * kvq_read_probe -- measurement helper, not a step of the method: reads
- * `bytes` of device memory at `buf` once with a plain streaming kernel, so a
- * caller can time the bandwidth an HBM-bound kernel can reach on this GPU.
+ * `bytes` of device memory at `buf` once with a plain streaming kernel (one
+ * contiguous 64 KiB run per block, nontemporal 16-byte loads), so a caller
+ * can time the bandwidth an HBM-bound kernel can reach on this GPU.
  * buf 16-byte aligned, bytes a multiple of 16 (else KVQ_ERR_INVALID_ARG);
  * sink is one device uint32 the kernel may write (in practice never does).
  */

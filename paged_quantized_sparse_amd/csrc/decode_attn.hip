@@ -276,13 +276,13 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const size_t off = (tile + (size_t)(i * TPL + tg) * D + ch0) * T::ELEM;
-      r.kr[i] = *(const uint4*)((const char*)a.k_pages + off);
-      r.vr[i] = *(const uint4*)((const char*)a.v_pages + off);
+      r.kr[i] = load_stream_u4((const char*)a.k_pages + off);
+      r.vr[i] = load_stream_u4((const char*)a.v_pages + off);
       if constexpr (FMT == kInt8Token)
-        r.pr[i] = *(const float4*)(a.params + ((size_t)ph * a.H + g) * (kPage * 4) + (i * TPL + tg) * 4);
+        r.pr[i] = load_stream_f4(a.params + ((size_t)ph * a.H + g) * (kPage * 4) + (i * TPL + tg) * 4);
     }
     if constexpr (FMT == kInt8Group) {
-      const float4 gp = *(const float4*)(a.params + ((size_t)ph * a.H + g) * 4);
+      const float4 gp = load_stream_f4(a.params + ((size_t)ph * a.H + g) * 4);
 #pragma unroll
       for (int i = 0; i < NL; ++i) r.pr[i] = gp;
     }

@@ -180,10 +180,10 @@ __device__ __forceinline__ void score_items(const ScoreView& a, const ScoreSeqs&
         const int ph = j0 + k < live ? __builtin_amdgcn_readlane(h.bt, k) : 0;
         const float* m = a.meta + ((size_t)ph * a.H + g) * 2 * D + lane * E;
         if constexpr (E == 4) {
-          const float4 v = *(const float4*)m;
+          const float4 v = load_stream_f4(m);
           vals[k][0] = v.x; vals[k][1] = v.y; vals[k][2] = v.z; vals[k][3] = v.w;
         } else {
-          const float2 v = *(const float2*)m;
+          const float2 v = load_stream_f2(m);
           vals[k][0] = v.x; vals[k][1] = v.y;
         }
       }
