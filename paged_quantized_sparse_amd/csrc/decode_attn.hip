@@ -41,6 +41,19 @@ namespace {
 #endif
 constexpr int kAttnWaves = 4;
 constexpr int kPrefetch = KVQ_ATTN_PREFETCH;  // tiles in flight ahead of the one being consumed
+#ifndef KVQ_MF_PREFETCH
+#define KVQ_MF_PREFETCH 2
+#endif
+// The matrix-core form's K and V loads each cover half of every 128-byte
+// row of a tile (the other half comes with the next load), so they are
+// ordinary loads: the line stays in L2 for its second half (config 5: 166
+// against 178 us per attention call with the streaming hint).
+#ifndef KVQ_MF_STREAM
+#define KVQ_MF_STREAM 0
+#endif
+#ifndef KVQ_MF_WAVES
+#define KVQ_MF_WAVES 1
+#endif
 constexpr float kLazy = 8.0f;
 
 struct AttnArgs {
@@ -81,6 +94,70 @@ struct Tile {
 __device__ __forceinline__ float byte_to_float(uint32_t w, int i) { return (float)((w >> (8 * i)) & 0xFFu); }
 
 __device__ __forceinline__ half2v as_half2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
+
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));  // four bf16 bit patterns
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// Matrix-core form for a GQA group (G >= 2 query heads per KV head) over an
+// INT8 cache, where q.k and p.v are small GEMMs per 16-token page.  One
+// v_mfma_f32_16x16x16_f16 takes A[i][k] from lane i + 16(k/4), element k%4,
+// B[k][j] from lane j + 16(k/4), element k%4, and leaves D[i][j] in lane
+// j + 16(i/4), register i%4.
+//   Logits: C[t][h] = sum_k K[t][k] Q[h][k] with the page's 16 tokens as rows
+//   and the heads (padded to 16) as columns.  Lane l holds token l%16's
+//   channels (D/4)(l/16) .. +D/4 (one contiguous run of its row), MFMA m
+//   taking the four at offset 4m; the query is laid out to match, once.  C
+//   then sits in lane h + 16g as tokens 4g .. 4g+3 of head h, which is
+//   exactly the A layout of the second product.
+//   Output: O[h][c] += sum_t W[h][t] V[t][c] on v_mfma_f32_16x16x16_bf16
+//   (same layouts), W = p * v_scale split by truncation into three bf16
+//   parts (three MFMAs, ~2^-21 relative; bf16 keeps fp32's exponent range,
+//   so small weights keep their relative precision, which an fp16 split
+//   loses below 2^-14), V as exact bf16 codes.  B needs four tokens of one
+//   channel per lane, so each lane loads a run of its row (token
+//   4g + l%4) and a 4x4 byte transpose inside each lane quad (two DPP
+//   exchanges and byte permutes) hands lane (g, q, r) channel
+//   (D/4)q + 4j + r of tokens 4g .. 4g+3 for MFMA j.
+// The key codes become fp16 1024 + c by byte permute, as in the vector path.
+template <int FMT, int D, int G>
+struct MfmaPath {
+  static constexpr bool on = FMT != kFp16 && G >= 2 && G <= 16;
+  static constexpr int NM = D / 16;  // MFMAs per product (4 channels or columns each)
+  static constexpr int NU = D / 64;  // 16-byte loads per lane per tile, K and V each
+};
+
+// Lane-quad byte transpose: lane r of each quad holds word W_r with bytes
+// (token r, channels c..c+3); afterwards it holds (tokens 0..3, channel c+r).
+__device__ __forceinline__ uint32_t quad_transpose_bytes(uint32_t x, uint32_t sel1, uint32_t sel2) {
+  const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppXor1, 0xF, 0xF, false);
+  const uint32_t t = __builtin_amdgcn_perm(x, p1, sel1);
+  const uint32_t p2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)t, kDppXor2, 0xF, 0xF, false);
+  return __builtin_amdgcn_perm(t, p2, sel2);
+}
+
+// Pairs of fp32 values' upper halves (their bf16 truncations) packed as the
+// four elements of an MFMA operand.
+__device__ __forceinline__ short4v pack_bf16(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+  const uint32_t lo = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+  const uint32_t hi = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
+  return __builtin_bit_cast(short4v, ((uint64_t)hi << 32) | lo);
+}
+
+// Four INT8 codes (bytes of w) as exact bf16 values.
+__device__ __forceinline__ short4v codes_bf16(uint32_t w) {
+  return pack_bf16(__builtin_bit_cast(uint32_t, (float)(w & 0xFFu)),
+                   __builtin_bit_cast(uint32_t, (float)((w >> 8) & 0xFFu)),
+                   __builtin_bit_cast(uint32_t, (float)((w >> 16) & 0xFFu)),
+                   __builtin_bit_cast(uint32_t, (float)(w >> 24)));
+}
+
+// Four INT8 codes (bytes of w) as fp16 1024 + c.
+__device__ __forceinline__ half4v codes_1024(uint32_t w) {
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, w, 0x04010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, w, 0x04030402u);
+  return __builtin_bit_cast(half4v, ((uint64_t)hi << 32) | lo);
+}
 
 // grid (B * Hq), 256 threads: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
 // with M = max_s m_s.  Thread (part, c) takes channel c of splits part,
@@ -158,11 +235,18 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
 
 // SEL: the block selects its pages itself (select_body.h) from a.scores.
 template <int FMT, int D, int G, int NW, bool SEL>
-__global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MfmaPath<FMT, D, G>::on ? KVQ_MF_WAVES : 1)))
+void decode_attn_kernel(AttnArgs a) {
   static_assert(NW == 4, "the split merge and the combine assume 4 waves");
   using T = Tile<FMT, D>;
   constexpr int LPT = T::LPT, TPL = T::TPL, NL = T::NL, CH = T::CH;
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  using MP = MfmaPath<FMT, D, G>;
+  constexpr bool MF = MP::on;
+  static_assert(!MF || NL == MP::NU, "an INT8 tile row is NL 16-byte loads per lane in both forms");
+  // grid (KV head, sequence, split): blocks are dispatched split-major, so a
+  // ragged batch's full first splits go out first and its shorter last
+  // splits last, and all splits of a head share the XCD of block id mod 8
+  const int g = blockIdx.x, b = blockIdx.y, s = blockIdx.z;
   const int row = b * a.H + g;
   const int first = s * a.pps;
   const int w = wave_id();
@@ -211,7 +295,30 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
     }
     qsum[hh] = acc;
   }
+  // matrix-core form: lane l holds head l%16's channels (D/4)(l/16) .. +D/4
+  // (zeros for the padding heads), MFMA m the four at offset 4m
+  half4v qB[MP::NM];
+  float qs_mf = 0.0f;
+  if constexpr (MF) {
+    const int hn = lane & 15, gq = lane >> 4;
+    const uint32_t* qp = (const uint32_t*)(a.q + ((size_t)b * a.Hq + g * G + min(hn, G - 1)) * D + (D / 4) * gq);
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      const uint4 raw = *(const uint4*)(qp + 4 * i);
+      const uint32_t wd[4] = {hn < G ? raw.x : 0u, hn < G ? raw.y : 0u, hn < G ? raw.z : 0u, hn < G ? raw.w : 0u};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc += half_bits_to_float(wd[j] & 0xFFFFu) + half_bits_to_float(wd[j] >> 16);
+      qB[2 * i] = __builtin_bit_cast(half4v, ((uint64_t)wd[1] << 32) | wd[0]);
+      qB[2 * i + 1] = __builtin_bit_cast(half4v, ((uint64_t)wd[3] << 32) | wd[2]);
+    }
+    qs_mf = acc;
+  }
   __builtin_amdgcn_sched_barrier(0);  // keep every level-1 load ahead of the first use below
+  if constexpr (MF) {  // the head's whole sum over its four lanes
+    qs_mf += __shfl_xor(qs_mf, 16, kWave);
+    qs_mf += __shfl_xor(qs_mf, 32, kWave);
+  }
 
   const int L = __builtin_amdgcn_readfirstlane(len_v);
   const int P = (L + kPage - 1) / kPage;
@@ -262,17 +369,49 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) acc[hh][i] = 0.0f;
   }
+  // matrix-core form: (m, l, z) of head lane%16 over this lane's tokens (m the
+  // same in the head's four lanes), and O[h][c] accumulators in MFMA layout
+  float mf_m = -INFINITY, mf_l = 0.0f, mf_z = 0.0f;
+  float4v mf_acc[MP::NM];
+#pragma unroll
+  for (int j = 0; j < MP::NM; ++j) mf_acc[j] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 
   const size_t tile_elems = (size_t)kPage * D;
+  // scale/zero registers per tile: the matrix-core form wants tokens
+  // 4(l/16) .. +3 per lane (per token) or the tile's one group pair
+  constexpr int NP = MF ? (FMT == kInt8Token ? 4 : 1) : NL;
   struct PageRegs {
     uint4 kr[NL], vr[NL];
-    float4 pr[NL];
+    float4 pr[NP];
     int nvalid;
   };
   // issue every load of one (page, KV head) tile
   auto load_page = [&](int jl, int ph, PageRegs& r) {
     r.nvalid = min(kPage, L - jl * kPage);
     const size_t tile = ((size_t)ph * a.H + g) * tile_elems;
+    if constexpr (MF) {
+      // K: token l%16, run (D/4)(l/16); V: token 4(l/16) + l%4, run (D/4)((l/4)%4)
+      const char* kp = (const char*)a.k_pages + tile + (lane & 15) * D + (D / 4) * (lane >> 4);
+      const char* vp = (const char*)a.v_pages + tile + (4 * (lane >> 4) + (lane & 3)) * D + (D / 4) * ((lane >> 2) & 3);
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+#if KVQ_MF_STREAM
+        r.kr[u] = load_stream_u4(kp + 16 * u);
+        r.vr[u] = load_stream_u4(vp + 16 * u);
+#else
+        r.kr[u] = *(const uint4*)(kp + 16 * u);
+        r.vr[u] = *(const uint4*)(vp + 16 * u);
+#endif
+      }
+      if constexpr (FMT == kInt8Token) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          r.pr[i] = load_stream_f4(a.params + (((size_t)ph * a.H + g) * kPage + 4 * (lane >> 4) + i) * 4);
+      } else {
+        r.pr[0] = load_stream_f4(a.params + ((size_t)ph * a.H + g) * 4);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const size_t off = (tile + (size_t)(i * TPL + tg) * D + ch0) * T::ELEM;
@@ -290,6 +429,81 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
   // fold one loaded tile into the online softmax of the G heads
   auto consume_page = [&](PageRegs& r) {
     const int nvalid = r.nvalid;
+    if constexpr (MF) {
+      const int hn = lane & 15, g4 = lane >> 4;
+      // logits of tokens 4 g4 + i for head hn: C = K Q^T on the matrix cores
+      float4v cq = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const uint32_t kw[4] = {r.kr[u].x, r.kr[u].y, r.kr[u].z, r.kr[u].w};
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4)
+          cq = __builtin_amdgcn_mfma_f32_16x16x16f16(codes_1024(kw[d4]), qB[4 * u + d4], cq, 0, 0, 0);
+      }
+      float lg[4];
+      bool valid[4];
+      float lm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        valid[i] = 4 * g4 + i < nvalid && hn < G;
+        const float4 pp = r.pr[NP == 4 ? i : 0];
+        const float zz = __builtin_fmaf(-1024.0f, pp.x, pp.y);
+        const float part = __builtin_fmaf(pp.x, cq[i], zz * qs_mf);
+        lg[i] = valid[i] ? part * a.scale_log2 : -INFINITY;
+        lm = fmaxf(lm, lg[i]);
+      }
+      if (__ballot(lm > mf_m + kLazy)) {  // wave-uniform; rare once the max settles
+        // every lane of a head decides on the head's max over its four lanes
+        float hm = fmaxf(lm, __shfl_xor(lm, 16, kWave));
+        hm = fmaxf(hm, __shfl_xor(hm, 32, kWave));
+        const float mn = hm > mf_m + kLazy ? hm : mf_m;
+        const float alpha = mn == mf_m ? 1.0f : __builtin_amdgcn_exp2f(mf_m - mn);
+        mf_l *= alpha;
+        mf_z *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // O row 4 g4 + i takes that head's factor (from its lane)
+          const float ai = __shfl(alpha, 4 * g4 + i, kWave);
+#pragma unroll
+          for (int j = 0; j < MP::NM; ++j) mf_acc[j][i] *= ai;
+        }
+        mf_m = mn;
+      }
+      uint32_t wb0[4], wb1[4], wb2[4];  // w = b0 + b1 + b2, each a bf16 (low 16 bits zero)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = lg[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lg[i] - mf_m);
+        mf_l += p;
+        // padding slots may hold any bits: their scale/zero never reach the sums
+        const float4 pp = r.pr[NP == 4 ? i : 0];
+        const float w = valid[i] ? p * pp.z : 0.0f;
+        mf_z = valid[i] ? __builtin_fmaf(p, pp.w, mf_z) : mf_z;
+        wb0[i] = __builtin_bit_cast(uint32_t, w) & 0xFFFF0000u;
+        const float r1 = w - __builtin_bit_cast(float, wb0[i]);  // exact
+        wb1[i] = __builtin_bit_cast(uint32_t, r1) & 0xFFFF0000u;
+        const float r2 = r1 - __builtin_bit_cast(float, wb1[i]);  // exact
+        wb2[i] = __builtin_bit_cast(uint32_t, r2) & 0xFFFF0000u;
+      }
+      const short4v wa0 = pack_bf16(wb0[0], wb0[1], wb0[2], wb0[3]);
+      const short4v wa1 = pack_bf16(wb1[0], wb1[1], wb1[2], wb1[3]);
+      const short4v wa2 = pack_bf16(wb2[0], wb2[1], wb2[2], wb2[3]);
+      // values: quad byte transpose to four tokens of one channel, exact bf16
+      // codes, then O += (W_0 + W_1 + W_2) V
+      const uint32_t sel1 = (lane & 1) ? 0x07030501u : 0x02060004u;
+      const uint32_t sel2 = (lane & 2) ? 0x07060302u : 0x01000504u;
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const uint32_t vw[4] = {r.vr[u].x, r.vr[u].y, r.vr[u].z, r.vr[u].w};
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4) {
+          const short4v vb = codes_bf16(quad_transpose_bytes(vw[d4], sel1, sel2));
+          const int j = 4 * u + d4;
+          mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa2, vb, mf_acc[j], 0, 0, 0);
+          mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa1, vb, mf_acc[j], 0, 0, 0);
+          mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa0, vb, mf_acc[j], 0, 0, 0);
+        }
+      }
+      return;
+    }
     // Padding slots of a partial last page hold no data (possibly NaN bits):
     // zero their values and scale/zero with per-lane selects.  A branch that
     // rewrote the loaded registers would make the compiler wait for every
@@ -397,37 +611,38 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
       phys_v = a.block_table[(size_t)b * a.max_pages + jlog_v];
     }
     const int cnt = min(64, nw - k0);
-    // Software pipeline over a ring of R = kPrefetch + 1 register tiles: the
-    // loads of tiles k+1 .. k+kPrefetch are in flight while tile k is consumed.
+    // Software pipeline over a ring of R = PF + 1 register tiles: the loads of
+    // tiles k+1 .. k+PF are in flight while tile k is consumed.
     // Every load is unconditional (an index past the chunk re-reads its last
     // tile, which is cached), so the compiler's wait counts stay exact; a
     // conditional load would make it wait for all outstanding loads.  The main
     // loop is unrolled by R so ring indices are compile-time constants.
-    constexpr int R = kPrefetch + 1;
+    constexpr int PF = MF ? KVQ_MF_PREFETCH : kPrefetch;
+    constexpr int R = PF + 1;
     PageRegs ring[R];
     auto load_idx = [&](int k, PageRegs& r) {
       const int kk = min(k, cnt - 1);
       load_page(__builtin_amdgcn_readlane(jlog_v, kk), __builtin_amdgcn_readlane(phys_v, kk), r);
     };
 #pragma unroll
-    for (int u = 0; u < kPrefetch; ++u) load_idx(u, ring[u]);
+    for (int u = 0; u < PF; ++u) load_idx(u, ring[u]);
     int k = 0;
     for (; k + R <= cnt; k += R) {
 #pragma unroll
       for (int u = 0; u < R; ++u) {
-        load_idx(k + u + kPrefetch, ring[(u + kPrefetch) % R]);
+        load_idx(k + u + PF, ring[(u + PF) % R]);
         consume_page(ring[u]);
       }
     }
     // fewer than R tiles remain; they are already in ring[0 ..] (no loads here)
 #pragma unroll
-    for (int u = 0; u < kPrefetch; ++u)
+    for (int u = 0; u < PF; ++u)
       if (k + u < cnt) consume_page(ring[u]);
   }
 
   // ---- merge the token groups of the wave (lanes congruent mod LPT)
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
+  for (int hh = 0; hh < (MF ? 0 : G); ++hh) {
     const float M = max_strided<LPT>(m[hh]);
     const float f = m[hh] == -INFINITY ? 0.0f : exp2f(m[hh] - M);
     l[hh] = sum_strided<LPT>(l[hh] * f);
@@ -439,7 +654,29 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
   // ---- merge the block's waves through LDS and write the split's partials
   __shared__ float sm_ml[NW][G][2];
   __shared__ float sm_acc[NW][G][D];
-  if (tg == 0) {
+  if constexpr (MF) {
+    // (l, z) of head lane%16 summed over its four lanes; O[h][c] = acc + z,
+    // lane l register i holding head 4(l/16) + i at channel
+    // (D/4)(n/4) + 4j + n%4 of MFMA j, n = l%16
+    mf_l += __shfl_xor(mf_l, 16, kWave);
+    mf_l += __shfl_xor(mf_l, 32, kWave);
+    mf_z += __shfl_xor(mf_z, 16, kWave);
+    mf_z += __shfl_xor(mf_z, 32, kWave);
+    const int hn = lane & 15, g4 = lane >> 4;
+    if (lane < G) {
+      sm_ml[w][lane][0] = mf_m;
+      sm_ml[w][lane][1] = mf_l;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 4 * g4 + i;
+      const float zh = __shfl(mf_z, hh, kWave);
+      if (hh < G) {
+#pragma unroll
+        for (int j = 0; j < MP::NM; ++j) sm_acc[w][hh][(D / 4) * (hn >> 2) + 4 * j + (hn & 3)] = mf_acc[j][i] + zh;
+      }
+    }
+  } else if (tg == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
 #pragma unroll
@@ -495,7 +732,8 @@ size_t sel_lds_room() {
 
 template <int FMT, int D, int G>
 hipError_t run(const AttnArgs& a, int B, hipStream_t st) {
-  dim3 grid(a.max_splits, a.H, B);
+  if (a.max_splits > 65535 || B > 65535) return hipErrorInvalidConfiguration;
+  dim3 grid(a.H, B, a.max_splits);
   if (a.scores) {
     const size_t dyn = (size_t)a.pps * sizeof(int);
     if (dyn > sel_lds_room<FMT, D, G>()) return hipErrorInvalidConfiguration;

@@ -432,6 +432,38 @@ def test_end_to_end_step(kind, n):
     assert err <= ATTN_ATOL
 
 
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("hq,hkv,d", [(4, 2, 128), (16, 2, 128), (8, 4, 64), (16, 2, 64)],
+                         ids=["g2d128", "g8d128", "g2d64", "g8d64"])
+def test_group_sizes_and_head_dims(fmt, hq, hkv, d):
+    """Query groups of 2 and 8 heads per KV head, at head_dim 128 and 64, on
+    the INT8 caches (the matrix-core form of the attention kernel): attention
+    over the oracle's selection, the whole step through both selection paths
+    (which agree bit for bit) and the dense path all match the oracle."""
+    w = workloads.small(5).with_(name=f"gqa{hq}x{hkv}_d{d}_fmt{fmt}", fmt=fmt, num_q_heads=hq, num_kv_heads=hkv,
+                                 head_dim=d)
+    bt = built(("gqa", fmt, hq, hkv, d), w)
+    st = bt.step()
+    osc = oracle.page_scores(bt.ocache, bt.table, bt.lens, bt.q)
+    osel, ocnt = oracle.topk(osc, bt.lens, w.ratio_num, w.ratio_den, w.k_fixed, st.k_cap)
+    out = to_np(st.attend(bt.q_dev, torch.from_numpy(osel).cuda(), torch.from_numpy(ocnt).cuda()))
+    want = oracle.attention(bt.ocache, bt.table, bt.lens, bt.q, osel, ocnt)
+    err = np.abs(out.astype(np.float64) - want).max()
+    log(f"[gqa] {w.name}: attention on the oracle's selection, max abs err {err:.3g}")
+    assert err <= ATTN_ATOL
+    fus, sep = bt.step(fused_select=True), bt.step(fused_select=False)
+    o_fus = fus.run(bt.q_dev).clone()
+    o_sep = sep.run(bt.q_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(fus.sel_pages, sep.sel_pages) and torch.equal(o_fus, o_sep)
+    gsel, gcnt = to_np(fus.sel_pages), to_np(fus.sel_count)
+    check_selection_near_ties(gsel, gcnt, osc, osel, ocnt)
+    want = oracle.attention(bt.ocache, bt.table, bt.lens, bt.q, gsel, gcnt)
+    assert np.abs(to_np(o_fus).astype(np.float64) - want).max() <= ATTN_ATOL
+    dense = to_np(bt.step(dense=True).attend(bt.q_dev)).astype(np.float64)
+    assert np.abs(dense - oracle.attention(bt.ocache, bt.table, bt.lens, bt.q)).max() <= ATTN_ATOL
+
+
 def test_k_equals_all_pages_matches_dense():
     """Config 1 with K = 64 of 64 pages: the full selection path equals the
     dense path and the oracle's dense attention."""
