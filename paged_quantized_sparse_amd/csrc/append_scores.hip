@@ -23,13 +23,21 @@ struct AppendScoreArgs {
 };
 
 // 1-D grid: blocks 0 .. rows-1 append for row b * H_kv + g (then exit); the
-// rest are a persistent scoring grid whose waves take 8-page items.
-template <int FMT, int D, int G>
+// rest are a persistent scoring grid whose waves take 8-page items (BAL:
+// balanced over the live items, for a persistent grid over a ragged batch).
+template <int FMT, int D, int G, bool BAL>
 __global__ __launch_bounds__(256) void append_scores_kernel(AppendScoreArgs a, int rows) {
   const int L = blockIdx.x;
   if (L >= rows) {  // block-uniform
     const ScoreSeqs ss{a.seq_lens, a.ap.new_off, a.ap.start_pos, rows};
-    score_items<D, G, true>(a.sc, ss, (L - rows) * kScoreWaves + wave_id(), (gridDim.x - rows) * kScoreWaves);
+    const int gw = (L - rows) * kScoreWaves + wave_id(), TW = ((int)gridDim.x - rows) * kScoreWaves;
+    if constexpr (BAL) {
+      __shared__ int sm_pref[kScoreMaxSeqs + 1];
+      __shared__ int sm_wsum[kScoreWaves];
+      score_items_balanced<D, G, true>(a.sc, ss, gw, TW, ScoreShared{sm_pref, sm_wsum});
+    } else {
+      score_items<D, G, true>(a.sc, ss, gw, TW);
+    }
     return;
   }
   __shared__ float sm_meta[kMaxTouched][2][D];
@@ -59,11 +67,20 @@ __global__ __launch_bounds__(256) void append_scores_kernel(AppendScoreArgs a, i
 
 template <int FMT, int D, int G>
 hipError_t launch_k(const AppendScoreArgs& a, int rows, hipStream_t st) {
-  static const int capacity = resident_blocks(reinterpret_cast<const void*>(&append_scores_kernel<FMT, D, G>));
+  static const int capacity =
+      resident_blocks(reinterpret_cast<const void*>(&append_scores_kernel<FMT, D, G, false>));
+  static const int capacity_bal =
+      resident_blocks(reinterpret_cast<const void*>(&append_scores_kernel<FMT, D, G, true>));
   const int items = rows * ((a.sc.max_pages + kScorePagesPerWave - 1) / kScorePagesPerWave);
-  const int blocks = score_grid_blocks(capacity, items, rows);
+  int blocks = score_grid_blocks(capacity, items, rows);
+  if (blocks < 1) return hipErrorInvalidConfiguration;
+  const bool bal = score_balanced(rows, a.sc.H, a.sc.max_pages, blocks * kScoreWaves);
+  if (bal) blocks = score_grid_blocks(capacity_bal, items, rows);
   if (blocks < 1 || (long long)blocks + rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((append_scores_kernel<FMT, D, G>), dim3(rows + blocks), dim3(256), 0, st, a, rows);
+  if (bal)
+    hipLaunchKernelGGL((append_scores_kernel<FMT, D, G, true>), dim3(rows + blocks), dim3(256), 0, st, a, rows);
+  else
+    hipLaunchKernelGGL((append_scores_kernel<FMT, D, G, false>), dim3(rows + blocks), dim3(256), 0, st, a, rows);
   return hipGetLastError();
 }
 

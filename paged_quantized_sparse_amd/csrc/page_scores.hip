@@ -12,19 +12,34 @@ struct ScoreArgs {
   ScoreSeqs ss;
 };
 
-// Persistent grid of 256-thread blocks; each wave scores 8-page items.
-template <int D, int G>
+// Persistent grid of 256-thread blocks; each wave scores 8-page items
+// (balanced over the live items for a persistent grid over a ragged batch).
+template <int D, int G, bool BAL>
 __global__ __launch_bounds__(256) void page_scores_kernel(ScoreArgs a) {
-  score_items<D, G, false>(a.v, a.ss, blockIdx.x * kScoreWaves + wave_id(), gridDim.x * kScoreWaves);
+  const int gw = blockIdx.x * kScoreWaves + wave_id(), TW = gridDim.x * kScoreWaves;
+  if constexpr (BAL) {
+    __shared__ int sm_pref[kScoreMaxSeqs + 1];
+    __shared__ int sm_wsum[kScoreWaves];
+    score_items_balanced<D, G, false>(a.v, a.ss, gw, TW, ScoreShared{sm_pref, sm_wsum});
+  } else {
+    score_items<D, G, false>(a.v, a.ss, gw, TW);
+  }
 }
 
 template <int D, int G>
 hipError_t launch_g(const ScoreArgs& a, hipStream_t st) {
-  static const int capacity = resident_blocks(reinterpret_cast<const void*>(&page_scores_kernel<D, G>));
+  static const int capacity = resident_blocks(reinterpret_cast<const void*>(&page_scores_kernel<D, G, false>));
+  static const int capacity_bal = resident_blocks(reinterpret_cast<const void*>(&page_scores_kernel<D, G, true>));
   const int items = a.ss.rows * ((a.v.max_pages + kScorePagesPerWave - 1) / kScorePagesPerWave);
-  const int blocks = score_grid_blocks(capacity, items, 0);
+  int blocks = score_grid_blocks(capacity, items, 0);
   if (blocks < 1) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((page_scores_kernel<D, G>), dim3(blocks), dim3(256), 0, st, a);
+  if (score_balanced(a.ss.rows, a.v.H, a.v.max_pages, blocks * kScoreWaves)) {
+    blocks = score_grid_blocks(capacity_bal, items, 0);
+    if (blocks < 1) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((page_scores_kernel<D, G, true>), dim3(blocks), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((page_scores_kernel<D, G, false>), dim3(blocks), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -207,6 +207,151 @@ __device__ __forceinline__ void score_items(const ScoreView& a, const ScoreSeqs&
   }
 }
 
+// Sequences the balanced mapping below indexes in LDS.
+constexpr int kScoreMaxSeqs = 2048;
+
+// LDS of the balanced mapping (the kernel declares it).
+struct ScoreShared {
+  int* pref;  // [kScoreMaxSeqs + 1]: live items before sequence b
+  int* wsum;  // [kScoreWaves]
+};
+
+// Pages of sequence b the scoring waves score: those below its length P, or
+// below the first page the rows appended in the same launch touch (exactly
+// the `skip` of score_items).
+template <bool APPEND>
+__device__ __forceinline__ int live_pages(const ScoreSeqs& ss, int b) {
+  const int P = (ss.seq_lens[b] + kPage - 1) / kPage;
+  if constexpr (APPEND) {
+    const int n = min(ss.new_off[b + 1] - ss.new_off[b], 64);
+    return n > 0 ? min(ss.start_pos[b] / kPage, P) : P;
+  }
+  return P;
+}
+
+// Whether a persistent scoring grid of TW waves over B = rows / H sequences
+// takes the balanced mapping: a ragged batch leaves score_items' fixed
+// stride with some waves all of whose items are live and others with none,
+// and the most loaded waves set the launch's time.  Decided by the launcher.
+__host__ __device__ __forceinline__ bool score_balanced(int rows, int H, int max_pages, int TW) {
+  const int B = rows / H;
+  const long long items = (long long)rows * ((max_pages + kScorePagesPerWave - 1) / kScorePagesPerWave);
+  return B > 1 && B <= kScoreMaxSeqs && items > TW;
+}
+
+// Persistent scoring over the live items only.  Every block builds in LDS
+// the prefix over sequences of (live 8-page chunks) x H items, sequence-
+// major as score_items orders them; wave gw takes the contiguous items
+// [gw T / TW, (gw+1) T / TW) of the T live ones, so waves get equal work
+// however ragged the batch is.  Pages at or past each row's length get their
+// -inf first, rows dealt round-robin to the waves; pages in [skip, P) are the
+// append block's.  Each score is computed as in score_items.  Called by all
+// threads of the block (it has barriers).
+template <int D, int G, bool APPEND>
+__device__ __forceinline__ void score_items_balanced(const ScoreView& a, const ScoreSeqs& ss, int gw, int TW,
+                                                     const ScoreShared& sm) {
+  constexpr int E = ScoreQuery<D, G>::E;
+  constexpr int SPT = kScoreMaxSeqs / (kScoreWaves * 64);  // sequences per thread
+  const int H = a.H;
+  const int B = ss.rows / H;
+  const int lane = lane_id(), w = wave_id();
+
+  // ---- -inf past each row's length (stores only)
+  for (int r = gw; r < ss.rows; r += TW) {
+    const int P = (__builtin_amdgcn_readfirstlane(vload_i32(ss.seq_lens, r / H)) + kPage - 1) / kPage;
+    float* out = a.scores + (size_t)r * a.max_pages;
+    for (int j = P + lane; j < a.max_pages; j += kWave) out[j] = -INFINITY;
+  }
+
+  // ---- prefix of live items over the sequences (thread t: sequences
+  // SPT t .. SPT t + SPT-1)
+  int cnt[SPT];
+  int own = 0;
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int b = SPT * (int)threadIdx.x + i;
+    cnt[i] = b < B ? (live_pages<APPEND>(ss, b) + kScorePagesPerWave - 1) / kScorePagesPerWave * H : 0;
+    own += cnt[i];
+  }
+  const int incl = wave_incl_scan_add(own);
+  if (lane == kWave - 1) sm.wsum[w] = incl;
+  __syncthreads();
+  int run = incl - own;
+#pragma unroll
+  for (int x = 0; x < kScoreWaves; ++x) run += x < w ? sm.wsum[x] : 0;
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int b = SPT * (int)threadIdx.x + i;
+    if (b < B) sm.pref[b] = run;
+    run += cnt[i];
+  }
+  if (threadIdx.x == kScoreWaves * kWave - 1) sm.pref[B] = run;  // the total
+  __syncthreads();
+  const int total = sm.pref[B];
+  const int lo = (int)((long long)gw * total / TW), hi = (int)((long long)(gw + 1) * total / TW);
+  if (lo >= hi) return;
+
+  // ---- the sequence of item lo: the last b with pref[b] <= lo (pref is
+  // non-decreasing), in two ballot rounds over B <= 64 * 64 entries
+  const int stride = (B + kWave - 1) / kWave;
+  const uint64_t r1 = __ballot(lane * stride < B && sm.pref[min(lane * stride, B - 1)] <= lo);
+  const int seg = (63 - __builtin_clzll(r1)) * stride;  // r1 has lane 0 (pref[0] = 0 <= lo)
+  const uint64_t r2 = __ballot(lane < stride && seg + lane < B && sm.pref[min(seg + lane, B - 1)] <= lo);
+  int b = seg + (63 - __builtin_clzll(r2));
+  auto chunks_of = [&](int bb) { return (sm.pref[bb + 1] - sm.pref[bb]) / H; };
+  int nc = chunks_of(b);
+  int g = (lo - sm.pref[b]) / nc, c = (lo - sm.pref[b]) % nc;
+  // the item after (b, g, c) in the same order
+  auto step = [&](int& bb, int& gg, int& cc, int& ncc) {
+    if (++cc < ncc) return;
+    cc = 0;
+    if (++gg < H) return;
+    gg = 0;
+    do {
+      ++bb;
+    } while (bb < B - 1 && sm.pref[bb + 1] == sm.pref[bb]);
+    ncc = chunks_of(min(bb, B - 1));
+  };
+  ScoreHead<D, G> nh = score_head_load<D, G, APPEND>(a, ss, b, g, c * kScorePagesPerWave);
+#pragma unroll 1
+  for (int it = lo; it < hi; ++it) {
+    const ScoreHead<D, G> h = nh;
+    const int cb = b, cg = g, j0 = c * kScorePagesPerWave;
+    float* out = a.scores + ((size_t)cb * H + cg) * a.max_pages;
+    const int P = (__builtin_amdgcn_readfirstlane(h.len) + kPage - 1) / kPage;
+    int live = P;
+    if constexpr (APPEND) {
+      const int n = min(__builtin_amdgcn_readfirstlane(h.o1) - __builtin_amdgcn_readfirstlane(h.o0), 64);
+      const int st = __builtin_amdgcn_readfirstlane(h.start);
+      live = n > 0 ? min(st / kPage, P) : P;
+    }
+    float vals[kScorePagesPerWave][E];
+#pragma unroll
+    for (int k = 0; k < kScorePagesPerWave; ++k) {
+      const int ph = j0 + k < live ? __builtin_amdgcn_readlane(h.bt, k) : 0;
+      const float* m = a.meta + ((size_t)ph * H + cg) * 2 * D + lane * E;
+      if constexpr (E == 4) {
+        const float4 v = load_stream_f4(m);
+        vals[k][0] = v.x; vals[k][1] = v.y; vals[k][2] = v.z; vals[k][3] = v.w;
+      } else {
+        const float2 v = load_stream_f2(m);
+        vals[k][0] = v.x; vals[k][1] = v.y;
+      }
+    }
+    // the next item's head (the last item re-reads its own, unused)
+    if (it + 1 < hi) step(b, g, c, nc);
+    nh = score_head_load<D, G, APPEND>(a, ss, b, g, c * kScorePagesPerWave);
+    const ScoreQuery<D, G> q = score_query_of<D, G>(h);
+#pragma unroll
+    for (int k = 0; k < kScorePagesPerWave; ++k) {
+      const int j = j0 + k;
+      if (j >= live) break;
+      const float best = score_from_values<D, G>(q, vals[k]);
+      if (lane == 0) out[j] = best;
+    }
+  }
+}
+
 // Blocks of `kernel` (256 threads) the current device keeps resident at
 // once, or 0 if that cannot be queried.  Launchers look it up once, into a
 // function-local static (initialized once even with concurrent callers).

@@ -464,6 +464,44 @@ def test_group_sizes_and_head_dims(fmt, hq, hkv, d):
     assert np.abs(dense - oracle.attention(bt.ocache, bt.table, bt.lens, bt.q)).max() <= ATTN_ATOL
 
 
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_scores_ragged_persistent_grid(fmt):
+    """A ragged batch large enough that scoring runs as a persistent grid
+    balanced over the live items (40 sequences of 1 to 8191 tokens, 8 KV
+    heads, groups of 4): every score matches the oracle, pages past each
+    length are -inf, and the fused append + scores kernel writes the same
+    scores, bit for bit, as the decode-time append followed by
+    kvq_page_scores."""
+    kvq, runtime = kvq_mod()
+    w = workloads.small(5).with_(name=f"ragged40_fmt{fmt}", fmt=fmt, batch=40, num_q_heads=32, num_kv_heads=8,
+                                 len_lo=1, len_hi=8191)
+    table, n_phys = w.block_table()
+    lens = w.seq_lens()
+    src = lambda b: (w.keys(b), w.values(b))  # noqa: E731
+    qn = w.query()
+    q = torch.from_numpy(qn.view(np.int16)).cuda()
+    runs = []
+    for fused in (True, False):
+        cache, seqs = runtime.build_cache(w.fmt, n_phys, w.num_kv_heads, w.head_dim, table, lens, src,
+                                          prefill_lens=lens - 1)
+        app = runtime.DecodeAppend(cache, seqs, lens, src)
+        st = runtime.DecodeStep(cache, seqs, w.num_q_heads, w.ratio_num, w.ratio_den, w.k_fixed)
+        st.scores.fill_(float("nan"))
+        if fused:
+            kvq.kvq_append_decode_scores(cache, seqs, app.start, app.off, app.max_new, app.k_new, app.v_new, q,
+                                         st.scores)
+        else:
+            app.run()
+            kvq.kvq_page_scores(cache, seqs, q, st.scores)
+        torch.cuda.synchronize()
+        runs.append(to_np(st.scores))
+    assert np.array_equal(runs[0], runs[1])
+    ocache, _ = oracle.build_cache(w)
+    want = oracle.page_scores(ocache, table, lens, qn)
+    check_scores(runs[0], want, score_tolerance(ocache, table, lens, qn, w.group))
+    log(f"[ragged] {w.name}: {int(np.isfinite(want).sum())} live scores, max_pages {table.shape[1]}")
+
+
 def test_k_equals_all_pages_matches_dense():
     """Config 1 with K = 64 of 64 pages: the full selection path equals the
     dense path and the oracle's dense attention."""
