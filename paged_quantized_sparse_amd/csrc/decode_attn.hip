@@ -41,19 +41,7 @@ namespace {
 #endif
 constexpr int kAttnWaves = 4;
 constexpr int kPrefetch = KVQ_ATTN_PREFETCH;  // tiles in flight ahead of the one being consumed
-#ifndef KVQ_MF_PREFETCH
-#define KVQ_MF_PREFETCH 2
-#endif
-// The matrix-core form's K and V loads each cover half of every 128-byte
-// row of a tile (the other half comes with the next load), so they are
-// ordinary loads: the line stays in L2 for its second half (config 5: 166
-// against 178 us per attention call with the streaming hint).
-#ifndef KVQ_MF_STREAM
-#define KVQ_MF_STREAM 0
-#endif
-#ifndef KVQ_MF_WAVES
-#define KVQ_MF_WAVES 1
-#endif
+
 constexpr float kLazy = 8.0f;
 
 struct AttnArgs {
@@ -235,8 +223,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
 
 // SEL: the block selects its pages itself (select_body.h) from a.scores.
 template <int FMT, int D, int G, int NW, bool SEL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MfmaPath<FMT, D, G>::on ? KVQ_MF_WAVES : 1)))
-void decode_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
   static_assert(NW == 4, "the split merge and the combine assume 4 waves");
   using T = Tile<FMT, D>;
   constexpr int LPT = T::LPT, TPL = T::TPL, NL = T::NL, CH = T::CH;
@@ -393,15 +380,14 @@ void decode_attn_kernel(AttnArgs a) {
       // K: token l%16, run (D/4)(l/16); V: token 4(l/16) + l%4, run (D/4)((l/4)%4)
       const char* kp = (const char*)a.k_pages + tile + (lane & 15) * D + (D / 4) * (lane >> 4);
       const char* vp = (const char*)a.v_pages + tile + (4 * (lane >> 4) + (lane & 3)) * D + (D / 4) * ((lane >> 2) & 3);
+      // Each of these loads covers half of every 128-byte row of the tile (the
+      // other half comes with the next), so they are ordinary loads, which keep
+      // the line in L2 for its second half (config 5: 166 against 178 us per
+      // attention call with the streaming hint).
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
-#if KVQ_MF_STREAM
-        r.kr[u] = load_stream_u4(kp + 16 * u);
-        r.vr[u] = load_stream_u4(vp + 16 * u);
-#else
         r.kr[u] = *(const uint4*)(kp + 16 * u);
         r.vr[u] = *(const uint4*)(vp + 16 * u);
-#endif
       }
       if constexpr (FMT == kInt8Token) {
 #pragma unroll
@@ -617,7 +603,7 @@ void decode_attn_kernel(AttnArgs a) {
     // tile, which is cached), so the compiler's wait counts stay exact; a
     // conditional load would make it wait for all outstanding loads.  The main
     // loop is unrolled by R so ring indices are compile-time constants.
-    constexpr int PF = MF ? KVQ_MF_PREFETCH : kPrefetch;
+    constexpr int PF = kPrefetch;
     constexpr int R = PF + 1;
     PageRegs ring[R];
     auto load_idx = [&](int k, PageRegs& r) {
