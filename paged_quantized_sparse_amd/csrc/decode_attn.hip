@@ -84,18 +84,20 @@ __device__ __forceinline__ float byte_to_float(uint32_t w, int i) { return (floa
 __device__ __forceinline__ half2v as_half2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 
 typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));  // four bf16 bit patterns
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 // Matrix-core form for a GQA group (G >= 2 query heads per KV head) over an
-// INT8 cache, where q.k and p.v are small GEMMs per 16-token page.  One
-// v_mfma_f32_16x16x16_f16 takes A[i][k] from lane i + 16(k/4), element k%4,
-// B[k][j] from lane j + 16(k/4), element k%4, and leaves D[i][j] in lane
-// j + 16(i/4), register i%4.
-//   Logits: C[t][h] = sum_k K[t][k] Q[h][k] with the page's 16 tokens as rows
-//   and the heads (padded to 16) as columns.  Lane l holds token l%16's
-//   channels (D/4)(l/16) .. +D/4 (one contiguous run of its row), MFMA m
-//   taking the four at offset 4m; the query is laid out to match, once.  C
+// INT8 cache, where q.k and p.v are small GEMMs per 16-token page.  A
+// 16x16xKB MFMA takes A[i][k] from lane i + 16(k/KL), element k%KL, B[k][j]
+// from lane j + 16(k/KL), element k%KL (KL = KB/4 elements per lane), and
+// leaves D[i][j] in lane j + 16(i/4), register i%4.
+//   Logits: C[t][h] = sum_k K[t][k] Q[h][k] on v_mfma_f32_16x16x32_f16 (the
+//   full-rate shape on gfx950) with the page's 16 tokens as rows and the
+//   heads (padded to 16) as columns.  Lane l holds token l%16's channels
+//   (D/4)(l/16) .. +D/4 (one contiguous run of its row), MFMA m taking the
+//   eight at offset 8m; the query is laid out to match, once.  C
 //   then sits in lane h + 16g as tokens 4g .. 4g+3 of head h, which is
 //   exactly the A layout of the second product.
 //   Output: O[h][c] += sum_t W[h][t] V[t][c] on v_mfma_f32_16x16x16_bf16
@@ -283,7 +285,8 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
     qsum[hh] = acc;
   }
   // matrix-core form: lane l holds head l%16's channels (D/4)(l/16) .. +D/4
-  // (zeros for the padding heads), MFMA m the four at offset 4m
+  // (zeros for the padding heads), as groups of 4 (two per MFMA, which
+  // takes the eight at offset 8m)
   half4v qB[MP::NM];
   float qs_mf = 0.0f;
   if constexpr (MF) {
@@ -423,8 +426,13 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
       for (int u = 0; u < NL; ++u) {
         const uint32_t kw[4] = {r.kr[u].x, r.kr[u].y, r.kr[u].z, r.kr[u].w};
 #pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4)
-          cq = __builtin_amdgcn_mfma_f32_16x16x16f16(codes_1024(kw[d4]), qB[4 * u + d4], cq, 0, 0, 0);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const half4v k0 = codes_1024(kw[2 * h2]), k1 = codes_1024(kw[2 * h2 + 1]);
+          const half4v q0 = qB[4 * u + 2 * h2], q1 = qB[4 * u + 2 * h2 + 1];
+          const half8v ka = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+          const half8v qa = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+          cq = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qa, cq, 0, 0, 0);
+        }
       }
       float lg[4];
       bool valid[4];
