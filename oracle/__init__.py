@@ -18,6 +18,9 @@ Every function follows the pages it cites in ``kvq_oracle.c``:
   attention   -- softmax(q k^T / sqrt(d)) v over the selected pages
                  (intelliparadigm.com page, section 2.1; TinyServe page,
                  section 3.1)
+  attention_mass -- the share of dense attention weight on the selected
+                 pages (selection quality; TinyServe page, section 1 claims
+                 the value sits in a minority of the KV cache)
 """
 from __future__ import annotations
 
@@ -67,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.kvqo_topk.restype = I
         L.kvqo_attention.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, ctypes.c_double, P]
         L.kvqo_attention.restype = None
+        L.kvqo_attention_mass.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, ctypes.c_double, P]
+        L.kvqo_attention_mass.restype = None
         L.kvqo_decode_step.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, I, I, I,
                                        ctypes.c_double, P, P, P, P, I]
         L.kvqo_decode_step.restype = I
@@ -177,6 +182,25 @@ def attention(cache: Cache, block_table, seq_lens, q, sel_pages=None, sel_count=
     lib().kvqo_attention(cache.fmt, B, Hq, cache.H, d, bt.shape[1], _p(bt), _p(sl), _p(qb),
                          _p(cache.k_pages), _p(cache.v_pages), _p(cache.params), _p(sp), _p(sc), k_cap,
                          float(sm_scale), _p(out))
+    return out
+
+
+def attention_mass(cache: Cache, block_table, seq_lens, q, sel_pages, sel_count, sm_scale=None) -> np.ndarray:
+    """float64 [B][H_q]: the share of each head's dense softmax weight that
+    falls on the tokens of its KV group's selected pages (1 when every page is
+    selected; 0 for an empty sequence)."""
+    bt = np.ascontiguousarray(block_table, np.int32)
+    sl = np.ascontiguousarray(seq_lens, np.int32)
+    qb = _bits(q)
+    B, Hq, d = qb.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    sp = np.ascontiguousarray(sel_pages, np.int32)
+    sc = np.ascontiguousarray(sel_count, np.int32)
+    out = np.empty((B, Hq), dtype=np.float64)
+    lib().kvqo_attention_mass(cache.fmt, B, Hq, cache.H, d, bt.shape[1], _p(bt), _p(sl), _p(qb),
+                              _p(cache.k_pages), _p(cache.params), _p(sp), _p(sc), sp.shape[2],
+                              float(sm_scale), _p(out))
     return out
 
 

@@ -465,6 +465,57 @@ void kvqo_attention(int fmt, int B, int Hq, int H, int d, int max_pages,
 }
 
 /* ------------------------------------------------------------------------- */
+/* Selection quality: the share of dense attention that the selected pages    */
+/* carry.  For (b, h): the softmax weights w_t = exp(l_t - mu) / sum_t' ... of */
+/* every valid token t of sequence b (l_t = q.k_t * sm_scale, the dense       */
+/* attention of [KV] section 2.1), summed over the tokens of the pages        */
+/* selected for (b, h / G).  1 when every page is selected.  fp64.            */
+/* out: [B][Hq] double; 0 for an empty sequence.                              */
+/* ------------------------------------------------------------------------- */
+void kvqo_attention_mass(int fmt, int B, int Hq, int H, int d, int max_pages,
+                         const int32_t *block_table, const int32_t *seq_lens, const uint16_t *q,
+                         const void *k_pages, const float *params,
+                         const int32_t *sel_pages, const int32_t *sel_count, int k_cap,
+                         double sm_scale, double *out)
+{
+    int G = Hq / H;
+    for (int b = 0; b < B; ++b) {
+        int L = seq_lens[b];
+        int P = (L + PAGE - 1) / PAGE;
+        const int32_t *bt = block_table + (size_t)b * max_pages;
+        double *logit = malloc(sizeof(double) * ((size_t)L + 1));
+        char *chosen = calloc((size_t)P + 1, 1);
+        for (int h = 0; h < Hq; ++h) {
+            int g = h / G;
+            const uint16_t *qh = q + ((size_t)b * Hq + h) * d;
+            memset(chosen, 0, (size_t)P + 1);
+            for (int s = 0; s < sel_count[(size_t)b * H + g]; ++s) {
+                int j = sel_pages[((size_t)b * H + g) * k_cap + s];
+                if (j >= 0 && j < P) chosen[j] = 1;
+            }
+            double mu = -INFINITY;
+            for (int t = 0; t < L; ++t) {
+                double dot = 0.0;
+                for (int i = 0; i < d; ++i)
+                    dot += (double)half_bits_to_float(qh[i]) *
+                           (double)key_decoded(fmt, k_pages, params, bt, t, g, i, H, d);
+                logit[t] = dot * sm_scale;
+                if (logit[t] > mu) mu = logit[t];
+            }
+            double all = 0.0, sel = 0.0;
+            for (int t = 0; t < L; ++t) {
+                double w = exp(logit[t] - mu);
+                all += w;
+                if (chosen[t / PAGE]) sel += w;
+            }
+            out[(size_t)b * Hq + h] = L ? sel / all : 0.0;
+        }
+        free(chosen);
+        free(logit);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* One decode step: scores -> top-K -> attention, over the (sequence, KV head) units,   */
 /* which are independent; nthreads host threads take whole units.             */
 /* scores / sel_pages / sel_count / out are outputs as above.                 */
