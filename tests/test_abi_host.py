@@ -94,6 +94,7 @@ def test_attention_argument_errors(lib):
                                       None) == INVALID
     assert _attn(lib, c, s, hq=6) == INVALID                 # H_q not a multiple of H_kv
     assert _attn(lib, c, s, hq=12) == UNSUPPORTED            # group size 3
+    assert _attn(lib, c, s, hq=64) == UNSUPPORTED            # group size 16: past the supported 1, 2, 4, 8
     assert _attn(lib, c, s, cnt=None) == INVALID             # selection without counts
     assert _attn(lib, c, s, k_cap=0) == INVALID
     assert _attn(lib, c, s, pps=5000) == INVALID
@@ -168,3 +169,12 @@ def test_select_attention_argument_errors(lib):
 def test_select_limit_matches_header():
     import paged_quantized_sparse_amd as kvq
     assert f"#define KVQ_SELECT_MAX_PAGES {kvq.SELECT_MAX_PAGES} " in open(HEADER).read()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The decode step runs on one GPU; bench.py says so for --gpus N > 1
+    before it touches a device."""
+    r = subprocess.run(["python", os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
