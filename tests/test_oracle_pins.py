@@ -581,7 +581,14 @@ def test_attention_mass_pins(n):
     q = w.query()
     k_cap = table.shape[1]
     sc, sel, cnt, _ = oracle.decode_step(cache, table, lens, q, 3, 10, 0, k_cap)
-    m = oracle.attention_mass(cache, table, lens, q, sel, cnt)
+    # a selection whose count differs between the KV heads of a sequence (each
+    # row keeps a prefix of its top-K), so a row's own count must be used
+    cnt_v = np.maximum(cnt - np.arange(w.num_kv_heads)[None, :], np.minimum(cnt, 1)).astype(np.int32)
+    sel_v = sel.copy()
+    for b in range(w.batch):
+        for g in range(w.num_kv_heads):
+            sel_v[b, g, cnt_v[b, g]:] = -1
+    mv = oracle.attention_mass(cache, table, lens, q, sel_v, cnt_v)
     for b in range(w.batch):
         K, _ = decoded_keys_values(w, cache, table, b)
         L = int(lens[b])
@@ -589,8 +596,9 @@ def test_attention_mass_pins(n):
             g = h // w.group
             lg = K[:, g].astype(np.float64) @ q[b, h].astype(np.float64) / math.sqrt(w.head_dim)
             p = np.exp(lg - lg.max())
-            mask = np.isin(np.arange(L) // PAGE, sel[b, g, :cnt[b, g]])
-            assert abs(m[b, h] - p[mask].sum() / p.sum()) <= 1e-12
+            mask = np.isin(np.arange(L) // PAGE, sel_v[b, g, :cnt_v[b, g]])
+            assert abs(mv[b, h] - p[mask].sum() / p.sum()) <= 1e-12
+    m = oracle.attention_mass(cache, table, lens, q, sel, cnt)
     _, sel_all, cnt_all, _ = oracle.decode_step(cache, table, lens, q, 1, 1, 0, k_cap)
     assert np.all(oracle.attention_mass(cache, table, lens, q, sel_all, cnt_all) == 1.0)
     sel_c, cnt_c = _complement(sel, cnt, lens, k_cap)
