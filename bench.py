@@ -141,7 +141,8 @@ def main() -> int:
     table, n_phys = w.block_table()
     lens = w.seq_lens()
     # each sequence's rows are drawn once: the prefill and the decode-time
-    # append both read them (config 5 draws ~1.2M tokens per pass)
+    # append both read them (the 64-sequence ragged batch draws ~1.2M tokens
+    # per pass)
     src = functools.lru_cache(maxsize=None)(lambda b: (w.keys(b), w.values(b)))
     print(f"[bench] building {w.name} ...", file=sys.stderr, flush=True)
     base, seqs = runtime.build_cache(w.fmt, n_phys, w.num_kv_heads, w.head_dim, table, lens, src,
