@@ -113,7 +113,9 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 template <int FMT, int D, int G>
 struct MfmaPath {
   static constexpr bool on = FMT != kFp16 && G >= 2 && G <= 16;
-  static constexpr int NM = D / 16;  // MFMAs per product (4 channels or columns each)
+  // value MFMAs per page (16 output channels each); also the query's groups
+  // of 4 channels per lane (two per logits MFMA)
+  static constexpr int NM = D / 16;
   static constexpr int NU = D / 64;  // 16-byte loads per lane per tile, K and V each
 };
 
