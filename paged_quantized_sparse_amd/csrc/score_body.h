@@ -218,15 +218,18 @@ struct ScoreShared {
 
 // Pages of sequence b the scoring waves score: those below its length P, or
 // below the first page the rows appended in the same launch touch (exactly
-// the `skip` of score_items).
+// the `skip` of score_items), clamped into [0, max_pages] so that a length
+// outside its documented range can neither write past the row nor break the
+// prefix.
 template <bool APPEND>
-__device__ __forceinline__ int live_pages(const ScoreSeqs& ss, int b) {
+__device__ __forceinline__ int live_pages(const ScoreSeqs& ss, int b, int max_pages) {
   const int P = (ss.seq_lens[b] + kPage - 1) / kPage;
+  int live = P;
   if constexpr (APPEND) {
     const int n = min(ss.new_off[b + 1] - ss.new_off[b], 64);
-    return n > 0 ? min(ss.start_pos[b] / kPage, P) : P;
+    live = n > 0 ? min(ss.start_pos[b] / kPage, P) : P;
   }
-  return P;
+  return min(max(live, 0), max_pages);
 }
 
 // Whether a persistent scoring grid of TW waves over B = rows / H sequences
@@ -260,7 +263,7 @@ __device__ __forceinline__ void score_items_balanced(const ScoreView& a, const S
   for (int r = gw; r < ss.rows; r += TW) {
     const int P = (__builtin_amdgcn_readfirstlane(vload_i32(ss.seq_lens, r / H)) + kPage - 1) / kPage;
     float* out = a.scores + (size_t)r * a.max_pages;
-    for (int j = P + lane; j < a.max_pages; j += kWave) out[j] = -INFINITY;
+    for (int j = max(P, 0) + lane; j < a.max_pages; j += kWave) out[j] = -INFINITY;
   }
 
   // ---- prefix of live items over the sequences (thread t: sequences
@@ -270,7 +273,7 @@ __device__ __forceinline__ void score_items_balanced(const ScoreView& a, const S
 #pragma unroll
   for (int i = 0; i < SPT; ++i) {
     const int b = SPT * (int)threadIdx.x + i;
-    cnt[i] = b < B ? (live_pages<APPEND>(ss, b) + kScorePagesPerWave - 1) / kScorePagesPerWave * H : 0;
+    cnt[i] = b < B ? (live_pages<APPEND>(ss, b, a.max_pages) + kScorePagesPerWave - 1) / kScorePagesPerWave * H : 0;
     own += cnt[i];
   }
   const int incl = wave_incl_scan_add(own);
@@ -325,6 +328,7 @@ __device__ __forceinline__ void score_items_balanced(const ScoreView& a, const S
       const int st = __builtin_amdgcn_readfirstlane(h.start);
       live = n > 0 ? min(st / kPage, P) : P;
     }
+    live = min(max(live, 0), a.max_pages);  // as live_pages counts it
     float vals[kScorePagesPerWave][E];
 #pragma unroll
     for (int k = 0; k < kScorePagesPerWave; ++k) {
