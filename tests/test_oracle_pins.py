@@ -656,3 +656,47 @@ def test_selection_quality_report():
             row.append(f"rho {num}/{den}: top-K {top[live].mean():.3f}, random {rnd[live].mean():.3f}")
             assert np.all((top >= 0) & (top <= 1 + 1e-12))
         print(f"[quality] {w.name}: " + "; ".join(row))
+
+
+def test_selection_variants_report():
+    """Selection variants on the GQA workload, by the same measure (parity
+    unpinned; reported, not graded): the group score as the max of its query
+    heads' page scores (the method here) or their sum, and the top-K with the
+    first and the last page of each sequence forced in (K stays the same).
+    A head's own page scores come from the oracle with that head's query
+    copied over its whole group, so the group max is that head's score."""
+    w = workloads.small(5).with_(batch=16, len_lo=600, len_hi=4000)
+    cache, table = oracle.build_cache(w)
+    lens = w.seq_lens()
+    q = w.query()
+    k_cap = table.shape[1]
+    G, H = w.group, w.num_kv_heads
+    per_head = []
+    for hh in range(G):
+        qh = q.copy()
+        for g in range(H):
+            qh[:, g * G:(g + 1) * G] = q[:, g * G + hh][:, None]
+        per_head.append(oracle.page_scores(cache, table, lens, qh))
+    r_max = oracle.page_scores(cache, table, lens, q)
+    assert np.array_equal(r_max, np.maximum.reduce(per_head))   # the group score is the max over its heads
+    r_sum = np.sum(per_head, axis=0)
+    r_sum[np.isneginf(r_max)] = -np.inf
+    out = []
+    for num, den in ((1, 10), (3, 10)):
+        sel_m, cnt = oracle.topk(r_max, lens, num, den, 0, k_cap)
+        sel_s, cnt_s = oracle.topk(r_sum, lens, num, den, 0, k_cap)
+        assert np.array_equal(cnt, cnt_s)
+        # forced first and last pages: the top K-2 others plus those two
+        sel_f = np.full_like(sel_m, -1)
+        for b in range(w.batch):
+            P = (int(lens[b]) + PAGE - 1) // PAGE
+            for g in range(H):
+                K = int(cnt[b, g])
+                row = r_max[b, g, :P].copy()
+                forced = sorted({0, P - 1})[:K]
+                row[forced] = -np.inf
+                rest = np.lexsort((np.arange(P), -row))[:K - len(forced)]
+                sel_f[b, g, :K] = np.sort(np.concatenate([forced, rest]))
+        m = [oracle.attention_mass(cache, table, lens, q, s, cnt).mean() for s in (sel_m, sel_s, sel_f)]
+        out.append(f"rho {num}/{den}: max {m[0]:.3f}, sum {m[1]:.3f}, max + first/last page {m[2]:.3f}")
+    print(f"[variants] {w.name} B=16 L 600-4000: " + "; ".join(out))
