@@ -6,6 +6,7 @@ numpy routines on the unpaged arrays (fp16 casts, min/max, sort, dense
 softmax attention), hand-derived fixtures under tests/golden/, closed forms,
 and invariants (the no-underestimate property of the TinyServe page, section
 2.1; the scale/2 error bound of min/max quantization)."""
+import copy
 import json
 import math
 import os
@@ -700,3 +701,71 @@ def test_selection_variants_report():
         m = [oracle.attention_mass(cache, table, lens, q, s, cnt).mean() for s in (sel_m, sel_s, sel_f)]
         out.append(f"rho {num}/{den}: max {m[0]:.3f}, sum {m[1]:.3f}, max + first/last page {m[2]:.3f}")
     print(f"[variants] {w.name} B=16 L 600-4000: " + "; ".join(out))
+
+
+def _decoded_keys_upto(w, cache, table, b, L):
+    """Decoded keys fp32 [L][H][d] of sequence b's first L tokens as stored."""
+    t = np.arange(L)
+    kc = cache.k_pages[table[b][t // PAGE], :, t % PAGE]
+    if w.fmt == workloads.FMT_FP16:
+        return kc.view(np.float16).astype(np.float32)
+    p = (cache.params[table[b][t // PAGE], :, t % PAGE] if w.fmt == workloads.FMT_INT8_TOKEN
+         else cache.params[table[b][t // PAGE]])
+    return np_dequant(kc, p[..., 0:1], p[..., 1:2])
+
+
+def test_lazy_metadata_refresh_report():
+    """A decode stream of 24 steps, one token appended per sequence per step and
+    a fresh query each step, with page metadata refreshed every step (as built)
+    or every 4th step (the lazy refresh TinyServe section 5.2 suggests).  Counts
+    the (sequence, KV head, page) scores that fall below the page's true
+    max q.k (the no-underestimate property, TinyServe section 2.1) and the
+    selections that differ from the exact-metadata ones.  Exact refresh never
+    underestimates (asserted); the lazy figures are reported, not graded."""
+    w = workloads.small(4).with_(batch=6, seq_len=0, len_lo=300, len_hi=900)
+    T = 24
+    lens_end = w.seq_lens().astype(np.int64)
+    table, _ = w.block_table()
+    L0 = lens_end - T
+    rng = np.random.default_rng(77)
+    G, H, d = w.group, w.num_kv_heads, w.head_dim
+    results = {}
+    for every in (1, 4):
+        cache, _ = oracle.build_cache(w, upto=L0)
+        under = pages = changed = 0
+        worst = 0.0
+        for t in range(T):
+            L = L0 + t + 1
+            ks = np.concatenate([w.keys(b)[L[b] - 1:L[b]] for b in range(w.batch)])
+            vs = np.concatenate([w.values(b)[L[b] - 1:L[b]] for b in range(w.batch)])
+            oracle.append(cache, table, (L - 1).astype(np.int32), np.arange(w.batch + 1, dtype=np.int32), ks, vs)
+            if (t + 1) % every == 0:
+                oracle.page_meta(cache, table, L.astype(np.int32))
+            q = rng.standard_normal((w.batch, w.num_q_heads, d)).astype(np.float16)
+            r = oracle.page_scores(cache, table, L, q)
+            exact_cache = cache
+            if every != 1:  # the exact metadata of the same cache, for the selection comparison
+                exact_cache = copy.deepcopy(cache)
+                oracle.page_meta(exact_cache, table, L.astype(np.int32))
+            r_exact = oracle.page_scores(exact_cache, table, L, q)
+            k_cap = table.shape[1]
+            s_lazy, c = oracle.topk(r, L, 3, 10, 0, k_cap)
+            s_exact, _ = oracle.topk(r_exact, L, 3, 10, 0, k_cap)
+            changed += int((s_lazy != s_exact).any(axis=-1).sum())
+            for b in range(w.batch):
+                K = _decoded_keys_upto(w, cache, table, b, int(L[b])).astype(np.float64)
+                P = (int(L[b]) + PAGE - 1) // PAGE
+                for g in range(H):
+                    qq = q[b, g * G:(g + 1) * G].astype(np.float64)          # [G][d]
+                    dots = (K[:, g] @ qq.T).max(axis=1)                      # [L]: max over the group's heads
+                    true = np.array([dots[j * PAGE:min((j + 1) * PAGE, int(L[b]))].max() for j in range(P)])
+                    gap = true - r[b, g, :P]
+                    tol = 1e-9 * (1.0 + np.abs(true))
+                    under += int((gap > tol).sum())
+                    worst = max(worst, float(gap.max()))
+                    pages += P
+        results[every] = (under, pages, changed, worst)
+    assert results[1][0] == 0 and results[1][2] == 0
+    u, p, ch, worst = results[4]
+    print(f"[lazy] {w.name}, 6 sequences, 24 steps: refresh every 4th step -> {u} of {p} page scores "
+          f"underestimate (worst by {worst:.3g}), {ch} of {T * w.batch * H} selections differ from exact metadata")
