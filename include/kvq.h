@@ -20,8 +20,8 @@
  * Conventions shared by every entry point:
  *   - Every array pointer is DEVICE memory owned by the caller, unless a
  *     comment says otherwise.  The library never allocates or frees memory and
- *     keeps no state between calls beyond a one-time, read-only lookup of the
- *     device's occupancy limits (the first device a kernel is launched on);
+ *     keeps no state between calls beyond a one-time, read-only lookup of
+ *     each device's occupancy limits (on the first launch on that device);
  *     calls are reentrant.
  *   - Each call only enqueues kernels on `stream` (a hipStream_t; NULL is the
  *     default stream) and returns.  Nothing synchronizes.  The caller keeps the
@@ -44,7 +44,8 @@
  *   page_meta          [P_phys][H_kv][2][d] fp32: row 0 per-channel min, row 1 max
  * A stored key or value decodes to fmaf(code, scale, zero) (INT8) or to the
  * fp16 value (FP16).  Codes are unsigned 0..255 with zero = the quantized
- * row's minimum and scale = (max - min) / 255; a constant row has scale 1.
+ * row's minimum (a minimum of -0 is stored as +0) and scale = (max - min) /
+ * 255; a constant row has scale 1.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 #define KVQ_PAGE_SIZE 16
 #define KVQ_SELECT_MAX_PAGES 2048 /* longest row (pages) kvq_select_decode_attn takes */
 
@@ -253,6 +254,15 @@ kvq_status kvq_select_decode_attn(const kvq_cache *cache, const kvq_seqs *seqs,
  * means every page (sel_pages NULL).  Returns 0 for invalid sizes. */
 size_t kvq_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                 int32_t max_pages, int32_t k_cap, int32_t pages_per_split);
+
+/*
+ * kvq_num_selected -- K for a row of P pages under the selection rule of
+ * kvq_topk_pages ("TinyServe", section 5.1 selection_ratio): min(P, k_fixed)
+ * if k_fixed > 0, else clamp(ceil(ratio_num * P / ratio_den), 1, P) in
+ * integers; 0 for P <= 0.  A caller sizes sel_pages with it (k_cap =
+ * kvq_num_selected(max_pages, ...)).  Host function, no device work.
+ */
+int32_t kvq_num_selected(int32_t num_pages, int32_t ratio_num, int32_t ratio_den, int32_t k_fixed);
 
 /* The pages_per_split kvq_sparse_decode_attn uses when given 0. */
 int32_t kvq_default_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t max_pages, int32_t k_cap);

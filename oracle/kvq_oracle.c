@@ -24,7 +24,8 @@
  *         section 2.1, Attention(Q,K,V) = softmax(Q K^T / sqrt(d)) V.
  *
  * Readings where the pages are silent:
- *   - quantization: unsigned codes 0..255, zero = row minimum (fp32),
+ *   - quantization: unsigned codes 0..255, zero = row minimum (fp32, a
+ *     minimum of -0 stored as +0),
  *     scale = (max - min) / 255 in fp32, codes = clamp(rint((x - zero) * (1/scale)))
  *     with round-half-to-even and every operation rounded to fp32; a constant
  *     row gets scale 1 and all-zero codes; dequant = fmaf(code, scale, zero).
@@ -91,6 +92,14 @@ static void quant_scale(float lo, float hi, float *scale, float *inv)
         *scale = 1.0f;
         *inv = 1.0f;
     }
+}
+
+/* The zero-point is the row minimum; a minimum of -0 is stored as +0 (both  */
+/* are the number zero, and -0 + 0 = +0 while x + 0 = x otherwise), so the   */
+/* stored bits do not depend on which of two equal zeros came first.          */
+static float zero_point(float lo)
+{
+    return lo + 0.0f;
 }
 
 static uint8_t quant_code(float x, float zero, float inv)
@@ -199,6 +208,8 @@ int kvqo_append(int fmt, int B, int H, int d, int max_pages,
                         if (vx > vhi) vhi = vx;
                     }
                     float ks, kinv, vs, vinv;
+                    klo = zero_point(klo);
+                    vlo = zero_point(vlo);
                     quant_scale(klo, khi, &ks, &kinv);
                     quant_scale(vlo, vhi, &vs, &vinv);
                     for (int ch = 0; ch < d; ++ch) {
@@ -228,6 +239,8 @@ int kvqo_append(int fmt, int B, int H, int d, int max_pages,
                             if (vx > vhi) vhi = vx;
                         }
                     float ks, kinv, vs, vinv;
+                    klo = zero_point(klo);
+                    vlo = zero_point(vlo);
                     quant_scale(klo, khi, &ks, &kinv);
                     quant_scale(vlo, vhi, &vs, &vinv);
                     for (int i = g0; i < g0 + gn; ++i) {

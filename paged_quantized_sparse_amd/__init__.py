@@ -9,7 +9,8 @@ entry points raises.
 Entry points keep the C names:
   kvq_append_quant, kvq_append_decode, kvq_append_decode_scores, kvq_build_page_meta,
   kvq_page_scores, kvq_topk_pages,
-  kvq_sparse_decode_attn, kvq_select_decode_attn, kvq_attn_workspace_bytes, kvq_default_pages_per_split
+  kvq_sparse_decode_attn, kvq_select_decode_attn, kvq_attn_workspace_bytes, kvq_default_pages_per_split,
+  kvq_num_selected (as num_selected)
 """
 from __future__ import annotations
 
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_read_probe.restype = ctypes.c_int
         L.kvq_attn_workspace_bytes.argtypes = [I, I, I, I, I, I]
         L.kvq_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.kvq_num_selected.argtypes = [I, I, I, I]
+        L.kvq_num_selected.restype = I
         L.kvq_default_pages_per_split.argtypes = [I, I, I, I]
         L.kvq_default_pages_per_split.restype = I
         L.kvq_status_string.argtypes = [ctypes.c_int]
@@ -259,8 +262,6 @@ def kvq_read_probe(buf, sink, stream=None) -> None:
 
 
 def num_selected(P: int, ratio_num: int, ratio_den: int, k_fixed: int) -> int:
-    """K for P pages (same integer rule as the library); sizes sel_pages."""
-    if P <= 0:
-        return 0
-    k = k_fixed if k_fixed > 0 else (ratio_num * P + ratio_den - 1) // ratio_den
-    return max(1, min(P, k))
+    """K for P pages under the library's selection rule (kvq_num_selected);
+    sizes sel_pages."""
+    return int(lib().kvq_num_selected(int(P), int(ratio_num), int(ratio_den), int(k_fixed)))

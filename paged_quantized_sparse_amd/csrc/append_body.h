@@ -68,9 +68,9 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
     __shared__ float red[4][4];
     if (lane == 0) { red[w][0] = klo; red[w][1] = khi; red[w][2] = vlo; red[w][3] = vhi; }
     __syncthreads();
-    klo = fminf(fminf(red[0][0], red[1][0]), fminf(red[2][0], red[3][0]));
+    klo = zero_point(fminf(fminf(red[0][0], red[1][0]), fminf(red[2][0], red[3][0])));
     khi = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1]));
-    vlo = fminf(fminf(red[0][2], red[1][2]), fminf(red[2][2], red[3][2]));
+    vlo = zero_point(fminf(fminf(red[0][2], red[1][2]), fminf(red[2][2], red[3][2])));
     vhi = fmaxf(fmaxf(red[0][3], red[1][3]), fmaxf(red[2][3], red[3][3]));
     quant_params(klo, khi, gk[0], ginv[0]);
     quant_params(vlo, vhi, gv[0], ginv[1]);
@@ -148,8 +148,8 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
             klo = fminf(klo, kx[e]); khi = fmaxf(khi, kx[e]);
             vlo = fminf(vlo, vx[e]); vhi = fmaxf(vhi, vx[e]);
           }
-          klo = min_contig<64>(klo); khi = max_contig<64>(khi);
-          vlo = min_contig<64>(vlo); vhi = max_contig<64>(vhi);
+          klo = zero_point(min_contig<64>(klo)); khi = max_contig<64>(khi);
+          vlo = zero_point(min_contig<64>(vlo)); vhi = max_contig<64>(vhi);
           quant_params(klo, khi, ks, kinv);
           quant_params(vlo, vhi, vs, vinv);
           kz = klo;

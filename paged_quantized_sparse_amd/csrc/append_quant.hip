@@ -75,8 +75,8 @@ __global__ __launch_bounds__(256) void append_int8_token_kernel(AppendArgs a) {
     klo = fminf(klo, kx[e]); khi = fmaxf(khi, kx[e]);
     vlo = fminf(vlo, vx[e]); vhi = fmaxf(vhi, vx[e]);
   }
-  klo = min_contig<64>(klo); khi = max_contig<64>(khi);
-  vlo = min_contig<64>(vlo); vhi = max_contig<64>(vhi);
+  klo = zero_point(min_contig<64>(klo)); khi = max_contig<64>(khi);
+  vlo = zero_point(min_contig<64>(vlo)); vhi = max_contig<64>(vhi);
   float ks, kinv, vs, vinv;
   quant_params(klo, khi, ks, kinv);
   quant_params(vlo, vhi, vs, vinv);
@@ -126,9 +126,9 @@ __global__ __launch_bounds__(256) void append_int8_group_kernel(AppendArgs a) {
   const int w = wave_id();
   if (lane_id() == 0) { red[w][0] = klo; red[w][1] = khi; red[w][2] = vlo; red[w][3] = vhi; }
   __syncthreads();
-  klo = fminf(fminf(red[0][0], red[1][0]), fminf(red[2][0], red[3][0]));
+  klo = zero_point(fminf(fminf(red[0][0], red[1][0]), fminf(red[2][0], red[3][0])));
   khi = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1]));
-  vlo = fminf(fminf(red[0][2], red[1][2]), fminf(red[2][2], red[3][2]));
+  vlo = zero_point(fminf(fminf(red[0][2], red[1][2]), fminf(red[2][2], red[3][2])));
   vhi = fmaxf(fmaxf(red[0][3], red[1][3]), fmaxf(red[2][3], red[3][3]));
   float ks, kinv, vs, vinv;
   quant_params(klo, khi, ks, kinv);

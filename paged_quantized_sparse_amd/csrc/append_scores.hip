@@ -67,10 +67,11 @@ __global__ __launch_bounds__(256) void append_scores_kernel(AppendScoreArgs a, i
 
 template <int FMT, int D, int G>
 hipError_t launch_k(const AppendScoreArgs& a, int rows, hipStream_t st) {
-  static const int capacity =
-      resident_blocks(reinterpret_cast<const void*>(&append_scores_kernel<FMT, D, G, false>));
-  static const int capacity_bal =
-      resident_blocks(reinterpret_cast<const void*>(&append_scores_kernel<FMT, D, G, true>));
+  static std::atomic<long long> memo[kMaxDevices], memo_bal[kMaxDevices];
+  const int capacity = (int)per_device(
+      memo, [] { return resident_blocks(reinterpret_cast<const void*>(&append_scores_kernel<FMT, D, G, false>)); });
+  const int capacity_bal = (int)per_device(
+      memo_bal, [] { return resident_blocks(reinterpret_cast<const void*>(&append_scores_kernel<FMT, D, G, true>)); });
   const int items = rows * ((a.sc.max_pages + kScorePagesPerWave - 1) / kScorePagesPerWave);
   int blocks = score_grid_blocks(capacity, items, rows);
   if (blocks < 1) return hipErrorInvalidConfiguration;

@@ -36,11 +36,10 @@
 namespace kvq {
 namespace {
 
-#ifndef KVQ_ATTN_PREFETCH
-#define KVQ_ATTN_PREFETCH 2
-#endif
 constexpr int kAttnWaves = 4;
-constexpr int kPrefetch = KVQ_ATTN_PREFETCH;  // tiles in flight ahead of the one being consumed
+// tiles in flight ahead of the one being consumed (1, 3, 4 and 6 measured the
+// same or slower at 32K context)
+constexpr int kPrefetch = 2;
 
 constexpr float kLazy = 8.0f;
 
@@ -190,12 +189,17 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   for (int s0 = 0;; s0 += U * PARTS) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float ms = s0 + part + u * PARTS < ns ? mlv[u].x : -INFINITY;
+      // a slot past the row's splits holds whatever the workspace held (any
+      // bits, NaN included): its values are replaced, not multiplied by 0
+      const bool live = s0 + part + u * PARTS < ns;
+      const float ms = live ? mlv[u].x : -INFINITY;
+      const float as = live ? av[u] : 0.0f;
+      const float ls = live ? mlv[u].y : 0.0f;
       const float Mn = fmaxf(M, ms);
       const float fo = M == -INFINITY ? 0.0f : exp2f(M - Mn);
       const float fs = ms == -INFINITY ? 0.0f : exp2f(ms - Mn);
-      num = __builtin_fmaf(fs, av[u], num * fo);
-      den = __builtin_fmaf(fs, mlv[u].y, den * fo);
+      num = __builtin_fmaf(fs, as, num * fo);
+      den = __builtin_fmaf(fs, ls, den * fo);
       M = Mn;
     }
     if (s0 + U * PARTS >= ns) break;  // block-uniform
@@ -600,7 +604,10 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
     // page ids with one lane each (the first 64 come from the prologue)
     int jlog_v = jlog0, phys_v = phys0;
     if (k0 > 0) {  // wave-uniform; only when a split gives a wave more than 64 pages
-      const int idx = min(first + w + (k0 + lane) * NW, K - 1);
+      // clamped to the split's last page: a slot past the wave's count reads
+      // some page of this split (its load is never used), and the in-kernel
+      // list holds only the split's n entries
+      const int idx = min(first + w + (k0 + lane) * NW, first + n - 1);
       if constexpr (SEL)
         jlog_v = list[idx - first];
       else
@@ -710,10 +717,11 @@ __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
 
 // Room for dynamic LDS a launch of the SEL kernel has under the device's
 // per-block limit (its static LDS taken off), or 0 if that cannot be queried.
-// Looked up once per instance (a function-local static).
+// Looked up once per instance and device.
 template <int FMT, int D, int G>
 size_t sel_lds_room() {
-  static const size_t room = [] {
+  static std::atomic<long long> memo[kMaxDevices];
+  return (size_t)per_device(memo, [] {
     hipFuncAttributes fa{};
     int dev = 0, lim = 0;
     if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&decode_attn_kernel<FMT, D, G, kAttnWaves, true>)) !=
@@ -721,10 +729,9 @@ size_t sel_lds_room() {
         hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
         (size_t)lim < fa.sharedSizeBytes)
-      return (size_t)0;
-    return (size_t)lim - fa.sharedSizeBytes;
-  }();
-  return room;
+      return 0LL;
+    return (long long)((size_t)lim - fa.sharedSizeBytes);
+  });
 }
 
 template <int FMT, int D, int G>

@@ -44,6 +44,37 @@ int32_t splits_for(int32_t max_pages, int32_t k_cap, int32_t pps) {
   return (cap + pps - 1) / pps;
 }
 
+// Validation and launch of kvq_select_decode_attn.
+kvq_status select_decode_attn(const kvq_cache* cache, const kvq_seqs* seqs, const uint16_t* q, int32_t num_q_heads,
+                              const float* scores, int32_t ratio_num, int32_t ratio_den, int32_t k_fixed,
+                              int32_t k_cap, int32_t* sel_pages, int32_t* sel_count, float sm_scale,
+                              int32_t pages_per_split, float* out, void* ws, size_t ws_bytes, void* stream) {
+  kvq_status st = check_cache(cache, false);
+  if (st != KVQ_OK) return st;
+  if ((st = check_seqs(seqs)) != KVQ_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != KVQ_OK) return st;
+  if (!q || !out || !scores || !aligned16(q)) return KVQ_ERR_INVALID_ARG;
+  if (k_fixed < 0 || (k_fixed == 0 && (ratio_num < 1 || ratio_den < 1))) return KVQ_ERR_INVALID_ARG;
+  if ((sel_pages == nullptr) != (sel_count == nullptr)) return KVQ_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale)) return KVQ_ERR_INVALID_ARG;
+  if (pages_per_split < 0 || pages_per_split > 4096) return KVQ_ERR_INVALID_ARG;
+  if (seqs->max_pages > kvq::kSelMaxPages) return KVQ_ERR_UNSUPPORTED;
+  if (k_cap < kvq::num_selected(seqs->max_pages, ratio_num, ratio_den, k_fixed)) return KVQ_ERR_INVALID_ARG;
+  const int32_t pps = pages_per_split ? pages_per_split
+                                      : kvq_default_pages_per_split(seqs->batch, cache->num_kv_heads,
+                                                                    seqs->max_pages, k_cap);
+  const int32_t max_splits = splits_for(seqs->max_pages, k_cap, pps);
+  const size_t need = kvq_attn_workspace_bytes(seqs->batch, num_q_heads, cache->head_dim, seqs->max_pages, k_cap,
+                                               pps);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return KVQ_ERR_WORKSPACE;
+  const kvq::InKernelSelect ks{scores, ratio_num, ratio_den, k_fixed, sel_pages, sel_count};
+  const hipError_t e = kvq::launch_decode_attn(*cache, *seqs, q, num_q_heads, nullptr, nullptr, &ks, k_cap, sm_scale,
+                                               pps, max_splits, out, ws, (hipStream_t)stream);
+  if (e == hipErrorInvalidConfiguration) return KVQ_ERR_UNSUPPORTED;  // LDS of this row length and split
+  return from_hip(e);
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -134,6 +165,11 @@ size_t kvq_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head
   return (size_t)batch * num_q_heads * splits * ((size_t)head_dim + 2) * sizeof(float);
 }
 
+int32_t kvq_num_selected(int32_t num_pages, int32_t ratio_num, int32_t ratio_den, int32_t k_fixed) {
+  if (k_fixed <= 0 && (ratio_num < 1 || ratio_den < 1)) return num_pages > 0 ? 1 : 0;
+  return kvq::num_selected(num_pages, ratio_num, ratio_den, k_fixed);
+}
+
 int32_t kvq_default_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t max_pages, int32_t k_cap) {
   // Few, long splits: each block streams its pages with the next tile in
   // flight, and every split adds a partial to merge.  Aim for about two
@@ -176,29 +212,8 @@ kvq_status kvq_select_decode_attn(const kvq_cache* cache, const kvq_seqs* seqs, 
                                   int32_t k_fixed, int32_t k_cap, int32_t* sel_pages, int32_t* sel_count,
                                   float sm_scale, int32_t pages_per_split, float* out, void* ws, size_t ws_bytes,
                                   void* stream) {
-  kvq_status st = check_cache(cache, false);
-  if (st != KVQ_OK) return st;
-  if ((st = check_seqs(seqs)) != KVQ_OK) return st;
-  if ((st = check_heads(cache, num_q_heads)) != KVQ_OK) return st;
-  if (!q || !out || !scores || !aligned16(q)) return KVQ_ERR_INVALID_ARG;
-  if (k_fixed < 0 || (k_fixed == 0 && (ratio_num < 1 || ratio_den < 1))) return KVQ_ERR_INVALID_ARG;
-  if ((sel_pages == nullptr) != (sel_count == nullptr)) return KVQ_ERR_INVALID_ARG;
-  if (!(sm_scale == sm_scale)) return KVQ_ERR_INVALID_ARG;
-  if (pages_per_split < 0 || pages_per_split > 4096) return KVQ_ERR_INVALID_ARG;
-  if (seqs->max_pages > kvq::kSelMaxPages) return KVQ_ERR_UNSUPPORTED;
-  if (k_cap < kvq::num_selected(seqs->max_pages, ratio_num, ratio_den, k_fixed)) return KVQ_ERR_INVALID_ARG;
-  const int32_t pps = pages_per_split ? pages_per_split
-                                      : kvq_default_pages_per_split(seqs->batch, cache->num_kv_heads,
-                                                                    seqs->max_pages, k_cap);
-  const int32_t max_splits = splits_for(seqs->max_pages, k_cap, pps);
-  const size_t need = kvq_attn_workspace_bytes(seqs->batch, num_q_heads, cache->head_dim, seqs->max_pages, k_cap,
-                                               pps);
-  if (!ws || ws_bytes < need || !aligned16(ws)) return KVQ_ERR_WORKSPACE;
-  const kvq::InKernelSelect ks{scores, ratio_num, ratio_den, k_fixed, sel_pages, sel_count};
-  const hipError_t e = kvq::launch_decode_attn(*cache, *seqs, q, num_q_heads, nullptr, nullptr, &ks, k_cap, sm_scale,
-                                               pps, max_splits, out, ws, (hipStream_t)stream);
-  if (e == hipErrorInvalidConfiguration) return KVQ_ERR_UNSUPPORTED;  // LDS of this row length and split
-  return from_hip(e);
+  return select_decode_attn(cache, seqs, q, num_q_heads, scores, ratio_num, ratio_den, k_fixed, k_cap, sel_pages,
+                            sel_count, sm_scale, pages_per_split, out, ws, ws_bytes, stream);
 }
 
 kvq_status kvq_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

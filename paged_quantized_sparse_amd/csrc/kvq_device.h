@@ -172,41 +172,25 @@ __device__ __forceinline__ int vload_i32(const int32_t* p, size_t i) {
 // their scale/zero, page metadata): the nontemporal hint marks the lines for
 // early eviction instead of normal allocation, which on this part raises the
 // rate of a plain streaming read from ~5.5 to ~6.3 TB/s (grid-stride) and to
-// ~7.1 TB/s when each block reads contiguous runs.  Switched off with
-// -DKVQ_STREAM_LOADS=0.
-#ifndef KVQ_STREAM_LOADS
-#define KVQ_STREAM_LOADS 1
-#endif
+// ~7.1 TB/s when each block reads contiguous runs.
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 load_stream_u4(const void* p) {
-#if KVQ_STREAM_LOADS
   const u32x4v v = __builtin_nontemporal_load((const u32x4v*)p);
   return make_uint4(v.x, v.y, v.z, v.w);
-#else
-  return *(const uint4*)p;
-#endif
 }
 
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float2 load_stream_f2(const float* p) {
-#if KVQ_STREAM_LOADS
   const f32x2v v = __builtin_nontemporal_load((const f32x2v*)p);
   return make_float2(v.x, v.y);
-#else
-  return *(const float2*)p;
-#endif
 }
 
 __device__ __forceinline__ float4 load_stream_f4(const float* p) {
-#if KVQ_STREAM_LOADS
   const f32x4v v = __builtin_nontemporal_load((const f32x4v*)p);
   return make_float4(v.x, v.y, v.z, v.w);
-#else
-  return *(const float4*)p;
-#endif
 }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -226,6 +210,14 @@ __device__ __forceinline__ void quant_params(float lo, float hi, float& scale, f
     scale = 1.0f;
     inv = 1.0f;
   }
+}
+
+// The zero-point of a row is its minimum, with a minimum of -0 stored as +0
+// (x + 0 is +0 for either zero and x otherwise), so the stored bits do not
+// depend on which of two equal zeros a min reduction happens to return.
+__device__ __forceinline__ float zero_point(float lo) {
+#pragma clang fp contract(off)
+  return lo + 0.0f;
 }
 
 __device__ __forceinline__ uint32_t quant_code(float x, float zero, float inv) {

@@ -7,9 +7,28 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/kvq.h"
 
 namespace kvq {
+
+// A host-side lookup of a device property (occupancy, LDS room) memoized per
+// device: computed on the first launch on each device (the current one) and
+// reused after.  `memo` starts zeroed and holds value + 1; concurrent first
+// calls compute the same value, so the race is benign.
+constexpr int kMaxDevices = 64;
+template <class F>
+long long per_device(std::atomic<long long> (&memo)[kMaxDevices], F compute) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return compute();
+  long long v = memo[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    v = compute() + 1;
+    memo[dev].store(v, std::memory_order_relaxed);
+  }
+  return v - 1;
+}
 
 hipError_t launch_append(const kvq_cache& c, const kvq_seqs& s, const int32_t* start_pos,
                          const int32_t* new_off, int max_new, const uint16_t* k_new,

@@ -28,8 +28,11 @@ __global__ __launch_bounds__(256) void page_scores_kernel(ScoreArgs a) {
 
 template <int D, int G>
 hipError_t launch_g(const ScoreArgs& a, hipStream_t st) {
-  static const int capacity = resident_blocks(reinterpret_cast<const void*>(&page_scores_kernel<D, G, false>));
-  static const int capacity_bal = resident_blocks(reinterpret_cast<const void*>(&page_scores_kernel<D, G, true>));
+  static std::atomic<long long> memo[kMaxDevices], memo_bal[kMaxDevices];
+  const int capacity = (int)per_device(
+      memo, [] { return resident_blocks(reinterpret_cast<const void*>(&page_scores_kernel<D, G, false>)); });
+  const int capacity_bal = (int)per_device(
+      memo_bal, [] { return resident_blocks(reinterpret_cast<const void*>(&page_scores_kernel<D, G, true>)); });
   const int items = a.ss.rows * ((a.v.max_pages + kScorePagesPerWave - 1) / kScorePagesPerWave);
   int blocks = score_grid_blocks(capacity, items, 0);
   if (blocks < 1) return hipErrorInvalidConfiguration;

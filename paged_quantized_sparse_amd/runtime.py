@@ -6,7 +6,7 @@ A decode step, as the TinyServe page (lpnh.cn, section 3.1) orders it:
   append the new token (and re-quantize its open group) -> refresh the
   metadata of the pages that changed -> score every page -> top-K ->
   attention over the selected pages (split-K + combine).
-DecodeStep.run_with_append does it in four launches: append + metadata +
+DecodeStep.run_with_append does it in three launches: append + metadata +
 scores (kvq_append_decode_scores), then top-K inside the attention kernel
 (kvq_select_decode_attn), then the split combine.
 """

@@ -58,8 +58,8 @@ def test_library_never_allocates_or_synchronizes():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == 2
-    assert "#define KVQ_ABI_VERSION 2" in open(HEADER).read()
+    assert lib.kvq_abi_version() == 3
+    assert "#define KVQ_ABI_VERSION 3" in open(HEADER).read()
     for s, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP"), (99, b"unknown")]:
         assert word in lib.kvq_status_string(s)
 
@@ -178,3 +178,16 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_num_selected_rule_matches_oracle(lib):
+    """The library's K rule (kvq_num_selected, which also sizes k_cap in the
+    binding) equals the oracle's on every row length up to 2048 pages and on
+    the fixed-K and ratio-1 cases; degenerate rows select nothing."""
+    import oracle
+    for P in range(0, 2049):
+        for rn, rd, kf in ((3, 10, 0), (1, 1, 0), (1, 7, 0), (0, 1, 16), (0, 1, 5000)):
+            assert lib.kvq_num_selected(P, rn, rd, kf) == oracle.num_selected(P, rn, rd, kf), (P, rn, rd, kf)
+    assert lib.kvq_num_selected(2048, 3, 10, 0) == 615
+    assert lib.kvq_num_selected(1024, 3, 10, 0) == 308
+    assert lib.kvq_num_selected(-5, 3, 10, 0) == 0

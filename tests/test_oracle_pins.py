@@ -108,6 +108,21 @@ def test_quant_golden_rows():
         assert dec.tolist() == [float(v) for v in row["decoded"]]
 
 
+def test_quant_zero_point_of_a_signed_zero_minimum_is_plus_zero():
+    """A row whose minimum is zero stores the zero-point +0 whichever sign the
+    first zero had (the reading that makes the stored bits independent of
+    reduction order); codes and decoded values are those of the number 0."""
+    nz, pz = np.float16(-0.0), np.float16(0.0)
+    for row in ([nz, pz, 1.0, 3.0], [pz, nz, 1.0, 3.0], [nz, 2.0], [nz, nz, nz], [pz, pz]):
+        x = np.array([row], np.float16)
+        cache, _ = one_token_cache(workloads.FMT_INT8_TOKEN, x)
+        z = cache.params[0, 0, 0, 1]
+        assert z.view(np.uint32) == 0, row
+        codes = cache.k_pages[0, 0, 0, :x.shape[1]]
+        assert all(int(c) == 0 for c, v in zip(codes, row) if v == 0)
+        assert np_dequant(codes[:1], cache.params[0, 0, 0, 0], z)[0].view(np.uint32) == 0
+
+
 def _random_rows(rng, n, d):
     x = rng.standard_normal((n, d)).astype(np.float32)
     x[: n // 3] *= 30.0                                      # wide rows
