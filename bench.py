@@ -10,14 +10,21 @@ Steps rotate over `--layers` independent copies of the layer cache (distinct
 device buffers), so a step never finds the previous step's working set in the
 256 MB Infinity Cache, as in a real decode pass over many layers.
 
-Prints one JSON line: achieved GB/s of the whole step (metadata of every page
-+ the selected KV tiles with their scale/zero, i.e. the bytes the method must
-read), microseconds per step (and its p10/p50/p90 over rotations), the sparse
-attention call's own GB/s against the 8 TB/s HBM peak (kvq_sparse_decode_attn
-over the step's selection, timed with HIP events on the launch stream), what a
-plain streaming-read kernel reaches over 2 GiB on the same GPU, the decode-time
-append alone, and the CPU oracle timed on the host on the same workload (all
-threads this process may use, up to 16, and one thread).
+Prints one JSON line:
+  * achieved GB/s of the whole step (metadata of every page + the selected KV
+    tiles with their scale/zero, i.e. the bytes the method must read) and
+    microseconds per step, with its p10/p50/p90 over rotations;
+  * `roofline`: the attention call exactly as the step runs it (selection
+    inside the split-K kernel, then the split combine), HIP events on its
+    launch stream around HIP-graph replays, against the 8 TB/s HBM peak;
+  * secondary figures, each timed the same way (graph replays, HIP events):
+    the attention over a given selection (no in-kernel selection), the fused
+    append + scores kernel, the decode-time append alone, the one-time cache
+    build (quantize + metadata of the whole prefill), and what a plain
+    streaming-read kernel reaches over 2 GiB on this GPU;
+  * the CPU oracle timed on the host on the same workload (all threads this
+    process may use, up to 16, and one thread), the oracle's own cache build,
+    and parity statistics of this run's step against the oracle.
 """
 from __future__ import annotations
 
@@ -57,8 +64,9 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_attn_cfg4_traffic.json")
 
 
 def measured_traffic():
-    """HBM bytes per launch of the attention split kernel from the committed
-    rocprofv3 FETCH_SIZE/WRITE_SIZE record, or None once its sources changed."""
+    """HBM bytes per call of the step's attention (selecting split kernel +
+    combine) from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE record, or
+    None once its sources changed."""
     import hashlib
     try:
         rec = json.load(open(TRAFFIC_RECORD))
@@ -73,28 +81,73 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(w, seconds: float, threads: int = 0, built=None):
-    """The oracle's decode step (scores -> top-K -> attention) on host threads
-    (0: all this process may use, at most 16)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(w, seconds: float, threads: int, built):
+    """The oracle's decode step (scores -> top-K -> attention) on host threads;
+    (median seconds, runs, last result)."""
     import oracle
-    cache, table = built if built is not None else oracle.build_cache(w)
+    cache, table = built
     lens, q = w.seq_lens(), w.query()
     k_cap = oracle.num_selected(int(table.shape[1]), w.ratio_num, w.ratio_den, w.k_fixed)
-    if threads <= 0:
-        try:
-            threads = len(os.sched_getaffinity(0))
-        except AttributeError:
-            threads = os.cpu_count() or 1
-        threads = max(1, min(16, threads))
     times = []
+    res = None
     t_end = time.perf_counter() + seconds
     while True:
         t0 = time.perf_counter()
-        oracle.decode_step(cache, table, lens, q, w.ratio_num, w.ratio_den, w.k_fixed, k_cap, nthreads=threads)
+        res = oracle.decode_step(cache, table, lens, q, w.ratio_num, w.ratio_den, w.k_fixed, k_cap, nthreads=threads)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() > t_end or len(times) >= 20:
             break
-    return float(np.median(times)), threads, len(times), (cache, table)
+    return float(np.median(times)), len(times), res
+
+
+def parity_stats(w, built, oracle_step, gpu):
+    """This run's step against the oracle on the same inputs: cache codes and
+    metadata, scores, selection (near-tie rule) and output."""
+    import oracle
+    cache, table = built
+    lens, q = w.seq_lens(), w.query()
+    osc, osel, ocnt, oout = oracle_step
+    st = {}
+    k = gpu["k_pages"]
+    st["k_codes_bit_exact"] = bool(np.array_equal(k.view(np.uint16) if k.dtype == np.int16 else k, cache.k_pages))
+    st["metadata_exact"] = bool(np.array_equal(gpu["meta"], cache.meta))
+    fin = np.isfinite(osc)
+    st["scores_max_rel_err"] = float(np.max(np.abs(gpu["scores"][fin] - osc[fin]) / np.maximum(np.abs(osc[fin]),
+                                                                                               1e-30)))
+    sel, cnt = gpu["sel"], gpu["cnt"]
+    rows = same = swaps = 0
+    for b in range(sel.shape[0]):
+        for g in range(sel.shape[1]):
+            K = int(ocnt[b, g])
+            rows += 1
+            d = set(sel[b, g, :K].tolist()) ^ set(osel[b, g, :K].tolist())
+            same += not d and int(cnt[b, g]) == K
+            swaps += len(d) // 2
+    st["selection_rows_identical"] = f"{same}/{rows}"
+    st["near_tie_page_swaps"] = swaps
+    want = oracle.attention(cache, table, lens, q, sel, cnt)
+    st["out_max_abs_err"] = float(np.abs(gpu["out"].astype(np.float64) - want).max())
+    st["out_max_abs_err_vs_oracle_step"] = float(np.abs(gpu["out"].astype(np.float64) - oout).max())
+    st["tolerance"] = 2e-3
+    return st
 
 
 def main() -> int:
@@ -107,7 +160,7 @@ def main() -> int:
     ap.add_argument("--eager", action="store_true", help="launch every kernel from the host (no HIP graph)")
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle legs (CPU baseline and parity)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB 10 times (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -147,6 +200,34 @@ def main() -> int:
     print(f"[bench] building {w.name} ...", file=sys.stderr, flush=True)
     base, seqs = runtime.build_cache(w.fmt, n_phys, w.num_kv_heads, w.head_dim, table, lens, src,
                                      prefill_lens=lens - 1, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def events():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    # ---- the one-time cache build (quantize + metadata of the prefill),
+    # rows already resident in HBM; run again on the built cache, which it
+    # rewrites with the same values
+    pre = lens.astype(np.int64) - 1
+    k_all = torch.from_numpy(np.ascontiguousarray(np.concatenate([src(b)[0][:pre[b]] for b in range(w.batch)]))
+                             .view(np.int16)).to(dev)
+    v_all = torch.from_numpy(np.ascontiguousarray(np.concatenate([src(b)[1][:pre[b]] for b in range(w.batch)]))
+                             .view(np.int16)).to(dev)
+    zeros_b = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    off_all = torch.from_numpy(np.concatenate([[0], np.cumsum(pre)]).astype(np.int32)).to(dev)
+    pre_seqs = kvq.Seqs(torch.from_numpy(pre.astype(np.int32)).to(dev), seqs.block_table)
+    build_us = []
+    for _ in range(3):
+        e0, e1 = events()
+        e0.record(stream)
+        kvq.kvq_append_quant(base, seqs, zeros_b, off_all, int(pre.max()), k_all, v_all)
+        kvq.kvq_build_page_meta(base, pre_seqs)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        build_us.append(e0.elapsed_time(e1) * 1e3)
+    del k_all, v_all
+    cache_build_us = float(np.median(build_us))
+
     layers = [base]
     for _ in range(args.layers - 1):
         layers.append(kvq.PagedCache(base.format, base.num_phys_pages, base.num_kv_heads, base.head_dim,
@@ -158,41 +239,62 @@ def main() -> int:
     appends = [runtime.DecodeAppend(c, seqs, lens, src, device=dev) for c in layers]
     steps = [runtime.DecodeStep(c, seqs, w.num_q_heads, w.ratio_num, w.ratio_den, w.k_fixed, dense=dense,
                                 pages_per_split=args.pages_per_split, device=dev) for c in layers]
+    NL = len(layers)
     torch.cuda.synchronize()
 
     def one_step(i):
-        steps[i % len(layers)].run_with_append(appends[i % len(layers)], q)
+        steps[i % NL].run_with_append(appends[i % NL], q)
 
     # warm-up (eager), which also fills every layer's selection
-    for i in range(max(args.warmup, len(layers))):
+    for i in range(max(args.warmup, NL)):
         one_step(i)
     torch.cuda.synchronize()
 
+    def rotation_graph(body):
+        """One HIP graph running body(li) for every layer li in turn."""
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for li in range(NL):
+                    body(li)
+        stream.wait_stream(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def per_call_us(g, replays):
+        """Microseconds per body call: HIP events on the launch stream around
+        `replays` back-to-back replays of a rotation graph."""
+        e0, e1 = events()
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (replays * NL)
+
     # HIP graphs: one per layer, and one holding a whole rotation over the
     # layers (a multi-layer decode pass is captured once and replayed)
-    stream = torch.cuda.current_stream()
     graphs = rotation = None
     if not args.eager:
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
         graphs = []
         with torch.cuda.stream(cap):
-            for li in range(len(layers)):
+            for li in range(NL):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
                     one_step(li)
                 graphs.append(g)
-            rotation = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(rotation, stream=cap):
-                for li in range(len(layers)):
-                    one_step(li)
         stream.wait_stream(cap)
-        for _ in range(2):
-            rotation.replay()
+        rotation = rotation_graph(one_step)
+        rotation.replay()
         torch.cuda.synchronize()
 
     # ---- timed region: exactly `steps` decode steps
-    n_rot, rest = divmod(args.steps, len(layers))
+    n_rot, rest = divmod(args.steps, NL)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if graphs is not None:
@@ -208,58 +310,67 @@ def main() -> int:
     ms_per_step = elapsed / args.steps * 1e3
 
     # ---- per-step spread (outside the timed region): HIP events around each
-    # replay of the rotation graph, or around each eager step
+    # replay of the rotation graph, or around each eager rotation
     per_step_us = []
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * 50)]
+    ev = [events() for _ in range(50)]
     for r in range(50):
-        ev[2 * r].record(stream)
+        ev[r][0].record(stream)
         if rotation is not None:
             rotation.replay()
         else:
-            for i in range(len(layers)):
+            for i in range(NL):
                 one_step(i)
-        ev[2 * r + 1].record(stream)
+        ev[r][1].record(stream)
     torch.cuda.synchronize()
     for r in range(50):
-        per_step_us.append(ev[2 * r].elapsed_time(ev[2 * r + 1]) * 1e3 / len(layers))
+        per_step_us.append(ev[r][0].elapsed_time(ev[r][1]) * 1e3 / NL)
     p10, p50, p90 = (float(np.percentile(per_step_us, x)) for x in (10, 50, 90))
 
-    # ---- the decode-time append alone (kvq_append_decode), rotating layers
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        appends[i % len(layers)].run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    append_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # ---- each call of the step on its own, in rotation graphs
+    replays = max(10, args.steps // NL)
+    st0 = steps[0]
+    rn, rd, kf = w.ratio_num, w.ratio_den, w.k_fixed
 
-    # ---- the sparse attention call alone (split kernel + combine), HIP events
-    # on the stream it is launched on, rotating over the same layers
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n_attn = args.steps
-    for i in range(len(layers)):
-        st = steps[i]
-        st.attend(q, None if dense else st.sel_pages, None if dense else st.sel_count)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(n_attn):
-        st = steps[i % len(layers)]
-        st.attend(q, None if dense else st.sel_pages, None if dense else st.sel_count)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    attn_us = ev0.elapsed_time(ev1) * 1e3 / n_attn
+    def step_attention(li):  # the attention call as run_with_append runs it
+        st = steps[li]
+        if dense:
+            st.attend(q, None, None)
+        elif st.fused_select:
+            st.select_attend(q)
+        else:
+            kvq.kvq_topk_pages(st.scores, st.seqs, w.num_kv_heads, rn, rd, kf, st.sel_pages, st.sel_count)
+            st.attend(q, st.sel_pages, st.sel_count)
 
-    counts = steps[0].sel_count.cpu().numpy() if not dense else np.tile(w.pages_per_seq()[:, None], (1, w.num_kv_heads))
+    def given_attention(li):  # attention over the step's selection, no selection in the kernel
+        st = steps[li]
+        st.attend(q, None if dense else st.sel_pages, None if dense else st.sel_count)
+
+    def append_scores(li):
+        st, app = steps[li], appends[li]
+        kvq.kvq_append_decode_scores(st.cache, st.seqs, app.start, app.off, app.max_new, app.k_new, app.v_new, q,
+                                     st.scores)
+
+    attn_step_us = per_call_us(rotation_graph(step_attention), replays)
+    attn_given_us = per_call_us(rotation_graph(given_attention), replays)
+    append_us = per_call_us(rotation_graph(lambda li: appends[li].run()), replays)
+    scores_us = None if dense else per_call_us(rotation_graph(append_scores), replays)
+    # leave every layer as the step leaves it
+    if rotation is not None:
+        rotation.replay()
+    torch.cuda.synchronize()
+
+    counts = st0.sel_count.cpu().numpy() if not dense else np.tile(w.pages_per_seq()[:, None], (1, w.num_kv_heads))
     meta_b, kv_b = algorithmic_bytes(w, counts)
     step_bytes = (0 if dense else meta_b) + kv_b
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    attn_gbs = kv_b / (attn_us * 1e-6) / 1e9
+    attn_gbs = kv_b / (attn_step_us * 1e-6) / 1e9
 
     # the attainable streaming read on this GPU: a plain read kernel over 2 GiB
     big = torch.empty(2 << 30, dtype=torch.uint8, device=dev).fill_(1)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     kvq.kvq_read_probe(big, sink)
     torch.cuda.synchronize()
+    e0, e1 = events()
     e0.record(stream)
     for _ in range(5):
         kvq.kvq_read_probe(big, sink)
@@ -268,19 +379,41 @@ def main() -> int:
     read_gbs = 5 * big.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del big
 
-    cpu = cpu1 = None
+    # layer 0's step once more, eagerly, for the parity statistics
+    one_step(0)
+    torch.cuda.synchronize()
+    gpu = {"out": st0.out.cpu().numpy(), "sel": st0.sel_pages.cpu().numpy(), "cnt": st0.sel_count.cpu().numpy(),
+           "scores": st0.scores.cpu().numpy().astype(np.float64), "k_pages": base.k_pages.cpu().numpy(),
+           "meta": base.page_meta.cpu().numpy()}
+
+    cpu = cpu1 = parity = None
+    oracle_build_s = None
+    threads = host_threads()
     if not args.no_cpu:
+        import oracle
+        print("[bench] building the oracle's cache ...", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        built = oracle.build_cache(w)
+        oracle_build_s = time.perf_counter() - t0
         print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
-        t_cpu, threads, reps, built = cpu_baseline(w, args.cpu_seconds)
+        t_cpu, reps, res = cpu_baseline(w, args.cpu_seconds, threads, built)
         cpu = {"value": round(step_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-               "sample": f"full decode step (scores, top-K, attention) of this workload, median of {reps} runs, "
-                         f"{t_cpu * 1e3:.1f} ms each",
+               "sample": f"full decode step (scores, top-K, attention) of this workload on {threads} threads "
+                         f"({cpu_model()}), median of {reps} runs, {t_cpu * 1e3:.1f} ms each",
                "us_per_step": round(t_cpu * 1e6, 1)}
-        t1, _, reps1, _ = cpu_baseline(w, args.cpu_seconds / 2, threads=1, built=built)
+        t1, reps1, _ = cpu_baseline(w, args.cpu_seconds / 2, 1, built)
         cpu1 = {"value": round(step_bytes / t1 / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                 "sample": f"the same step on one thread, median of {reps1} runs", "us_per_step": round(t1 * 1e6, 1)}
+        if not dense:
+            parity = parity_stats(w, built, res, gpu)
+        else:
+            want = oracle.attention(built[0], built[1], lens, w.query())
+            parity = {"out_max_abs_err": float(np.abs(gpu["out"].astype(np.float64) - want).max()), "tolerance": 2e-3}
 
     ratio = f"{w.ratio_num}/{w.ratio_den}" if not w.k_fixed else f"k={w.k_fixed}"
+    kernel = ("kvq_sparse_decode_attn over every page (split kernel + combine)" if dense else
+              "kvq_select_decode_attn as the step runs it (top-K inside the split kernel + combine)"
+              if st0.fused_select else "kvq_topk_pages + kvq_sparse_decode_attn as the step runs them")
     rec = {
         "metric": "achieved HBM GB/s (% of peak) + us/decode-step, 32K ctx INT8 sparse",
         "value": round(gbs, 2),
@@ -299,21 +432,28 @@ def main() -> int:
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "context": int(lens.max()), "page": 16,
                    "storage": workloads.FORMAT_NAMES[w.fmt], "selection": ratio,
-                   "selected_pages_per_head": int(counts.max()), "layers_rotated": len(layers),
+                   "selected_pages_per_head": int(counts.max()), "layers_rotated": NL,
                    "launch": "eager" if graphs is None else "hip_graph",
-                   "pages_per_split": steps[0].pps},
+                   "pages_per_split": st0.pps, "select_in_attention_kernel": bool(st0.fused_select)},
         "bytes_per_step": {"metadata": meta_b if not dense else 0, "selected_kv": kv_b},
-        "roofline": {"bound": "hbm", "kernel": "kvq_sparse_decode_attn (split kernel + combine kernel)",
+        "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if args.config == 4 and not args.pages_per_split else None,
-                     "algorithmic_bytes": kv_b, "us_per_launch": round(attn_us, 2)},
+                     "algorithmic_bytes": kv_b, "us_per_launch": round(attn_step_us, 2)},
         "us_per_step_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
+        "attention_given_selection_us": round(attn_given_us, 2),
+        "attention_given_selection_gbs": round(kv_b / (attn_given_us * 1e-6) / 1e9, 1),
+        "append_scores_us": None if scores_us is None else round(scores_us, 2),
+        "append_scores_gbs": None if scores_us is None else round(meta_b / (scores_us * 1e-6) / 1e9, 1),
         "append_decode_us": round(append_us, 2),
+        "cache_build_us": round(cache_build_us, 1),
+        "oracle_cache_build_s": None if oracle_build_s is None else round(oracle_build_s, 3),
         "read_probe_2gib_gbs": round(read_gbs, 1),
         "attention_vs_read_probe": round(attn_gbs / read_gbs, 4),
         "cpu_baseline": cpu,
         "cpu_baseline_1thread": cpu1,
+        "parity": parity,
     }
     print(json.dumps(rec), flush=True)
     return 0

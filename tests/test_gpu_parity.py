@@ -184,9 +184,7 @@ def test_topk_on_identical_scores_is_exact(kind, n):
     kvq, _ = kvq_mod()
     bt = built((kind, n), workload(kind, n))
     w = bt.w
-    if w.is_dense():
-        pytest.skip("selection bypassed for ratio 1")
-    st = bt.step()
+    st = bt.step()   # ratio 1 (the dense configs): K = P, every page in order
     sc32 = oracle.page_scores(bt.ocache, bt.table, bt.lens, bt.q).astype(np.float32)
     st.scores.copy_(torch.from_numpy(sc32))
     kvq.kvq_topk_pages(st.scores, bt.seqs, w.num_kv_heads, w.ratio_num, w.ratio_den, w.k_fixed,
@@ -284,9 +282,7 @@ def test_select_attention_equals_topk_then_attention(kind, n):
     selection kvq_topk_pages writes and, bit for bit, the output of
     kvq_sparse_decode_attn over it, at the default split and at others."""
     kvq, _ = kvq_mod()
-    bt = built((kind, n), workload(kind, n))
-    if bt.w.is_dense():
-        pytest.skip("selection bypassed for ratio 1")
+    bt = built((kind, n), workload(kind, n))   # ratio 1 runs the selecting path with K = P
     for pps in ([0, 1, 3, 16, 64] if kind == "small" else [0, 16]):
         sep = bt.step(pages_per_split=pps, fused_select=False)
         kvq.kvq_page_scores(bt.cache, bt.seqs, bt.q_dev, sep.scores)
