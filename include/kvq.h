@@ -250,6 +250,29 @@ kvq_status kvq_select_decode_attn(const kvq_cache *cache, const kvq_seqs *seqs,
                                   float sm_scale, int32_t pages_per_split,
                                   float *out, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * kvq_select_decode_attn_noalloc -- kvq_select_decode_attn without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The per-split partials go to a scratch array the library
+ * holds in device memory, KVQ_NOALLOC_SCRATCH_BYTES per GPU it runs on, kept
+ * until the process ends; its address is looked up on the first call on each
+ * device (that device current).  The call allocates nothing and otherwise
+ * behaves, and computes bit for bit, as kvq_select_decode_attn with the same
+ * arguments.  Sizes whose kvq_attn_workspace_bytes(...) exceeds
+ * KVQ_NOALLOC_SCRATCH_BYTES return KVQ_ERR_WORKSPACE before anything is
+ * enqueued; a failed lookup returns KVQ_ERR_HIP.  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialized by the caller.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvq_status kvq_select_decode_attn_noalloc(const kvq_cache *cache, const kvq_seqs *seqs,
+                                          const uint16_t *q, int32_t num_q_heads, const float *scores,
+                                          int32_t ratio_num, int32_t ratio_den, int32_t k_fixed, int32_t k_cap,
+                                          int32_t *sel_pages, int32_t *sel_count,
+                                          float sm_scale, int32_t pages_per_split,
+                                          float *out, void *stream);
+
 /* Workspace bytes kvq_sparse_decode_attn needs for these sizes; k_cap 0
  * means every page (sel_pages NULL).  Returns 0 for invalid sizes. */
 size_t kvq_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,

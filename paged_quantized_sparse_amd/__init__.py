@@ -9,8 +9,8 @@ entry points raises.
 Entry points keep the C names:
   kvq_append_quant, kvq_append_decode, kvq_append_decode_scores, kvq_build_page_meta,
   kvq_page_scores, kvq_topk_pages,
-  kvq_sparse_decode_attn, kvq_select_decode_attn, kvq_attn_workspace_bytes, kvq_default_pages_per_split,
-  kvq_num_selected (as num_selected)
+  kvq_sparse_decode_attn, kvq_select_decode_attn, kvq_select_decode_attn_noalloc, kvq_attn_workspace_bytes,
+  kvq_default_pages_per_split, kvq_num_selected (as num_selected)
 """
 from __future__ import annotations
 
@@ -69,8 +69,10 @@ def lib() -> ctypes.CDLL:
         L.kvq_sparse_decode_attn.argtypes = [C, S, P, I, P, P, I, ctypes.c_float, I, P, P, ctypes.c_size_t, P]
         L.kvq_select_decode_attn.argtypes = [C, S, P, I, P, I, I, I, I, P, P, ctypes.c_float, I, P, P,
                                              ctypes.c_size_t, P]
+        L.kvq_select_decode_attn_noalloc.argtypes = [C, S, P, I, P, I, I, I, I, P, P, ctypes.c_float, I, P, P]
         for f in ("kvq_append_quant", "kvq_append_decode", "kvq_append_decode_scores", "kvq_build_page_meta",
-                  "kvq_page_scores", "kvq_topk_pages", "kvq_sparse_decode_attn", "kvq_select_decode_attn"):
+                  "kvq_page_scores", "kvq_topk_pages", "kvq_sparse_decode_attn", "kvq_select_decode_attn",
+                  "kvq_select_decode_attn_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.kvq_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
         L.kvq_read_probe.restype = ctypes.c_int
@@ -253,6 +255,21 @@ def kvq_select_decode_attn(cache: PagedCache, seqs: Seqs, q, scores, ratio_num: 
         int(ratio_num), int(ratio_den), int(k_fixed), int(k_cap), _ptr(sel_pages), _ptr(sel_count),
         float(sm_scale), int(pages_per_split), _ptr(out), _ptr(workspace),
         int(workspace.numel() * workspace.element_size()), _stream(stream)))
+
+
+def kvq_select_decode_attn_noalloc(cache: PagedCache, seqs: Seqs, q, scores, ratio_num: int, ratio_den: int,
+                                   k_fixed: int, k_cap: int, out, sm_scale: float, pages_per_split: int = 0,
+                                   stream=None, *, sel_pages=None, sel_count=None) -> None:
+    """kvq_select_decode_attn with the library's own scratch in place of a
+    workspace (no allocation; calls on one GPU must not overlap)."""
+    qb = _half_bits(q)
+    _check("kvq_select_decode_attn_noalloc", lib().kvq_select_decode_attn_noalloc(
+        ctypes.byref(cache.struct()), ctypes.byref(seqs.struct()), _ptr(qb), int(qb.shape[1]), _ptr(scores),
+        int(ratio_num), int(ratio_den), int(k_fixed), int(k_cap), _ptr(sel_pages), _ptr(sel_count),
+        float(sm_scale), int(pages_per_split), _ptr(out), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # KVQ_NOALLOC_SCRATCH_BYTES
 
 
 def kvq_read_probe(buf, sink, stream=None) -> None:

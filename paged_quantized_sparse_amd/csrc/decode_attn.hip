@@ -29,6 +29,8 @@
 // The SEL instances select the block's pages themselves (select_body.h) from
 // the row's scores instead of reading a selection: every block of the row
 // repeats the row's top-K and keeps the pages of its split's ranks.
+#include <mutex>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "select_body.h"
@@ -766,7 +768,36 @@ hipError_t run_d(const AttnArgs& a, int B, int D, int G, hipStream_t st) {
   return D == 64 ? run_g<FMT, 64>(a, B, G, st) : run_g<FMT, 128>(a, B, G, st);
 }
 
+// Scratch for callers that cannot allocate (kvq_select_decode_attn_noalloc):
+// the per-split partials live in this file-scope device array instead of a
+// caller's workspace.  Its name is a host-side stand-in, never a device
+// address: the address comes from hipGetSymbolAddress, once per device, with
+// that device current, and only that address reaches a kernel.
+__device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
 }  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] {
+    void* p = nullptr;
+    slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    slot.ptr = slot.err == hipSuccess ? p : nullptr;
+  });
+  *ptr = slot.ptr;
+  return slot.err;
+}
 
 hipError_t launch_decode_attn(const kvq_cache& c, const kvq_seqs& s, const uint16_t* q, int num_q_heads,
                               const int32_t* sel_pages, const int32_t* sel_count, const InKernelSelect* ks,

@@ -44,11 +44,13 @@ int32_t splits_for(int32_t max_pages, int32_t k_cap, int32_t pps) {
   return (cap + pps - 1) / pps;
 }
 
-// Validation and launch of kvq_select_decode_attn.
+// Validation and launch shared by kvq_select_decode_attn and its variant
+// without a workspace argument (ws NULL there: the library's scratch).
 kvq_status select_decode_attn(const kvq_cache* cache, const kvq_seqs* seqs, const uint16_t* q, int32_t num_q_heads,
                               const float* scores, int32_t ratio_num, int32_t ratio_den, int32_t k_fixed,
                               int32_t k_cap, int32_t* sel_pages, int32_t* sel_count, float sm_scale,
-                              int32_t pages_per_split, float* out, void* ws, size_t ws_bytes, void* stream) {
+                              int32_t pages_per_split, float* out, void* ws, size_t ws_bytes, bool scratch,
+                              void* stream) {
   kvq_status st = check_cache(cache, false);
   if (st != KVQ_OK) return st;
   if ((st = check_seqs(seqs)) != KVQ_OK) return st;
@@ -66,7 +68,13 @@ kvq_status select_decode_attn(const kvq_cache* cache, const kvq_seqs* seqs, cons
   const int32_t max_splits = splits_for(seqs->max_pages, k_cap, pps);
   const size_t need = kvq_attn_workspace_bytes(seqs->batch, num_q_heads, cache->head_dim, seqs->max_pages, k_cap,
                                                pps);
-  if (!ws || ws_bytes < need || !aligned16(ws)) return KVQ_ERR_WORKSPACE;
+  if (scratch) {
+    if (need == 0 || need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+    const hipError_t e = kvq::noalloc_scratch(&ws);
+    if (e != hipSuccess || !ws) return KVQ_ERR_HIP;
+  } else if (!ws || ws_bytes < need || !aligned16(ws)) {
+    return KVQ_ERR_WORKSPACE;
+  }
   const kvq::InKernelSelect ks{scores, ratio_num, ratio_den, k_fixed, sel_pages, sel_count};
   const hipError_t e = kvq::launch_decode_attn(*cache, *seqs, q, num_q_heads, nullptr, nullptr, &ks, k_cap, sm_scale,
                                                pps, max_splits, out, ws, (hipStream_t)stream);
@@ -213,7 +221,16 @@ kvq_status kvq_select_decode_attn(const kvq_cache* cache, const kvq_seqs* seqs, 
                                   float sm_scale, int32_t pages_per_split, float* out, void* ws, size_t ws_bytes,
                                   void* stream) {
   return select_decode_attn(cache, seqs, q, num_q_heads, scores, ratio_num, ratio_den, k_fixed, k_cap, sel_pages,
-                            sel_count, sm_scale, pages_per_split, out, ws, ws_bytes, stream);
+                            sel_count, sm_scale, pages_per_split, out, ws, ws_bytes, false, stream);
+}
+
+kvq_status kvq_select_decode_attn_noalloc(const kvq_cache* cache, const kvq_seqs* seqs, const uint16_t* q,
+                                          int32_t num_q_heads, const float* scores, int32_t ratio_num,
+                                          int32_t ratio_den, int32_t k_fixed, int32_t k_cap, int32_t* sel_pages,
+                                          int32_t* sel_count, float sm_scale, int32_t pages_per_split, float* out,
+                                          void* stream) {
+  return select_decode_attn(cache, seqs, q, num_q_heads, scores, ratio_num, ratio_den, k_fixed, k_cap, sel_pages,
+                            sel_count, sm_scale, pages_per_split, out, nullptr, 0, true, stream);
 }
 
 kvq_status kvq_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

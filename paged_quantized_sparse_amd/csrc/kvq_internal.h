@@ -69,6 +69,10 @@ struct InKernelSelect {
   int32_t* cnt_out;
 };
 
+// The device address of the library's scratch array on the current device
+// (looked up on the first call per device; KVQ_NOALLOC_SCRATCH_BYTES long).
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_decode_attn(const kvq_cache& c, const kvq_seqs& s, const uint16_t* q, int num_q_heads,
                               const int32_t* sel_pages, const int32_t* sel_count, const InKernelSelect* ks,
                               int k_cap, float sm_scale,

@@ -191,3 +191,21 @@ def test_num_selected_rule_matches_oracle(lib):
     assert lib.kvq_num_selected(2048, 3, 10, 0) == 615
     assert lib.kvq_num_selected(1024, 3, 10, 0) == 308
     assert lib.kvq_num_selected(-5, 3, 10, 0) == 0
+
+
+def test_noalloc_attention_rejects_sizes_beyond_its_scratch(lib):
+    """kvq_select_decode_attn_noalloc checks its arguments like the workspace
+    call and refuses sizes whose partials exceed KVQ_NOALLOC_SCRATCH_BYTES
+    before any device work; the limit in the header is the binding's."""
+    import paged_quantized_sparse_amd as kvq
+    assert f"#define KVQ_NOALLOC_SCRATCH_BYTES ({kvq.NOALLOC_SCRATCH_BYTES >> 20}u << 20)" in open(HEADER).read()
+
+    def call(c, s, hq=4, k_cap=3, pps=8, q=FAKE):
+        return lib.kvq_select_decode_attn_noalloc(ctypes.byref(c), ctypes.byref(s), q, hq, FAKE, 3, 10, 0, k_cap,
+                                                  None, None, 0.1, pps, FAKE, None)
+    c, s = _structs()
+    assert call(c, s, k_cap=2) == INVALID
+    assert call(c, s, hq=12) == UNSUPPORTED
+    assert call(c, s, q=FAKE + 2) == INVALID
+    _, big = _structs(B=60000, maxp=2048)                     # 60000 x 4 heads x 2048 pages: far beyond 16 MiB
+    assert call(c, big, k_cap=2048, pps=1) == WORKSPACE
