@@ -159,6 +159,8 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=8, help="independent layer caches rotated per step")
     ap.add_argument("--eager", action="store_true", help="launch every kernel from the host (no HIP graph)")
     ap.add_argument("--pages-per-split", type=int, default=0)
+    ap.add_argument("--one-launch", action="store_true",
+                    help="run the step as one persistent launch (kvq_decode_step) instead of three")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle legs (CPU baseline and parity)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -238,7 +240,8 @@ def main() -> int:
     dense = w.is_dense()
     appends = [runtime.DecodeAppend(c, seqs, lens, src, device=dev) for c in layers]
     steps = [runtime.DecodeStep(c, seqs, w.num_q_heads, w.ratio_num, w.ratio_den, w.k_fixed, dense=dense,
-                                pages_per_split=args.pages_per_split, device=dev) for c in layers]
+                                pages_per_split=args.pages_per_split, device=dev,
+                                fused_step=args.one_launch) for c in layers]
     NL = len(layers)
     torch.cuda.synchronize()
 
@@ -434,7 +437,8 @@ def main() -> int:
                    "storage": workloads.FORMAT_NAMES[w.fmt], "selection": ratio,
                    "selected_pages_per_head": int(counts.max()), "layers_rotated": NL,
                    "launch": "eager" if graphs is None else "hip_graph",
-                   "pages_per_split": st0.pps, "select_in_attention_kernel": bool(st0.fused_select)},
+                   "pages_per_split": st0.pps, "select_in_attention_kernel": bool(st0.fused_select),
+                   "one_launch_step": bool(st0.fused_step)},
         "bytes_per_step": {"metadata": meta_b if not dense else 0, "selected_kv": kv_b},
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

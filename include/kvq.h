@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 3
+#define KVQ_ABI_VERSION 4
 #define KVQ_PAGE_SIZE 16
 #define KVQ_SELECT_MAX_PAGES 2048 /* longest row (pages) kvq_select_decode_attn takes */
 
@@ -249,6 +249,48 @@ kvq_status kvq_select_decode_attn(const kvq_cache *cache, const kvq_seqs *seqs,
                                   int32_t *sel_pages, int32_t *sel_count,
                                   float sm_scale, int32_t pages_per_split,
                                   float *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * kvq_decode_step -- the whole decode step in ONE persistent launch
+ * ("TinyServe", section 3.1: score, top-K, sparse load and reduce fused into
+ * one kernel; section 5.2: kernel-launch overhead): kvq_append_decode_scores
+ * (append the newest rows, refresh the touched pages' metadata, score every
+ * page) followed by kvq_select_decode_attn (top-K inside the attention,
+ * split-K attention, split combine), with the same arguments.  Rows, their
+ * scores and splits are items of one work list that the blocks of a grid of
+ * resident blocks take in turn; a row's splits wait for its scores.
+ *   - Codes, scale/zero, metadata, the selection (sel_pages/sel_count, if
+ *     given), the scores of every page below ceil(L_b/16) and `out` equal,
+ *     bit for bit, the two calls above with the same pages_per_split.
+ *     scores past a row's pages are left unspecified (not -inf).
+ *   - ws: at least kvq_step_workspace_bytes(...) bytes.  Its first
+ *     kvq_step_counter_bytes(batch, num_kv_heads) bytes are counters that
+ *     must be zero before the first call on this workspace (zero the buffer
+ *     when allocating it); every call leaves them zero.  Calls sharing a
+ *     workspace must not overlap in time.  The second 32-bit word of ws is
+ *     set to 1, and stays 1, if a wait inside a launch ever ran out of its
+ *     bound (the launch then still ends, with wrong results, and may leave
+ *     counters set); a correct launch never does that.
+ *   - Limits (else KVQ_ERR_UNSUPPORTED): max_pages <= KVQ_SELECT_MAX_PAGES,
+ *     batch <= KVQ_STEP_MAX_SEQS, pages_per_split <= KVQ_STEP_MAX_SPLIT_PAGES.
+ * max_new may be 0 (no rows appended; k_new / v_new may then be NULL).
+ */
+#define KVQ_STEP_MAX_SEQS 512
+#define KVQ_STEP_MAX_SPLIT_PAGES 512
+kvq_status kvq_decode_step(const kvq_cache *cache, const kvq_seqs *seqs,
+                           const int32_t *start_pos, const int32_t *new_off, int32_t max_new,
+                           const uint16_t *k_new, const uint16_t *v_new,
+                           const uint16_t *q, int32_t num_q_heads, float *scores,
+                           int32_t ratio_num, int32_t ratio_den, int32_t k_fixed, int32_t k_cap,
+                           int32_t *sel_pages, int32_t *sel_count,
+                           float sm_scale, int32_t pages_per_split,
+                           float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of kvq_decode_step (counters, then the per-split partials),
+ * and the leading counter bytes that must start zero; 0 for invalid sizes. */
+size_t kvq_step_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_pages, int32_t k_cap, int32_t pages_per_split);
+size_t kvq_step_counter_bytes(int32_t batch, int32_t num_kv_heads);
 
 /*
  * kvq_select_decode_attn_noalloc -- kvq_select_decode_attn without a

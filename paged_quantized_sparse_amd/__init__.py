@@ -10,7 +10,8 @@ Entry points keep the C names:
   kvq_append_quant, kvq_append_decode, kvq_append_decode_scores, kvq_build_page_meta,
   kvq_page_scores, kvq_topk_pages,
   kvq_sparse_decode_attn, kvq_select_decode_attn, kvq_select_decode_attn_noalloc, kvq_attn_workspace_bytes,
-  kvq_default_pages_per_split, kvq_num_selected (as num_selected)
+  kvq_default_pages_per_split, kvq_decode_step, kvq_step_workspace_bytes, kvq_step_counter_bytes,
+  kvq_num_selected (as num_selected)
 """
 from __future__ import annotations
 
@@ -70,9 +71,15 @@ def lib() -> ctypes.CDLL:
         L.kvq_select_decode_attn.argtypes = [C, S, P, I, P, I, I, I, I, P, P, ctypes.c_float, I, P, P,
                                              ctypes.c_size_t, P]
         L.kvq_select_decode_attn_noalloc.argtypes = [C, S, P, I, P, I, I, I, I, P, P, ctypes.c_float, I, P, P]
+        L.kvq_decode_step.argtypes = [C, S, P, P, I, P, P, P, I, P, I, I, I, I, P, P, ctypes.c_float, I, P, P,
+                                      ctypes.c_size_t, P]
+        L.kvq_step_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        L.kvq_step_workspace_bytes.restype = ctypes.c_size_t
+        L.kvq_step_counter_bytes.argtypes = [I, I]
+        L.kvq_step_counter_bytes.restype = ctypes.c_size_t
         for f in ("kvq_append_quant", "kvq_append_decode", "kvq_append_decode_scores", "kvq_build_page_meta",
                   "kvq_page_scores", "kvq_topk_pages", "kvq_sparse_decode_attn", "kvq_select_decode_attn",
-                  "kvq_select_decode_attn_noalloc"):
+                  "kvq_select_decode_attn_noalloc", "kvq_decode_step"):
             getattr(L, f).restype = ctypes.c_int
         L.kvq_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
         L.kvq_read_probe.restype = ctypes.c_int
@@ -270,6 +277,34 @@ def kvq_select_decode_attn_noalloc(cache: PagedCache, seqs: Seqs, q, scores, rat
 
 
 NOALLOC_SCRATCH_BYTES = 16 << 20  # KVQ_NOALLOC_SCRATCH_BYTES
+STEP_MAX_SEQS = 512               # KVQ_STEP_MAX_SEQS
+STEP_MAX_SPLIT_PAGES = 512        # KVQ_STEP_MAX_SPLIT_PAGES
+
+
+def kvq_step_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_pages: int,
+                             k_cap: int, pages_per_split: int) -> int:
+    return int(lib().kvq_step_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_pages, k_cap,
+                                              pages_per_split))
+
+
+def kvq_step_counter_bytes(batch: int, num_kv_heads: int) -> int:
+    return int(lib().kvq_step_counter_bytes(batch, num_kv_heads))
+
+
+def kvq_decode_step(cache: PagedCache, seqs: Seqs, start_pos, new_off, max_new: int, k_new, v_new, q, scores,
+                    ratio_num: int, ratio_den: int, k_fixed: int, k_cap: int, out, workspace, sm_scale: float,
+                    pages_per_split: int = 0, stream=None, *, sel_pages=None, sel_count=None) -> None:
+    """The whole decode step in one launch (append, metadata, scores, top-K,
+    attention, combine).  The workspace's leading counter bytes must be zero
+    before its first use (allocate it zeroed)."""
+    k = _half_bits(k_new) if k_new is not None else None
+    v = _half_bits(v_new) if v_new is not None else None
+    qb = _half_bits(q)
+    _check("kvq_decode_step", lib().kvq_decode_step(
+        ctypes.byref(cache.struct()), ctypes.byref(seqs.struct()), _ptr(start_pos), _ptr(new_off), int(max_new),
+        _ptr(k), _ptr(v), _ptr(qb), int(qb.shape[1]), _ptr(scores), int(ratio_num), int(ratio_den), int(k_fixed),
+        int(k_cap), _ptr(sel_pages), _ptr(sel_count), float(sm_scale), int(pages_per_split), _ptr(out),
+        _ptr(workspace), int(workspace.numel() * workspace.element_size()), _stream(stream)))
 
 
 def kvq_read_probe(buf, sink, stream=None) -> None:

@@ -40,7 +40,28 @@ struct AppendView {
   int max_pages;
 };
 
-template <int FMT, int D>
+// One token row's codes, NB bytes per lane (lane l holding bytes NB l ..
+// NB l + NB-1 of the row), written as whole dwords with device-scope stores:
+// lanes gather their neighbours' bytes over DPP and every (4/NB)-th lane stores.
+template <int NB>
+__device__ __forceinline__ void store_row_dev(uint8_t* row, uint32_t bits) {
+  const int lane = lane_id();
+  if constexpr (NB == 4) {
+    store_u32<true>((uint32_t*)(row + 4 * lane), bits);
+  } else if constexpr (NB == 2) {
+    const uint32_t nb = dpp_u32<kDppXor1>(bits);
+    if ((lane & 1) == 0) store_u32<true>((uint32_t*)(row + 2 * lane), (bits & 0xFFFFu) | (nb << 16));
+  } else {
+    const uint32_t b1 = dpp_u32<0x39>(bits), b2 = dpp_u32<kDppXor2>(bits), b3 = dpp_u32<0x93>(bits);  // lanes +1, +2, +3 of the quad
+    if ((lane & 3) == 0)
+      store_u32<true>((uint32_t*)(row + lane), (bits & 0xFFu) | ((b1 & 0xFFu) << 8) | ((b2 & 0xFFu) << 16) | (b3 << 24));
+  }
+}
+
+// WT: every store is a device-scope (written-through) store, for readers in
+// other blocks of the same launch (the fused decode step); otherwise the
+// stores are ordinary.
+template <int FMT, int D, bool WT = false>
 __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b, int h,
                                                      float (*sm_meta)[2][D]) {
   constexpr int E = D / 64;
@@ -78,7 +99,15 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
     gv[1] = vlo;
     if (threadIdx.x < 4 && threadIdx.x * kPage < n) {  // every page holding a row of the group
       const int phys = bt[(start + threadIdx.x * kPage) / kPage];
-      *(float4*)(a.params + ((size_t)phys * a.H + h) * 4) = make_float4(gk[0], gk[1], gv[0], gv[1]);
+      float* gp = a.params + ((size_t)phys * a.H + h) * 4;
+      if constexpr (WT) {
+        store_f<true>(gp, gk[0]);
+        store_f<true>(gp + 1, gk[1]);
+        store_f<true>(gp + 2, gv[0]);
+        store_f<true>(gp + 3, gv[1]);
+      } else {
+        *(float4*)gp = make_float4(gk[0], gk[1], gv[0], gv[1]);
+      }
     }
   }
 
@@ -126,12 +155,24 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
       const size_t dst = (tile + t % kPage) * D + lane * E;
       float kdec[E];
       if constexpr (FMT == kFp16) {
+        uint32_t kw = 0, vw = 0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const uint16_t kb = a.k_new[src + e];
-          ((uint16_t*)a.k_pages)[dst + e] = kb;
-          ((uint16_t*)a.v_pages)[dst + e] = a.v_new[src + e];
+          const uint16_t vb = a.v_new[src + e];
+          if constexpr (WT) {
+            kw |= (uint32_t)kb << (16 * e);
+            vw |= (uint32_t)vb << (16 * e);
+          } else {
+            ((uint16_t*)a.k_pages)[dst + e] = kb;
+            ((uint16_t*)a.v_pages)[dst + e] = vb;
+          }
           kdec[e] = half_bits_to_float(kb);
+        }
+        if constexpr (WT) {
+          const size_t row = (tile + t % kPage) * D * 2;
+          store_row_dev<2 * E>((uint8_t*)a.k_pages + row, kw);
+          store_row_dev<2 * E>((uint8_t*)a.v_pages + row, vw);
         }
       } else {
         float kx[E], vx[E];
@@ -154,14 +195,36 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
           quant_params(vlo, vhi, vs, vinv);
           kz = klo;
           vz = vlo;
-          if (lane == 0) *(float4*)(a.params + (tile + t % kPage) * 4) = make_float4(ks, kz, vs, vz);
+          if (lane == 0) {
+            float* tp = a.params + (tile + t % kPage) * 4;
+            if constexpr (WT) {
+              store_f<true>(tp, ks);
+              store_f<true>(tp + 1, kz);
+              store_f<true>(tp + 2, vs);
+              store_f<true>(tp + 3, vz);
+            } else {
+              *(float4*)tp = make_float4(ks, kz, vs, vz);
+            }
+          }
         }
+        uint32_t kw = 0, vw = 0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const uint32_t kc = quant_code(kx[e], kz, kinv);
-          ((uint8_t*)a.k_pages)[dst + e] = (uint8_t)kc;
-          ((uint8_t*)a.v_pages)[dst + e] = (uint8_t)quant_code(vx[e], vz, vinv);
+          const uint32_t vc = quant_code(vx[e], vz, vinv);
+          if constexpr (WT) {
+            kw |= kc << (8 * e);
+            vw |= vc << (8 * e);
+          } else {
+            ((uint8_t*)a.k_pages)[dst + e] = (uint8_t)kc;
+            ((uint8_t*)a.v_pages)[dst + e] = (uint8_t)vc;
+          }
           kdec[e] = __builtin_fmaf((float)kc, ks, kz);
+        }
+        if constexpr (WT) {
+          const size_t row = (tile + t % kPage) * D;
+          store_row_dev<E>((uint8_t*)a.k_pages + row, kw);
+          store_row_dev<E>((uint8_t*)a.v_pages + row, vw);
         }
       }
 #pragma unroll
@@ -175,8 +238,8 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
     float* m = a.meta + ((size_t)phys * a.H + h) * 2 * D + lane * E;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      m[e] = lo[e];
-      m[D + e] = hi[e];
+      store_f<WT>(m + e, lo[e]);
+      store_f<WT>(m + D + e, hi[e]);
       if (sm_meta) {
         sm_meta[pi][0][lane * E + e] = lo[e];
         sm_meta[pi][1][lane * E + e] = hi[e];

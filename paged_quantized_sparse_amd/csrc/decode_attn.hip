@@ -1,720 +1,29 @@
 // decode_attn.hip -- single-token attention over the selected pages of a
 // paged, optionally INT8, KV cache ("TinyServe", lpnh.cn, section 3.1 phases
-// 3-4: load only the selected pages' KV, then reduce; attention itself is
-// softmax(q k^T / sqrt(d)) v, intelliparadigm.com KV-cache page, section 2.1).
-//
-// Split-K: block (split s, KV head g, sequence b) takes selected pages
-// [s*PPS, (s+1)*PPS) of row (b, g); its waves take every NW-th page.  A wave
-// holds a whole (page, KV head) tile in flight as 16-byte loads: for a token
-// row of RB = d * elem bytes, LPT = RB/16 lanes share a token, so one load
-// instruction covers TPL = 64/LPT tokens, and NL = 16/TPL loads cover the page.
-// The next tile's loads are issued before the current tile is consumed.
-//
-// Keys: q.k runs on v_dot2_f32_f16 with the fp16 query.  An INT8 code c
-// becomes the fp16 value 1024 + c with one byte permute (0x64 is the high byte
-// of 1024.0h), so for per-token or per-group (scale s, zero z)
-//   q.k = s * sum q_i (1024 + c_i) + (z - 1024 s) * sum q_i.
-// Values: acc += (p s) * c per channel (byte converts + fma), plus p z once per
-// token.  The G query heads of a KV group share every loaded tile.
-//
-// Online softmax per lane (exp2 domain): each lane keeps the running max m of
-// the tokens it saw and rescales only when a logit exceeds m by more than
-// kLazy (weights stay below 2^kLazy), so the inner loop needs no cross-lane
-// max.  Lanes, then waves, merge with log-sum-exp weights; each block writes a
-// partial (m, l, acc) per query head and split, and combine_kernel merges a
-// row's splits.  (Merging in the last-arriving split block instead needs a
-// device-scope release per block, which on gfx950 writes back the XCD's L2
-// each time and costs far more than a second launch.)
-//
-// The SEL instances select the block's pages themselves (select_body.h) from
-// the row's scores instead of reading a selection: every block of the row
-// repeats the row's top-K and keeps the pages of its split's ranks.
+// 3-4; intelliparadigm.com KV-cache page, section 2.1): the split kernel and
+// the split combine as launches of their own, and the launchers.  The
+// arithmetic is attn_body.h.
 #include <mutex>
 
-#include "kvq_device.h"
-#include "kvq_internal.h"
-#include "select_body.h"
+#include "attn_body.h"
 
 namespace kvq {
 namespace {
 
-constexpr int kAttnWaves = 4;
-// tiles in flight ahead of the one being consumed (1, 3, 4 and 6 measured the
-// same or slower at 32K context)
-constexpr int kPrefetch = 2;
-
-constexpr float kLazy = 8.0f;
-
-struct AttnArgs {
-  const void* k_pages;
-  const void* v_pages;
-  const float* params;
-  const int32_t* block_table;
-  const int32_t* seq_lens;
-  const uint16_t* q;
-  const int32_t* sel_pages;  // NULL: all pages (or selection in the kernel, below)
-  const int32_t* sel_count;
-  const float* scores;       // [B][H][max_pages]: select in the kernel (the SEL instances)
-  int32_t* sel_out;          // optional copies of that selection, as kvq_topk_pages writes it
-  int32_t* cnt_out;
-  int rnum, rden, k_fixed;   // its selection rule
-  float* part_acc;    // [B][Hq][max_splits][D]
-  float* part_ml;     // [B][Hq][max_splits][2]
-  float* out;         // [B][Hq][D]
-  int H;
-  int Hq;
-  int max_pages;
-  int k_cap;
-  int pps;  // pages per split
-  int max_splits;
-  float scale_log2;  // sm_scale * log2(e)
-};
-
-template <int FMT, int D>
-struct Tile {
-  static constexpr int ELEM = FMT == kFp16 ? 2 : 1;
-  static constexpr int RB = D * ELEM;
-  static constexpr int LPT = RB / 16;     // lanes per token
-  static constexpr int TPL = 64 / LPT;    // tokens per load
-  static constexpr int NL = kPage / TPL;  // loads per page
-  static constexpr int CH = 16 / ELEM;    // channels per lane
-};
-
-__device__ __forceinline__ float byte_to_float(uint32_t w, int i) { return (float)((w >> (8 * i)) & 0xFFu); }
-
-__device__ __forceinline__ half2v as_half2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
-
-typedef _Float16 half4v __attribute__((ext_vector_type(4)));
-typedef _Float16 half8v __attribute__((ext_vector_type(8)));
-typedef short short4v __attribute__((ext_vector_type(4)));  // four bf16 bit patterns
-typedef float float4v __attribute__((ext_vector_type(4)));
-
-// Matrix-core form for a GQA group (G >= 2 query heads per KV head) over an
-// INT8 cache, where q.k and p.v are small GEMMs per 16-token page.  A
-// 16x16xKB MFMA takes A[i][k] from lane i + 16(k/KL), element k%KL, B[k][j]
-// from lane j + 16(k/KL), element k%KL (KL = KB/4 elements per lane), and
-// leaves D[i][j] in lane j + 16(i/4), register i%4.
-//   Logits: C[t][h] = sum_k K[t][k] Q[h][k] on v_mfma_f32_16x16x32_f16 (the
-//   full-rate shape on gfx950) with the page's 16 tokens as rows and the
-//   heads (padded to 16) as columns.  Lane l holds token l%16's channels
-//   (D/4)(l/16) .. +D/4 (one contiguous run of its row), MFMA m taking the
-//   eight at offset 8m; the query is laid out to match, once.  C
-//   then sits in lane h + 16g as tokens 4g .. 4g+3 of head h, which is
-//   exactly the A layout of the second product.
-//   Output: O[h][c] += sum_t W[h][t] V[t][c] on v_mfma_f32_16x16x16_bf16
-//   (same layouts), W = p * v_scale split by truncation into three bf16
-//   parts (three MFMAs, ~2^-21 relative; bf16 keeps fp32's exponent range,
-//   so small weights keep their relative precision, which an fp16 split
-//   loses below 2^-14), V as exact bf16 codes.  B needs four tokens of one
-//   channel per lane, so each lane loads a run of its row (token
-//   4g + l%4) and a 4x4 byte transpose inside each lane quad (two DPP
-//   exchanges and byte permutes) hands lane (g, q, r) channel
-//   (D/4)q + 4j + r of tokens 4g .. 4g+3 for MFMA j.
-// The key codes become fp16 1024 + c by byte permute, as in the vector path.
-template <int FMT, int D, int G>
-struct MfmaPath {
-  static constexpr bool on = FMT != kFp16 && G >= 2 && G <= 16;
-  // value MFMAs per page (16 output channels each); also the query's groups
-  // of 4 channels per lane (two per logits MFMA)
-  static constexpr int NM = D / 16;
-  static constexpr int NU = D / 64;  // 16-byte loads per lane per tile, K and V each
-};
-
-// Lane-quad byte transpose: lane r of each quad holds word W_r with bytes
-// (token r, channels c..c+3); afterwards it holds (tokens 0..3, channel c+r).
-__device__ __forceinline__ uint32_t quad_transpose_bytes(uint32_t x, uint32_t sel1, uint32_t sel2) {
-  const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppXor1, 0xF, 0xF, false);
-  const uint32_t t = __builtin_amdgcn_perm(x, p1, sel1);
-  const uint32_t p2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)t, kDppXor2, 0xF, 0xF, false);
-  return __builtin_amdgcn_perm(t, p2, sel2);
-}
-
-// Pairs of fp32 values' upper halves (their bf16 truncations) packed as the
-// four elements of an MFMA operand.
-__device__ __forceinline__ short4v pack_bf16(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
-  const uint32_t lo = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-  const uint32_t hi = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
-  return __builtin_bit_cast(short4v, ((uint64_t)hi << 32) | lo);
-}
-
-// Four INT8 codes (bytes of w) as exact bf16 values.
-__device__ __forceinline__ short4v codes_bf16(uint32_t w) {
-  return pack_bf16(__builtin_bit_cast(uint32_t, (float)(w & 0xFFu)),
-                   __builtin_bit_cast(uint32_t, (float)((w >> 8) & 0xFFu)),
-                   __builtin_bit_cast(uint32_t, (float)((w >> 16) & 0xFFu)),
-                   __builtin_bit_cast(uint32_t, (float)(w >> 24)));
-}
-
-// Four INT8 codes (bytes of w) as fp16 1024 + c.
-__device__ __forceinline__ half4v codes_1024(uint32_t w) {
-  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, w, 0x04010400u);
-  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, w, 0x04030402u);
-  return __builtin_bit_cast(half4v, ((uint64_t)hi << 32) | lo);
-}
-
-// grid (B * Hq), 256 threads: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
-// with M = max_s m_s.  Thread (part, c) takes channel c of splits part,
-// part + PARTS, ...: it loads eight splits' (m, l, acc) at once (indices past
-// the row's splits re-read its last split and are masked), together with the
-// split count, and merges them online; the PARTS partial merges then meet in
-// LDS.  So the block waits on one round of loads, not two.
+// grid (B * Hq), 256 threads: the splits of query head bh = b * Hq + h.
 template <int D, int G>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
-  constexpr int PARTS = 256 / D;
-  constexpr int U = 8;  // splits in flight per thread
-  __shared__ float sm_m[PARTS][D], sm_num[PARTS][D], sm_den[PARTS][D];
-  const int bh = blockIdx.x;
-  const int b = bh / a.Hq, h = bh % a.Hq;
-  const int row = b * a.H + h / G;
-  const int tid = threadIdx.x;
-  const int c = tid % D, part = tid / D;
-  const float* ml = a.part_ml + (size_t)bh * a.max_splits * 2;
-  const float* pa = a.part_acc + (size_t)bh * a.max_splits * D;
-  const int32_t* cnt_p = a.sel_pages ? a.sel_count + row : a.seq_lens + b;  // a select, not a branch
-  const int cnt_v = vload_i32(cnt_p, 0);
-  float2 mlv[U];
-  float av[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {  // speculative: the first U splits of this part
-    const int sp = min(part + u * PARTS, a.max_splits - 1);
-    mlv[u] = *(const float2*)(ml + 2 * sp);
-    av[u] = pa[(size_t)sp * D + c];
-  }
-  __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the count is waited for
-  // with every page selected cnt_p points at the length, so K = P either way
-  // (using the value on both paths keeps the load where it is issued)
-  const int cnt = __builtin_amdgcn_readfirstlane(cnt_v);
-  const int Pc = (cnt + kPage - 1) / kPage;
-  const int K = a.sel_pages ? cnt : (a.scores ? num_selected(Pc, a.rnum, a.rden, a.k_fixed) : Pc);
-  const int ns = (K + a.pps - 1) / a.pps;
-  float M = -INFINITY, num = 0.0f, den = 0.0f;
-  for (int s0 = 0;; s0 += U * PARTS) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // a slot past the row's splits holds whatever the workspace held (any
-      // bits, NaN included): its values are replaced, not multiplied by 0
-      const bool live = s0 + part + u * PARTS < ns;
-      const float ms = live ? mlv[u].x : -INFINITY;
-      const float as = live ? av[u] : 0.0f;
-      const float ls = live ? mlv[u].y : 0.0f;
-      const float Mn = fmaxf(M, ms);
-      const float fo = M == -INFINITY ? 0.0f : exp2f(M - Mn);
-      const float fs = ms == -INFINITY ? 0.0f : exp2f(ms - Mn);
-      num = __builtin_fmaf(fs, as, num * fo);
-      den = __builtin_fmaf(fs, ls, den * fo);
-      M = Mn;
-    }
-    if (s0 + U * PARTS >= ns) break;  // block-uniform
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int sp = min(s0 + U * PARTS + part + u * PARTS, a.max_splits - 1);
-      mlv[u] = *(const float2*)(ml + 2 * sp);
-      av[u] = pa[(size_t)sp * D + c];
-    }
-  }
-  sm_m[part][c] = M;
-  sm_num[part][c] = num;
-  sm_den[part][c] = den;
-  __syncthreads();
-  if (part == 0) {
-    float Mt = -INFINITY;
-#pragma unroll
-    for (int p = 0; p < PARTS; ++p) Mt = fmaxf(Mt, sm_m[p][c]);
-    float n = 0.0f, dd = 0.0f;
-#pragma unroll
-    for (int p = 0; p < PARTS; ++p) {
-      const float f = sm_m[p][c] == -INFINITY ? 0.0f : exp2f(sm_m[p][c] - Mt);
-      n = __builtin_fmaf(f, sm_num[p][c], n);
-      dd = __builtin_fmaf(f, sm_den[p][c], dd);
-    }
-    a.out[(size_t)bh * D + c] = dd > 0.0f ? n / dd : 0.0f;
-  }
+  combine_one<D, G, false>(a, blockIdx.x);
 }
 
-// SEL: the block selects its pages itself (select_body.h) from a.scores.
+// grid (KV head, sequence, split): blocks are dispatched split-major, so a
+// ragged batch's full first splits go out first and its shorter last splits
+// last, and all splits of a head share the XCD of block id mod 8.  The SEL
+// instance's dynamic LDS holds the block's pages (pps entries).
 template <int FMT, int D, int G, int NW, bool SEL>
 __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
-  static_assert(NW == 4, "the split merge and the combine assume 4 waves");
-  using T = Tile<FMT, D>;
-  constexpr int LPT = T::LPT, TPL = T::TPL, NL = T::NL, CH = T::CH;
-  using MP = MfmaPath<FMT, D, G>;
-  constexpr bool MF = MP::on;
-  static_assert(!MF || NL == MP::NU, "an INT8 tile row is NL 16-byte loads per lane in both forms");
-  // grid (KV head, sequence, split): blocks are dispatched split-major, so a
-  // ragged batch's full first splits go out first and its shorter last
-  // splits last, and all splits of a head share the XCD of block id mod 8
-  const int g = blockIdx.x, b = blockIdx.y, s = blockIdx.z;
-  const int row = b * a.H + g;
-  const int first = s * a.pps;
-  const int w = wave_id();
-  const int lane = lane_id();
-  // Prologue, three levels of dependent loads.  Level 1, issued together and
-  // unconditionally: this lane's selection slot (first + w + lane * NW, the
-  // wave's first 64 pages), the sequence length, the selected count and the
-  // query.  Level 2: the block-table entry of the slot's page.  Level 3: the
-  // first tiles.  Indices are clamped into their arrays, so a slot past the
-  // row's count reads some entry of the row and is never used; with no
-  // selection (all pages) the slot load reads the block table and is replaced
-  // by the slot index itself.
-  // With in-kernel selection, level 1 carries the row's first scores
-  // instead of the selection slot, and the slot comes from LDS after the
-  // selection.
-  const bool sparse = !SEL && a.sel_pages != nullptr;
-  const int idx0 = first + w + lane * NW;
-  SelPrefetch<NW * 64> pre;
-  if constexpr (SEL) pre.load(a.scores + (size_t)row * a.max_pages, a.max_pages);
-  const int slot_raw = SEL      ? 0
-                       : sparse ? vload_i32(a.sel_pages, (size_t)row * a.k_cap + min(idx0, a.k_cap - 1))
-                                : vload_i32(a.block_table, (size_t)b * a.max_pages + min(idx0, a.max_pages - 1));
-  const int len_v = vload_i32(a.seq_lens, b);
-  const int32_t* cnt_p = sparse ? a.sel_count + row : a.seq_lens + b;  // a select, not a branch
-  const int cnt_v = vload_i32(cnt_p, 0);
-  const int tg = lane / LPT;  // token group
-  const int cc = lane % LPT;  // channel chunk
-  const int ch0 = cc * CH;
-
-  // ---- query chunk in registers: fp16 pairs for v_dot2, and its fp32 sum
-  half2v qh[G][CH / 2];
-  float qsum[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const uint32_t* qp = (const uint32_t*)(a.q + ((size_t)b * a.Hq + g * G + hh) * D + ch0);
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < CH / 8; ++i) {
-      const uint4 raw = *(const uint4*)(qp + 4 * i);
-      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        qh[hh][4 * i + j] = as_half2(wd[j]);
-        acc += half_bits_to_float(wd[j] & 0xFFFFu) + half_bits_to_float(wd[j] >> 16);
-      }
-    }
-    qsum[hh] = acc;
-  }
-  // matrix-core form: lane l holds head l%16's channels (D/4)(l/16) .. +D/4
-  // (zeros for the padding heads), as groups of 4 (two per MFMA, which
-  // takes the eight at offset 8m)
-  half4v qB[MP::NM];
-  float qs_mf = 0.0f;
-  if constexpr (MF) {
-    const int hn = lane & 15, gq = lane >> 4;
-    const uint32_t* qp = (const uint32_t*)(a.q + ((size_t)b * a.Hq + g * G + min(hn, G - 1)) * D + (D / 4) * gq);
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      const uint4 raw = *(const uint4*)(qp + 4 * i);
-      const uint32_t wd[4] = {hn < G ? raw.x : 0u, hn < G ? raw.y : 0u, hn < G ? raw.z : 0u, hn < G ? raw.w : 0u};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc += half_bits_to_float(wd[j] & 0xFFFFu) + half_bits_to_float(wd[j] >> 16);
-      qB[2 * i] = __builtin_bit_cast(half4v, ((uint64_t)wd[1] << 32) | wd[0]);
-      qB[2 * i + 1] = __builtin_bit_cast(half4v, ((uint64_t)wd[3] << 32) | wd[2]);
-    }
-    qs_mf = acc;
-  }
-  __builtin_amdgcn_sched_barrier(0);  // keep every level-1 load ahead of the first use below
-  if constexpr (MF) {  // the head's whole sum over its four lanes
-    qs_mf += __shfl_xor(qs_mf, 16, kWave);
-    qs_mf += __shfl_xor(qs_mf, 32, kWave);
-  }
-
-  const int L = __builtin_amdgcn_readfirstlane(len_v);
-  const int P = (L + kPage - 1) / kPage;
-  // with every page selected cnt_p points at the length, so K = P either way
-  // (using the value on both paths keeps the load where it is issued)
-  const int cnt = __builtin_amdgcn_readfirstlane(cnt_v);
-  const int Pc = (cnt + kPage - 1) / kPage;
-  const int K = SEL ? num_selected(Pc, a.rnum, a.rden, a.k_fixed) : (sparse ? cnt : Pc);
-  if constexpr (SEL) {  // the selection's count and padding, once per row
-    if (s == 0 && a.sel_out) {
-      if (threadIdx.x == 0) a.cnt_out[row] = K;
-      for (int i = K + threadIdx.x; i < a.k_cap; i += NW * 64) a.sel_out[(size_t)row * a.k_cap + i] = -1;
-    }
-  }
-  if (first >= K) return;
-  const int n = min(a.pps, K - first);
-  int* list = nullptr;  // SEL: this block's pages, ascending
-  int jlog0;
-  if constexpr (SEL) {
-    __shared__ int sm_hist[2 * kSelBins];
-    __shared__ int sm_wtot[2 * NW];
-    __shared__ uint32_t sm_wrange[2 * NW];
-    extern __shared__ int sm_dyn[];  // the block's pages [pps]
-    list = sm_dyn;
-    if (K < P) {
-      select_chunk<NW>(pre, P, K, first, n, SelShared{sm_hist, sm_wtot, sm_wrange}, list);
-    } else {
-      for (int i = threadIdx.x; i < n; i += NW * 64) list[i] = first + i;
-      __syncthreads();
-    }
-    if (a.sel_out)
-      for (int i = threadIdx.x; i < n; i += NW * 64) a.sel_out[(size_t)row * a.k_cap + first + i] = list[i];
-    jlog0 = list[min(w + lane * NW, n - 1)];
-  } else {
-    jlog0 = sparse ? min(max(slot_raw, 0), a.max_pages - 1) : min(idx0, a.max_pages - 1);
-  }
-  // level 2 for the wave's first 64 pages
-  const int phys0 = vload_i32(a.block_table, (size_t)b * a.max_pages + jlog0);
-
-  // ---- per-lane online softmax state
-  const int nw = n > w ? (n - w + NW - 1) / NW : 0;
-  float m[G], l[G], acc[G][CH], zacc[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.0f;
-    zacc[hh] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) acc[hh][i] = 0.0f;
-  }
-  // matrix-core form: (m, l, z) of head lane%16 over this lane's tokens (m the
-  // same in the head's four lanes), and O[h][c] accumulators in MFMA layout
-  float mf_m = -INFINITY, mf_l = 0.0f, mf_z = 0.0f;
-  float4v mf_acc[MP::NM];
-#pragma unroll
-  for (int j = 0; j < MP::NM; ++j) mf_acc[j] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-
-  const size_t tile_elems = (size_t)kPage * D;
-  // scale/zero registers per tile: the matrix-core form wants tokens
-  // 4(l/16) .. +3 per lane (per token) or the tile's one group pair
-  constexpr int NP = MF ? (FMT == kInt8Token ? 4 : 1) : NL;
-  struct PageRegs {
-    uint4 kr[NL], vr[NL];
-    float4 pr[NP];
-    int nvalid;
-  };
-  // issue every load of one (page, KV head) tile
-  auto load_page = [&](int jl, int ph, PageRegs& r) {
-    r.nvalid = min(kPage, L - jl * kPage);
-    const size_t tile = ((size_t)ph * a.H + g) * tile_elems;
-    if constexpr (MF) {
-      // K: token l%16, run (D/4)(l/16); V: token 4(l/16) + l%4, run (D/4)((l/4)%4)
-      const char* kp = (const char*)a.k_pages + tile + (lane & 15) * D + (D / 4) * (lane >> 4);
-      const char* vp = (const char*)a.v_pages + tile + (4 * (lane >> 4) + (lane & 3)) * D + (D / 4) * ((lane >> 2) & 3);
-      // Each of these loads covers half of every 128-byte row of the tile (the
-      // other half comes with the next), so they are ordinary loads, which keep
-      // the line in L2 for its second half (64 ragged sequences, 8 KV heads in
-      // groups of 4: 166 against 178 us per attention call with the streaming
-      // hint).
-#pragma unroll
-      for (int u = 0; u < NL; ++u) {
-        r.kr[u] = *(const uint4*)(kp + 16 * u);
-        r.vr[u] = *(const uint4*)(vp + 16 * u);
-      }
-      if constexpr (FMT == kInt8Token) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          r.pr[i] = load_stream_f4(a.params + (((size_t)ph * a.H + g) * kPage + 4 * (lane >> 4) + i) * 4);
-      } else {
-        r.pr[0] = load_stream_f4(a.params + ((size_t)ph * a.H + g) * 4);
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const size_t off = (tile + (size_t)(i * TPL + tg) * D + ch0) * T::ELEM;
-      r.kr[i] = load_stream_u4((const char*)a.k_pages + off);
-      r.vr[i] = load_stream_u4((const char*)a.v_pages + off);
-      if constexpr (FMT == kInt8Token)
-        r.pr[i] = load_stream_f4(a.params + ((size_t)ph * a.H + g) * (kPage * 4) + (i * TPL + tg) * 4);
-    }
-    if constexpr (FMT == kInt8Group) {
-      const float4 gp = load_stream_f4(a.params + ((size_t)ph * a.H + g) * 4);
-#pragma unroll
-      for (int i = 0; i < NL; ++i) r.pr[i] = gp;
-    }
-  };
-  // fold one loaded tile into the online softmax of the G heads
-  auto consume_page = [&](PageRegs& r) {
-    const int nvalid = r.nvalid;
-    if constexpr (MF) {
-      const int hn = lane & 15, g4 = lane >> 4;
-      // logits of tokens 4 g4 + i for head hn: C = K Q^T on the matrix cores
-      float4v cq = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int u = 0; u < NL; ++u) {
-        const uint32_t kw[4] = {r.kr[u].x, r.kr[u].y, r.kr[u].z, r.kr[u].w};
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const half4v k0 = codes_1024(kw[2 * h2]), k1 = codes_1024(kw[2 * h2 + 1]);
-          const half4v q0 = qB[4 * u + 2 * h2], q1 = qB[4 * u + 2 * h2 + 1];
-          const half8v ka = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
-          const half8v qa = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-          cq = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qa, cq, 0, 0, 0);
-        }
-      }
-      float lg[4];
-      bool valid[4];
-      float lm = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        valid[i] = 4 * g4 + i < nvalid && hn < G;
-        const float4 pp = r.pr[NP == 4 ? i : 0];
-        const float zz = __builtin_fmaf(-1024.0f, pp.x, pp.y);
-        const float part = __builtin_fmaf(pp.x, cq[i], zz * qs_mf);
-        lg[i] = valid[i] ? part * a.scale_log2 : -INFINITY;
-        lm = fmaxf(lm, lg[i]);
-      }
-      if (__ballot(lm > mf_m + kLazy)) {  // wave-uniform; rare once the max settles
-        // every lane of a head decides on the head's max over its four lanes
-        float hm = fmaxf(lm, __shfl_xor(lm, 16, kWave));
-        hm = fmaxf(hm, __shfl_xor(hm, 32, kWave));
-        const float mn = hm > mf_m + kLazy ? hm : mf_m;
-        const float alpha = mn == mf_m ? 1.0f : __builtin_amdgcn_exp2f(mf_m - mn);
-        mf_l *= alpha;
-        mf_z *= alpha;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {  // O row 4 g4 + i takes that head's factor (from its lane)
-          const float ai = __shfl(alpha, 4 * g4 + i, kWave);
-#pragma unroll
-          for (int j = 0; j < MP::NM; ++j) mf_acc[j][i] *= ai;
-        }
-        mf_m = mn;
-      }
-      uint32_t wb0[4], wb1[4], wb2[4];  // w = b0 + b1 + b2, each a bf16 (low 16 bits zero)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = lg[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lg[i] - mf_m);
-        mf_l += p;
-        // padding slots may hold any bits: their scale/zero never reach the sums
-        const float4 pp = r.pr[NP == 4 ? i : 0];
-        const float w = valid[i] ? p * pp.z : 0.0f;
-        mf_z = valid[i] ? __builtin_fmaf(p, pp.w, mf_z) : mf_z;
-        wb0[i] = __builtin_bit_cast(uint32_t, w) & 0xFFFF0000u;
-        const float r1 = w - __builtin_bit_cast(float, wb0[i]);  // exact
-        wb1[i] = __builtin_bit_cast(uint32_t, r1) & 0xFFFF0000u;
-        const float r2 = r1 - __builtin_bit_cast(float, wb1[i]);  // exact
-        wb2[i] = __builtin_bit_cast(uint32_t, r2) & 0xFFFF0000u;
-      }
-      const short4v wa0 = pack_bf16(wb0[0], wb0[1], wb0[2], wb0[3]);
-      const short4v wa1 = pack_bf16(wb1[0], wb1[1], wb1[2], wb1[3]);
-      const short4v wa2 = pack_bf16(wb2[0], wb2[1], wb2[2], wb2[3]);
-      // values: quad byte transpose to four tokens of one channel, exact bf16
-      // codes, then O += (W_0 + W_1 + W_2) V
-      const uint32_t sel1 = (lane & 1) ? 0x07030501u : 0x02060004u;
-      const uint32_t sel2 = (lane & 2) ? 0x07060302u : 0x01000504u;
-#pragma unroll
-      for (int u = 0; u < NL; ++u) {
-        const uint32_t vw[4] = {r.vr[u].x, r.vr[u].y, r.vr[u].z, r.vr[u].w};
-#pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4) {
-          const short4v vb = codes_bf16(quad_transpose_bytes(vw[d4], sel1, sel2));
-          const int j = 4 * u + d4;
-          mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa2, vb, mf_acc[j], 0, 0, 0);
-          mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa1, vb, mf_acc[j], 0, 0, 0);
-          mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa0, vb, mf_acc[j], 0, 0, 0);
-        }
-      }
-      return;
-    }
-    // Padding slots of a partial last page hold no data (possibly NaN bits):
-    // zero their values and scale/zero with per-lane selects.  A branch that
-    // rewrote the loaded registers would make the compiler wait for every
-    // outstanding load, including the prefetched tiles, at its join.
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const bool pad = i * TPL + tg >= nvalid;
-      r.vr[i].x = pad ? 0u : r.vr[i].x;
-      r.vr[i].y = pad ? 0u : r.vr[i].y;
-      r.vr[i].z = pad ? 0u : r.vr[i].z;
-      r.vr[i].w = pad ? 0u : r.vr[i].w;
-      if constexpr (FMT != kFp16) {
-        r.pr[i].z = pad ? 0.0f : r.pr[i].z;
-        r.pr[i].w = pad ? 0.0f : r.pr[i].w;
-      }
-    }
-    // logits
-    float lg[G][NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const uint32_t kw[4] = {r.kr[i].x, r.kr[i].y, r.kr[i].z, r.kr[i].w};
-      float dot[G];
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) dot[hh] = 0.0f;
-#pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4) {
-        if constexpr (FMT == kFp16) {
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) dot[hh] = __builtin_amdgcn_fdot2(as_half2(kw[d4]), qh[hh][d4], dot[hh], false);
-        } else {
-          const half2v lo = as_half2(__builtin_amdgcn_perm(0x64646464u, kw[d4], 0x04010400u));
-          const half2v hi = as_half2(__builtin_amdgcn_perm(0x64646464u, kw[d4], 0x04030402u));
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) {
-            dot[hh] = __builtin_amdgcn_fdot2(lo, qh[hh][2 * d4], dot[hh], false);
-            dot[hh] = __builtin_amdgcn_fdot2(hi, qh[hh][2 * d4 + 1], dot[hh], false);
-          }
-        }
-      }
-      const bool valid = i * TPL + tg < nvalid;
-      float zz = 0.0f;
-      if constexpr (FMT != kFp16) zz = __builtin_fmaf(-1024.0f, r.pr[i].x, r.pr[i].y);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float part = dot[hh];
-        if constexpr (FMT != kFp16) part = __builtin_fmaf(r.pr[i].x, dot[hh], zz * qsum[hh]);
-        part = sum_contig<LPT>(part);
-        lg[hh][i] = valid ? part * a.scale_log2 : -INFINITY;
-      }
-    }
-    // values, decoded once for the G heads
-    float vf[NL][CH];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const uint32_t vw[4] = {r.vr[i].x, r.vr[i].y, r.vr[i].z, r.vr[i].w};
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        if constexpr (FMT == kFp16)
-          vf[i][c] = half_bits_to_float((vw[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
-        else
-          vf[i][c] = byte_to_float(vw[c / 4], c % 4);
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float mx = lg[hh][0];
-#pragma unroll
-      for (int i = 1; i < NL; ++i) mx = fmaxf(mx, lg[hh][i]);
-      const bool need = mx > m[hh] + kLazy;
-      if (__ballot(need)) {  // wave-uniform branch; rare once the max settles
-        const float mn = need ? mx : m[hh];
-        const float alpha = mn == m[hh] ? 1.0f : __builtin_amdgcn_exp2f(m[hh] - mn);
-        l[hh] *= alpha;
-        zacc[hh] *= alpha;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) acc[hh][c] *= alpha;
-        m[hh] = mn;
-      }
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const float p = lg[hh][i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lg[hh][i] - m[hh]);
-        l[hh] += p;
-        if constexpr (FMT == kFp16) {
-#pragma unroll
-          for (int c = 0; c < CH; ++c) acc[hh][c] = __builtin_fmaf(p, vf[i][c], acc[hh][c]);
-        } else {
-          const float ps = p * r.pr[i].z;
-          zacc[hh] = __builtin_fmaf(p, r.pr[i].w, zacc[hh]);
-#pragma unroll
-          for (int c = 0; c < CH; ++c) acc[hh][c] = __builtin_fmaf(ps, vf[i][c], acc[hh][c]);
-        }
-      }
-    }
-  };
-
-  for (int k0 = 0; k0 < nw; k0 += 64) {
-    // page ids with one lane each (the first 64 come from the prologue)
-    int jlog_v = jlog0, phys_v = phys0;
-    if (k0 > 0) {  // wave-uniform; only when a split gives a wave more than 64 pages
-      // clamped to the split's last page: a slot past the wave's count reads
-      // some page of this split (its load is never used), and the in-kernel
-      // list holds only the split's n entries
-      const int idx = min(first + w + (k0 + lane) * NW, first + n - 1);
-      if constexpr (SEL)
-        jlog_v = list[idx - first];
-      else
-        jlog_v = sparse ? min(max(a.sel_pages[(size_t)row * a.k_cap + idx], 0), a.max_pages - 1) : idx;
-      phys_v = a.block_table[(size_t)b * a.max_pages + jlog_v];
-    }
-    const int cnt = min(64, nw - k0);
-    // Software pipeline over a ring of R = PF + 1 register tiles: the loads of
-    // tiles k+1 .. k+PF are in flight while tile k is consumed.
-    // Every load is unconditional (an index past the chunk re-reads its last
-    // tile, which is cached), so the compiler's wait counts stay exact; a
-    // conditional load would make it wait for all outstanding loads.  The main
-    // loop is unrolled by R so ring indices are compile-time constants.
-    constexpr int PF = kPrefetch;
-    constexpr int R = PF + 1;
-    PageRegs ring[R];
-    auto load_idx = [&](int k, PageRegs& r) {
-      const int kk = min(k, cnt - 1);
-      load_page(__builtin_amdgcn_readlane(jlog_v, kk), __builtin_amdgcn_readlane(phys_v, kk), r);
-    };
-#pragma unroll
-    for (int u = 0; u < PF; ++u) load_idx(u, ring[u]);
-    int k = 0;
-    for (; k + R <= cnt; k += R) {
-#pragma unroll
-      for (int u = 0; u < R; ++u) {
-        load_idx(k + u + PF, ring[(u + PF) % R]);
-        consume_page(ring[u]);
-      }
-    }
-    // fewer than R tiles remain; they are already in ring[0 ..] (no loads here)
-#pragma unroll
-    for (int u = 0; u < PF; ++u)
-      if (k + u < cnt) consume_page(ring[u]);
-  }
-
-  // ---- merge the token groups of the wave (lanes congruent mod LPT)
-#pragma unroll
-  for (int hh = 0; hh < (MF ? 0 : G); ++hh) {
-    const float M = max_strided<LPT>(m[hh]);
-    const float f = m[hh] == -INFINITY ? 0.0f : exp2f(m[hh] - M);
-    l[hh] = sum_strided<LPT>(l[hh] * f);
-#pragma unroll
-    for (int c = 0; c < CH; ++c) acc[hh][c] = sum_strided<LPT>((acc[hh][c] + zacc[hh]) * f);
-    m[hh] = M;
-  }
-
-  // ---- merge the block's waves through LDS and write the split's partials
-  __shared__ float sm_ml[NW][G][2];
-  __shared__ float sm_acc[NW][G][D];
-  if constexpr (MF) {
-    // (l, z) of head lane%16 summed over its four lanes; O[h][c] = acc + z,
-    // lane l register i holding head 4(l/16) + i at channel
-    // (D/4)(n/4) + 4j + n%4 of MFMA j, n = l%16
-    mf_l += __shfl_xor(mf_l, 16, kWave);
-    mf_l += __shfl_xor(mf_l, 32, kWave);
-    mf_z += __shfl_xor(mf_z, 16, kWave);
-    mf_z += __shfl_xor(mf_z, 32, kWave);
-    const int hn = lane & 15, g4 = lane >> 4;
-    if (lane < G) {
-      sm_ml[w][lane][0] = mf_m;
-      sm_ml[w][lane][1] = mf_l;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = 4 * g4 + i;
-      const float zh = __shfl(mf_z, hh, kWave);
-      if (hh < G) {
-#pragma unroll
-        for (int j = 0; j < MP::NM; ++j) sm_acc[w][hh][(D / 4) * (hn >> 2) + 4 * j + (hn & 3)] = mf_acc[j][i] + zh;
-      }
-    }
-  } else if (tg == 0) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) sm_acc[w][hh][ch0 + c] = acc[hh][c];
-      if (lane == 0) {
-        sm_ml[w][hh][0] = m[hh];
-        sm_ml[w][hh][1] = l[hh];
-      }
-    }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < G * D; e += NW * 64) {
-    const int hh = e / D, c = e % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) M = fmaxf(M, sm_ml[v][hh][0]);
-    float sa = 0.0f, sl = 0.0f;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      const float mv = sm_ml[v][hh][0];
-      const float f = mv == -INFINITY ? 0.0f : exp2f(mv - M);  // 0 for a wave without pages
-      sa = __builtin_fmaf(f, sm_acc[v][hh][c], sa);
-      sl = __builtin_fmaf(f, sm_ml[v][hh][1], sl);
-    }
-    const size_t prow = ((size_t)b * a.Hq + g * G + hh) * a.max_splits + s;
-    a.part_acc[prow * D + c] = sa;
-    if (c == 0) {
-      a.part_ml[prow * 2 + 0] = M;
-      a.part_ml[prow * 2 + 1] = sl;
-    }
-  }
-
+  extern __shared__ int sm_dyn[];
+  attend_split<FMT, D, G, NW, SEL, false>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm_dyn);
 }
 
 // Room for dynamic LDS a launch of the SEL kernel has under the device's

@@ -233,6 +233,54 @@ kvq_status kvq_select_decode_attn_noalloc(const kvq_cache* cache, const kvq_seqs
                             sel_count, sm_scale, pages_per_split, out, nullptr, 0, true, stream);
 }
 
+size_t kvq_step_counter_bytes(int32_t batch, int32_t num_kv_heads) {
+  if (batch < 1 || num_kv_heads < 1 || (long long)batch * num_kv_heads > (1LL << 24)) return 0;
+  return kvq::step_counter_bytes(batch, batch * num_kv_heads);
+}
+
+size_t kvq_step_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_pages, int32_t k_cap, int32_t pages_per_split) {
+  const size_t ctr = kvq_step_counter_bytes(batch, num_kv_heads);
+  const size_t part = kvq_attn_workspace_bytes(batch, num_q_heads, head_dim, max_pages, k_cap, pages_per_split);
+  if (ctr == 0 || part == 0) return 0;
+  return ctr + part;
+}
+
+kvq_status kvq_decode_step(const kvq_cache* cache, const kvq_seqs* seqs, const int32_t* start_pos,
+                           const int32_t* new_off, int32_t max_new, const uint16_t* k_new, const uint16_t* v_new,
+                           const uint16_t* q, int32_t num_q_heads, float* scores, int32_t ratio_num,
+                           int32_t ratio_den, int32_t k_fixed, int32_t k_cap, int32_t* sel_pages,
+                           int32_t* sel_count, float sm_scale, int32_t pages_per_split, float* out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  kvq_status st = check_cache(cache, true);
+  if (st != KVQ_OK) return st;
+  if ((st = check_seqs(seqs)) != KVQ_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != KVQ_OK) return st;
+  if (!q || !out || !scores || !aligned16(q)) return KVQ_ERR_INVALID_ARG;
+  if (!start_pos || !new_off || max_new < 0) return KVQ_ERR_INVALID_ARG;
+  if (max_new > KVQ_DECODE_MAX_ROWS) return KVQ_ERR_UNSUPPORTED;
+  if (max_new > 0 && (!k_new || !v_new)) return KVQ_ERR_INVALID_ARG;
+  if (k_fixed < 0 || (k_fixed == 0 && (ratio_num < 1 || ratio_den < 1))) return KVQ_ERR_INVALID_ARG;
+  if ((sel_pages == nullptr) != (sel_count == nullptr)) return KVQ_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale)) return KVQ_ERR_INVALID_ARG;
+  if (pages_per_split < 0 || pages_per_split > 4096) return KVQ_ERR_INVALID_ARG;
+  if (seqs->max_pages > kvq::kSelMaxPages || seqs->batch > kvq::kStepMaxSeqs) return KVQ_ERR_UNSUPPORTED;
+  if (k_cap < kvq::num_selected(seqs->max_pages, ratio_num, ratio_den, k_fixed)) return KVQ_ERR_INVALID_ARG;
+  const int32_t pps = pages_per_split ? pages_per_split
+                                      : kvq_default_pages_per_split(seqs->batch, cache->num_kv_heads,
+                                                                    seqs->max_pages, k_cap);
+  if (pps > kvq::kStepMaxSplitPages) return KVQ_ERR_UNSUPPORTED;
+  const int32_t max_splits = splits_for(seqs->max_pages, k_cap, pps);
+  const size_t need = kvq_step_workspace_bytes(seqs->batch, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                               seqs->max_pages, k_cap, pps);
+  if (!ws || need == 0 || ws_bytes < need || !aligned16(ws)) return KVQ_ERR_WORKSPACE;
+  const hipError_t e = kvq::launch_decode_step(*cache, *seqs, start_pos, new_off, k_new, v_new, q, num_q_heads,
+                                               scores, ratio_num, ratio_den, k_fixed, k_cap, sel_pages, sel_count,
+                                               sm_scale, pps, max_splits, out, ws, (hipStream_t)stream);
+  if (e == hipErrorInvalidConfiguration) return KVQ_ERR_UNSUPPORTED;
+  return from_hip(e);
+}
+
 kvq_status kvq_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (!buf || !sink || !aligned16(buf) || bytes % 16 != 0) return KVQ_ERR_INVALID_ARG;
   return from_hip(kvq::launch_read_probe(buf, bytes, sink, (hipStream_t)stream));

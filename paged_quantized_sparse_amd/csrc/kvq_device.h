@@ -193,6 +193,44 @@ __device__ __forceinline__ float4 load_stream_f4(const float* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
+// Loads and stores of data other blocks of the same launch write or read
+// (COH = true): device-scope relaxed accesses, which on gfx950 are the sc1
+// forms -- a store written through to memory, a load served from memory --
+// so no L2 write-back or invalidate is needed for that data.  COH = false:
+// ordinary accesses.
+template <bool COH>
+__device__ __forceinline__ float load_f(const float* p) {
+  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+
+template <bool COH>
+__device__ __forceinline__ float2 load_f2(const float* p) {
+  if constexpr (COH) return make_float2(load_f<true>(p), load_f<true>(p + 1));
+  return *(const float2*)p;
+}
+
+template <bool COH>
+__device__ __forceinline__ void store_f(float* p, float v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
+template <bool COH>
+__device__ __forceinline__ void store_u32(uint32_t* p, uint32_t v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
+// Every store this thread issued has completed (reached the level its cache
+// policy writes to): the ordering point before a device-scope counter update
+// that publishes data written with store_f<true> / store_u32<true>.
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 

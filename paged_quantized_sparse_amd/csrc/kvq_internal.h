@@ -69,6 +69,18 @@ struct InKernelSelect {
   int32_t* cnt_out;
 };
 
+// The fused decode step (decode_step.hip): rows of at most kSelMaxPages
+// pages, at most kStepMaxSeqs sequences, splits of at most kStepMaxSplitPages.
+constexpr int kStepMaxSeqs = KVQ_STEP_MAX_SEQS;
+constexpr int kStepMaxSplitPages = KVQ_STEP_MAX_SPLIT_PAGES;
+// bytes of the step's counters at the start of its workspace (the partials follow)
+size_t step_counter_bytes(int batch, int rows);
+hipError_t launch_decode_step(const kvq_cache& c, const kvq_seqs& s, const int32_t* start_pos,
+                              const int32_t* new_off, const uint16_t* k_new, const uint16_t* v_new,
+                              const uint16_t* q, int num_q_heads, float* scores, int rnum, int rden, int k_fixed,
+                              int k_cap, int32_t* sel_pages, int32_t* sel_count, float sm_scale,
+                              int pages_per_split, int max_splits, float* out, void* ws, hipStream_t st);
+
 // The device address of the library's scratch array on the current device
 // (looked up on the first call per device; KVQ_NOALLOC_SCRATCH_BYTES long).
 hipError_t noalloc_scratch(void** ptr);

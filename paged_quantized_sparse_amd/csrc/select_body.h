@@ -41,13 +41,15 @@ struct SelShared {
 
 // Thread t's 8 scores (pages 8t .. 8t+7), loaded before the row length is
 // known (indices clamped into the row of max_pages scores), so these loads
-// are in flight with the kernel's other first loads.
+// are in flight with the kernel's other first loads; COH: at device scope,
+// for scores other blocks of the same launch wrote.
 template <int NT>
 struct SelPrefetch {
   float v[kSelKeys];
+  template <bool COH>
   __device__ __forceinline__ void load(const float* sc, int max_pages) {
 #pragma unroll
-    for (int u = 0; u < kSelKeys; ++u) v[u] = sc[min(kSelKeys * (int)threadIdx.x + u, max_pages - 1)];
+    for (int u = 0; u < kSelKeys; ++u) v[u] = load_f<COH>(sc + min(kSelKeys * (int)threadIdx.x + u, max_pages - 1));
   }
 };
 

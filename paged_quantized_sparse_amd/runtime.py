@@ -8,7 +8,8 @@ A decode step, as the TinyServe page (lpnh.cn, section 3.1) orders it:
   attention over the selected pages (split-K + combine).
 DecodeStep.run_with_append does it in three launches: append + metadata +
 scores (kvq_append_decode_scores), then top-K inside the attention kernel
-(kvq_select_decode_attn), then the split combine.
+(kvq_select_decode_attn), then the split combine; or, with fused_step, in one
+persistent launch (kvq_decode_step).
 """
 from __future__ import annotations
 
@@ -17,10 +18,11 @@ from typing import Callable
 import numpy as np
 import torch
 
-from . import (KVQ_INT8_GROUP64, PAGE_SIZE, SELECT_MAX_PAGES, PagedCache, Seqs, kvq_append_decode, kvq_append_decode_scores,
-               kvq_append_quant,
-               kvq_attn_workspace_bytes, kvq_build_page_meta, kvq_default_pages_per_split, kvq_page_scores,
-               kvq_select_decode_attn, kvq_sparse_decode_attn, kvq_topk_pages, num_selected)
+from . import (KVQ_INT8_GROUP64, PAGE_SIZE, SELECT_MAX_PAGES, STEP_MAX_SEQS, STEP_MAX_SPLIT_PAGES, PagedCache, Seqs,
+               kvq_append_decode, kvq_append_decode_scores, kvq_append_quant, kvq_attn_workspace_bytes,
+               kvq_build_page_meta, kvq_decode_step, kvq_default_pages_per_split, kvq_page_scores,
+               kvq_select_decode_attn, kvq_sparse_decode_attn, kvq_step_workspace_bytes, kvq_topk_pages,
+               num_selected)
 
 FUSED_SELECT_MAX_BLOCKS = 512  # one round of attention blocks on 256 CUs (2 per CU)
 
@@ -133,7 +135,7 @@ class DecodeStep:
 
     def __init__(self, cache: PagedCache, seqs: Seqs, num_q_heads: int, ratio_num: int, ratio_den: int,
                  k_fixed: int, dense: bool = False, pages_per_split: int = 0, device="cuda",
-                 fused_select: bool = True):
+                 fused_select: bool = True, fused_step: bool = False):
         self.cache, self.seqs, self.Hq = cache, seqs, num_q_heads
         self.ratio = (ratio_num, ratio_den, k_fixed)
         self.dense = dense
@@ -150,6 +152,14 @@ class DecodeStep:
         nbytes = kvq_attn_workspace_bytes(B, num_q_heads, d, maxp, self.k_cap, self.pps)
         self.workspace = torch.zeros((nbytes + 255) // 4, dtype=torch.float32, device=device)
         self.sm_scale = 1.0 / float(np.sqrt(d))
+        # the one-launch step (kvq_decode_step): its workspace starts zeroed
+        # (counters) and the step keeps it so
+        self.fused_step = (fused_step and not dense and maxp <= SELECT_MAX_PAGES and B <= STEP_MAX_SEQS
+                           and self.pps <= STEP_MAX_SPLIT_PAGES)
+        self.step_workspace = None
+        if self.fused_step:
+            sb = kvq_step_workspace_bytes(B, num_q_heads, H, d, maxp, self.k_cap, self.pps)
+            self.step_workspace = torch.zeros((sb + 255) // 4, dtype=torch.float32, device=device)
 
     def select(self, q, stream=None) -> None:
         kvq_page_scores(self.cache, self.seqs, q, self.scores, stream)
@@ -181,10 +191,17 @@ class DecodeStep:
 
     def run_with_append(self, app: "DecodeAppend", q, stream=None) -> torch.Tensor:
         """The whole decode step: append the newest rows (app) and score in
-        one kernel, then top-K and attention."""
+        one kernel, then top-K and attention (fused_step: all of it in one
+        launch, kvq_decode_step)."""
         if self.dense:
             app.run(stream)
             return self.attend(q, None, None, stream)
+        if self.fused_step:
+            rn, rd, kf = self.ratio
+            kvq_decode_step(self.cache, self.seqs, app.start, app.off, app.max_new, app.k_new, app.v_new, q,
+                            self.scores, rn, rd, kf, self.k_cap, self.out, self.step_workspace, self.sm_scale,
+                            self.pps, stream, sel_pages=self.sel_pages, sel_count=self.sel_count)
+            return self.out
         kvq_append_decode_scores(self.cache, self.seqs, app.start, app.off, app.max_new, app.k_new, app.v_new, q,
                                  self.scores, stream)
         if self.fused_select:
