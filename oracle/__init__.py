@@ -21,6 +21,8 @@ Every function follows the pages it cites in ``kvq_oracle.c``:
   attention_mass -- the share of dense attention weight on the selected
                  pages (selection quality; TinyServe page, section 1 claims
                  the value sits in a minority of the KV cache)
+  coarse_meta, mask_scores, hier_select -- coarse-then-fine selection over
+                 super-pages of consecutive pages (TinyServe page, section 6)
 """
 from __future__ import annotations
 
@@ -75,6 +77,10 @@ def lib() -> ctypes.CDLL:
         L.kvqo_decode_step.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, I, I, I,
                                        ctypes.c_double, P, P, P, P, I]
         L.kvqo_decode_step.restype = I
+        L.kvqo_coarse_meta.argtypes = [I, I, I, I, P, P, I, P, P]
+        L.kvqo_coarse_meta.restype = None
+        L.kvqo_mask_scores.argtypes = [I, I, I, I, P, P, I, P]
+        L.kvqo_mask_scores.restype = None
         L.kvqo_half_to_float.argtypes = [ctypes.c_uint16]
         L.kvqo_half_to_float.restype = ctypes.c_float
         L.kvqo_dequant.argtypes = [ctypes.c_uint8, ctypes.c_float, ctypes.c_float]
@@ -225,6 +231,62 @@ def decode_step(cache: Cache, block_table, seq_lens, q, ratio_num, ratio_den, k_
     if rc != 0:
         raise ValueError("oracle decode_step: k_cap too small")
     return scores, sel, cnt, out
+
+
+# -------------------------------------------------- hierarchical selection
+def coarse_meta(cache: Cache, block_table, seq_lens, group: int) -> np.ndarray:
+    """float32 [B * pc_max][H][2][d]: each super-page's bounding box, the
+    min of its pages' minima and max of their maxima (pc_max =
+    ceil(max_pages / group)); super-pages past a sequence stay +inf / -inf."""
+    bt = np.ascontiguousarray(block_table, np.int32)
+    sl = np.ascontiguousarray(seq_lens, np.int32)
+    B, maxp = bt.shape
+    pc_max = (maxp + group - 1) // group
+    out = np.empty((B * pc_max, cache.H, 2, cache.d), np.float32)
+    out[:, :, 0] = np.inf
+    out[:, :, 1] = -np.inf
+    lib().kvqo_coarse_meta(B, cache.H, cache.d, maxp, _p(bt), _p(sl), group, _p(cache.meta), _p(out))
+    return out
+
+
+def coarse_view(cache: Cache, block_table, seq_lens, group: int):
+    """(cache view whose page metadata are the super-pages' boxes, its block
+    table b -> b * pc_max + jc, its lengths in 16-token units of super-pages):
+    page scores and top-K on this view are the coarse screen."""
+    B, maxp = np.asarray(block_table).shape
+    pc_max = (maxp + group - 1) // group
+    view = Cache(cache.fmt, B * pc_max, cache.H, cache.d)
+    view.meta = coarse_meta(cache, block_table, seq_lens, group)
+    table = (np.arange(B, dtype=np.int32)[:, None] * pc_max + np.arange(pc_max, dtype=np.int32)[None]).astype(np.int32)
+    P = (np.asarray(seq_lens, np.int64) + PAGE - 1) // PAGE
+    lens_c = (((P + group - 1) // group) * PAGE).astype(np.int32)
+    return view, table, lens_c
+
+
+def mask_scores(scores, group: int, sel_super, sel_super_count) -> np.ndarray:
+    """A copy of the fine scores with every page outside the kept super-pages
+    set to -inf."""
+    sc = np.array(scores, dtype=np.float64, order="C")
+    B, H, maxp = sc.shape
+    sel = np.ascontiguousarray(sel_super, np.int32)
+    cnt = np.ascontiguousarray(sel_super_count, np.int32)
+    lib().kvqo_mask_scores(B, H, maxp, group, _p(sel), _p(cnt), sel.shape[2], _p(sc))
+    return sc
+
+
+def hier_select(cache: Cache, block_table, seq_lens, q, group: int, kc: int, ratio_num: int, ratio_den: int,
+                k_fixed: int, k_cap: int):
+    """The coarse-then-fine selection ([TS] section 6): coarse scores of the
+    super-pages, the top kc of them, the fine scores of their pages (-inf
+    elsewhere), then the top-K rule of topk().  Returns (coarse scores,
+    coarse selection, coarse counts, masked fine scores, selection, counts)."""
+    view, ctable, clens = coarse_view(cache, block_table, seq_lens, group)
+    csc = page_scores(view, ctable, clens, q)
+    csel, ccnt = topk(csc, clens, 0, 1, kc, kc)
+    fine = page_scores(cache, block_table, seq_lens, q)
+    masked = mask_scores(fine, group, csel, ccnt)
+    sel, cnt = topk(masked, seq_lens, ratio_num, ratio_den, k_fixed, k_cap)
+    return csc, csel, ccnt, masked, sel, cnt
 
 
 # ------------------------------------------------------------ element probes

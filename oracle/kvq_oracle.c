@@ -414,6 +414,68 @@ int kvqo_topk(int B, int H, int max_pages, const int32_t *seq_lens, const double
 }
 
 /* ------------------------------------------------------------------------- */
+/* Hierarchical selection, coarse then fine ([TS] section 6: for large       */
+/* models, screen coarsely first, then finely).  Reading: a super-page is     */
+/* `group` consecutive logical pages of a sequence; its bounding box is the   */
+/* channel-wise min of the member pages' minima and max of their maxima, so   */
+/* its score (the page score formula on that box) is at least every member    */
+/* page's score.  The top kc super-pages by that score survive, and only      */
+/* their pages keep their fine scores; every other page scores -inf before    */
+/* the usual top-K.                                                           */
+/*                                                                            */
+/* Coarse boxes: coarse[b * pc_max + jc][h] = (min row, max row) over the     */
+/* valid pages j of super-page jc (group jc <= j < group (jc+1), j < P_b).    */
+/* The layout is that of page metadata with "physical page" b * pc_max + jc,  */
+/* so page scores on it are the coarse scores.  Super-pages past the          */
+/* sequence's pages are left untouched.                                       */
+/* ------------------------------------------------------------------------- */
+void kvqo_coarse_meta(int B, int H, int d, int max_pages, const int32_t *block_table,
+                      const int32_t *seq_lens, int group, const float *meta, float *coarse)
+{
+    int pc_max = (max_pages + group - 1) / group;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *bt = block_table + (size_t)b * max_pages;
+        int P = (seq_lens[b] + PAGE - 1) / PAGE;
+        int Pc = (P + group - 1) / group;
+        for (int jc = 0; jc < Pc; ++jc)
+            for (int h = 0; h < H; ++h) {
+                float *out = coarse + (((size_t)b * pc_max + jc) * H + h) * 2 * d;
+                for (int ch = 0; ch < d; ++ch) {
+                    float lo = INFINITY, hi = -INFINITY;
+                    for (int j = jc * group; j < (jc + 1) * group && j < P; ++j) {
+                        const float *m = meta + ((size_t)bt[j] * H + h) * 2 * d;
+                        if (m[ch] < lo) lo = m[ch];
+                        if (m[d + ch] > hi) hi = m[d + ch];
+                    }
+                    out[ch] = lo;
+                    out[d + ch] = hi;
+                }
+            }
+    }
+}
+
+/* The fine scores kept after the coarse screen: scores[b][h][j] stays for     */
+/* pages j whose super-page j / group is among sel_super[b][h][0 .. count),    */
+/* and becomes -inf for every other page (in place).                          */
+void kvqo_mask_scores(int B, int H, int max_pages, int group, const int32_t *sel_super,
+                      const int32_t *sel_super_count, int kc_cap, double *scores)
+{
+    int pc_max = (max_pages + group - 1) / group;
+    char *keep = malloc((size_t)pc_max + 1);
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            memset(keep, 0, (size_t)pc_max + 1);
+            const int32_t *sel = sel_super + ((size_t)b * H + h) * kc_cap;
+            for (int i = 0; i < sel_super_count[(size_t)b * H + h]; ++i)
+                if (sel[i] >= 0 && sel[i] < pc_max) keep[sel[i]] = 1;
+            double *row = scores + ((size_t)b * H + h) * max_pages;
+            for (int j = 0; j < max_pages; ++j)
+                if (!keep[j / group]) row[j] = -INFINITY;
+        }
+    free(keep);
+}
+
+/* ------------------------------------------------------------------------- */
 /* Attention of each query head over every valid token of the selected   */
 /* pages of its KV group: softmax(q k^T * sm_scale) v ([KV] section 2.1;      */
 /* [TS] section 3.1 phases 3-4), fp64.  sel_pages NULL: all pages.            */

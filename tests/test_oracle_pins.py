@@ -784,3 +784,133 @@ def test_lazy_metadata_refresh_report():
     u, p, ch, worst = results[4]
     print(f"[lazy] {w.name}, 6 sequences, 24 steps: refresh every 4th step -> {u} of {p} page scores "
           f"underestimate (worst by {worst:.3g}), {ch} of {T * w.batch * H} selections differ from exact metadata")
+
+
+# ------------------------------------------------- hierarchical selection
+def _decoded_keys(cache, table, lens, b, g):
+    """float64 [L][d]: sequence b's keys for KV head g as decoded, straight
+    from the storage arrays (fp16 bits, or code * scale + zero rounded once)."""
+    L = int(lens[b])
+    t = np.arange(L)
+    phys = table[b, t // PAGE]
+    if cache.fmt == workloads.FMT_FP16:
+        return cache.k_pages[phys, g, t % PAGE].view(np.float16).astype(np.float64)
+    codes = cache.k_pages[phys, g, t % PAGE]
+    if cache.fmt == workloads.FMT_INT8_TOKEN:
+        p = cache.params[phys, g, t % PAGE]
+    else:
+        p = cache.params[phys, g]
+    return np_dequant(codes, p[:, 0:1], p[:, 1:2]).astype(np.float64)
+
+
+@pytest.mark.parametrize("n,group", [(4, 8), (5, 4), (2, 16), (5, 1)])
+def test_coarse_boxes_are_the_min_max_of_their_tokens(n, group):
+    """A super-page's box equals the min / max of the decoded keys of all its
+    tokens (brute force over the storage), and past the sequence nothing is
+    written."""
+    w = workloads.small(n)
+    cache, table = oracle.build_cache(w)
+    lens = w.seq_lens()
+    cm = oracle.coarse_meta(cache, table, lens, group)
+    pc_max = (table.shape[1] + group - 1) // group
+    for b in range(w.batch):
+        P = (int(lens[b]) + PAGE - 1) // PAGE
+        for g in range(w.num_kv_heads):
+            k = _decoded_keys(cache, table, lens, b, g)
+            for jc in range(pc_max):
+                box = cm[b * pc_max + jc, g].astype(np.float64)
+                t0, t1 = jc * group * PAGE, min((jc + 1) * group * PAGE, int(lens[b]))
+                if jc * group >= P:
+                    assert np.all(np.isinf(box)), (b, g, jc)
+                    continue
+                assert np.array_equal(box[0], k[t0:t1].min(0)) and np.array_equal(box[1], k[t0:t1].max(0))
+
+
+@pytest.mark.parametrize("n,group", [(4, 8), (5, 4), (2, 8)])
+def test_coarse_score_bounds_every_member_page(n, group):
+    """The coarse score of a super-page is at least the fine score of every
+    page in it (its box contains theirs), so it never underestimates q.k of
+    any of its tokens either."""
+    w = workloads.small(n)
+    cache, table = oracle.build_cache(w)
+    lens, q = w.seq_lens(), w.query()
+    view, ct, cl = oracle.coarse_view(cache, table, lens, group)
+    csc = oracle.page_scores(view, ct, cl, q)
+    fine = oracle.page_scores(cache, table, lens, q)
+    for b in range(w.batch):
+        P = (int(lens[b]) + PAGE - 1) // PAGE
+        for j in range(P):
+            r = fine[b, :, j]
+            R = csc[b, :, j // group]
+            assert np.all(R >= r - 1e-9 * np.maximum(1.0, np.abs(r))), (b, j)
+
+
+@pytest.mark.parametrize("n", [2, 4, 5])
+def test_hier_select_reduces_to_flat_top_k(n):
+    """Keeping every super-page, or super-pages of one page with at least K
+    kept, gives exactly the flat top-K selection; in general the selection
+    lies inside the kept super-pages once they hold at least K pages."""
+    w = workloads.small(n)
+    cache, table = oracle.build_cache(w)
+    lens, q = w.seq_lens(), w.query()
+    k_cap = table.shape[1]
+    flat_sc = oracle.page_scores(cache, table, lens, q)
+    fsel, fcnt = oracle.topk(flat_sc, lens, w.ratio_num, w.ratio_den, w.k_fixed, k_cap)
+    for group in (4, 8):
+        pc_max = (k_cap + group - 1) // group
+        *_, sel, cnt = oracle.hier_select(cache, table, lens, q, group, pc_max, w.ratio_num, w.ratio_den, w.k_fixed,
+                                          k_cap)
+        assert np.array_equal(sel, fsel) and np.array_equal(cnt, fcnt)
+    *_, sel, cnt = oracle.hier_select(cache, table, lens, q, 1, k_cap, w.ratio_num, w.ratio_den, w.k_fixed, k_cap)
+    assert np.array_equal(sel, fsel) and np.array_equal(cnt, fcnt)
+    group, kc = 4, 3
+    csc, csel, ccnt, masked, sel, cnt = oracle.hier_select(cache, table, lens, q, group, kc, w.ratio_num, w.ratio_den,
+                                                           w.k_fixed, k_cap)
+    for b in range(w.batch):
+        P = (int(lens[b]) + PAGE - 1) // PAGE
+        for g in range(w.num_kv_heads):
+            kept = set(csel[b, g, :ccnt[b, g]].tolist())
+            cand = [j for j in range(P) if j // group in kept]
+            assert ccnt[b, g] == min(kc, (P + group - 1) // group)
+            assert np.all(np.isneginf(masked[b, g, [j for j in range(P) if j not in cand]]))
+            assert np.array_equal(masked[b, g, cand], flat_sc[b, g, cand])
+            chosen = sel[b, g, :cnt[b, g]].tolist()
+            if len(cand) >= cnt[b, g]:
+                assert set(chosen) <= set(cand)
+            # the kept super-pages are the kc best coarse scores
+            order = sorted(range((P + group - 1) // group), key=lambda jc: (-csc[b, g, jc], jc))
+            assert kept == set(order[:kc])
+
+
+def test_hier_select_recall_report():
+    """Coarse-then-fine selection on the synthetic workloads (parity
+    unpinned, reported): the share of the flat top-K pages it keeps, the
+    share of dense attention weight on its pages beside flat top-K's, and
+    the metadata it reads (coarse boxes + the kept super-pages' pages) as a
+    share of all pages' metadata, for super-pages of 8 pages keeping 20-60%
+    of them."""
+    for w in [workloads.config(2), workloads.config(4), workloads.small(5).with_(batch=16, len_lo=600, len_hi=4000)]:
+        cache, table = oracle.build_cache(w)
+        lens, q = w.seq_lens(), w.query()
+        k_cap = table.shape[1]
+        flat = oracle.page_scores(cache, table, lens, q)
+        fsel, fcnt = oracle.topk(flat, lens, w.ratio_num, w.ratio_den, w.k_fixed, k_cap)
+        flat_mass = oracle.attention_mass(cache, table, lens, q, fsel, fcnt)
+        group = 8
+        P = (lens.astype(np.int64) + PAGE - 1) // PAGE
+        Pc = (P + group - 1) // group
+        row = [f"flat mass {flat_mass.mean():.3f}"]
+        for frac in (0.2, 0.4, 0.6):
+            kc = int(np.ceil(frac * Pc.max()))
+            *_, sel, cnt = oracle.hier_select(cache, table, lens, q, group, kc, w.ratio_num, w.ratio_den, w.k_fixed,
+                                              k_cap)
+            hit = tot = 0
+            for b in range(w.batch):
+                for g in range(w.num_kv_heads):
+                    K = int(fcnt[b, g])
+                    hit += len(set(sel[b, g, :K].tolist()) & set(fsel[b, g, :K].tolist()))
+                    tot += K
+            mass = oracle.attention_mass(cache, table, lens, q, sel, cnt)
+            read = (Pc.sum() + np.minimum(kc, Pc).sum() * group) / P.sum()
+            row.append(f"keep {frac:.0%}: recall {hit / tot:.3f}, mass {mass.mean():.3f}, metadata {read:.2f}")
+        print(f"[hier] {w.name}: " + "; ".join(row))
