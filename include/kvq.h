@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 4
+#define KVQ_ABI_VERSION 5
 #define KVQ_PAGE_SIZE 16
 #define KVQ_SELECT_MAX_PAGES 2048 /* longest row (pages) kvq_select_decode_attn takes */
 
@@ -179,6 +179,42 @@ kvq_status kvq_append_decode_scores(const kvq_cache *cache, const kvq_seqs *seqs
                                     const int32_t *start_pos, const int32_t *new_off, int32_t max_new,
                                     const uint16_t *k_new, const uint16_t *v_new,
                                     const uint16_t *q, int32_t num_q_heads, float *scores, void *stream);
+
+/*
+ * Coarse-then-fine selection ("TinyServe", section 6: for large models,
+ * screen coarsely first, then finely).  A super-page is group_pages
+ * consecutive logical pages of a sequence (1 <= group_pages <= 64; pc_max =
+ * ceil(max_pages / group_pages) super-pages per row).
+ *
+ * kvq_build_coarse_meta -- each super-page's box: the channel-wise min of its
+ * valid pages' metadata minima and max of their maxima, exact (min/max of
+ * page_meta, which must be current).  Written for super-pages
+ * super_begin[b] <= jc < ceil(P_b / group_pages) (super_begin NULL: all), as
+ *   coarse_meta  [B * pc_max][H_kv][2][d] fp32 (the page_meta layout with
+ *                "physical page" b * pc_max + jc),
+ *   coarse_lens  [B] int32: 16 * ceil(P_b / group_pages), and
+ *   coarse_table [B][pc_max] int32: b * pc_max + jc.
+ * With these as a cache view (page_meta = coarse_meta, num_phys_pages =
+ * B * pc_max) and a kvq_seqs view (max_pages = pc_max, seq_lens =
+ * coarse_lens, block_table = coarse_table), kvq_page_scores gives the coarse
+ * scores (each at least every member page's score) and kvq_topk_pages with
+ * k_fixed = kc the kept super-pages.
+ */
+kvq_status kvq_build_coarse_meta(const kvq_cache *cache, const kvq_seqs *seqs, int32_t group_pages,
+                                 const int32_t *super_begin, float *coarse_meta, int32_t *coarse_lens,
+                                 int32_t *coarse_table, void *stream);
+
+/*
+ * kvq_page_scores_masked -- kvq_page_scores restricted to the kept
+ * super-pages: for row (b, g), pages of the super-pages
+ * sel_super[b][g][0 .. sel_super_count[b][g]) (ascending, as kvq_topk_pages
+ * writes them; kc_cap is the row stride) get their page score, bit for bit
+ * what kvq_page_scores writes, and every other page j < max_pages gets -inf.
+ * Only the kept pages' metadata is read.
+ */
+kvq_status kvq_page_scores_masked(const kvq_cache *cache, const kvq_seqs *seqs, const uint16_t *q,
+                                  int32_t num_q_heads, int32_t group_pages, const int32_t *sel_super,
+                                  const int32_t *sel_super_count, int32_t kc_cap, float *scores, void *stream);
 
 /*
  * kvq_topk_pages -- per (sequence b, KV head) row of `scores`, select K_b of

@@ -11,7 +11,7 @@ Entry points keep the C names:
   kvq_page_scores, kvq_topk_pages,
   kvq_sparse_decode_attn, kvq_select_decode_attn, kvq_select_decode_attn_noalloc, kvq_attn_workspace_bytes,
   kvq_default_pages_per_split, kvq_decode_step, kvq_step_workspace_bytes, kvq_step_counter_bytes,
-  kvq_num_selected (as num_selected)
+  kvq_build_coarse_meta, kvq_page_scores_masked, kvq_num_selected (as num_selected)
 """
 from __future__ import annotations
 
@@ -73,13 +73,16 @@ def lib() -> ctypes.CDLL:
         L.kvq_select_decode_attn_noalloc.argtypes = [C, S, P, I, P, I, I, I, I, P, P, ctypes.c_float, I, P, P]
         L.kvq_decode_step.argtypes = [C, S, P, P, I, P, P, P, I, P, I, I, I, I, P, P, ctypes.c_float, I, P, P,
                                       ctypes.c_size_t, P]
+        L.kvq_build_coarse_meta.argtypes = [C, S, I, P, P, P, P, P]
+        L.kvq_page_scores_masked.argtypes = [C, S, P, I, I, P, P, I, P, P]
         L.kvq_step_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.kvq_step_workspace_bytes.restype = ctypes.c_size_t
         L.kvq_step_counter_bytes.argtypes = [I, I]
         L.kvq_step_counter_bytes.restype = ctypes.c_size_t
         for f in ("kvq_append_quant", "kvq_append_decode", "kvq_append_decode_scores", "kvq_build_page_meta",
                   "kvq_page_scores", "kvq_topk_pages", "kvq_sparse_decode_attn", "kvq_select_decode_attn",
-                  "kvq_select_decode_attn_noalloc", "kvq_decode_step"):
+                  "kvq_select_decode_attn_noalloc", "kvq_decode_step", "kvq_build_coarse_meta",
+                  "kvq_page_scores_masked"):
             getattr(L, f).restype = ctypes.c_int
         L.kvq_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
         L.kvq_read_probe.restype = ctypes.c_int
@@ -225,6 +228,21 @@ def kvq_page_scores(cache: PagedCache, seqs: Seqs, q, scores, stream=None) -> No
     _check("kvq_page_scores", lib().kvq_page_scores(
         ctypes.byref(cache.struct()), ctypes.byref(seqs.struct()), _ptr(qb), int(qb.shape[1]), _ptr(scores),
         _stream(stream)))
+
+
+def kvq_build_coarse_meta(cache: PagedCache, seqs: Seqs, group_pages: int, super_begin, coarse_meta, coarse_lens,
+                          coarse_table, stream=None) -> None:
+    _check("kvq_build_coarse_meta", lib().kvq_build_coarse_meta(
+        ctypes.byref(cache.struct()), ctypes.byref(seqs.struct()), int(group_pages), _ptr(super_begin),
+        _ptr(coarse_meta), _ptr(coarse_lens), _ptr(coarse_table), _stream(stream)))
+
+
+def kvq_page_scores_masked(cache: PagedCache, seqs: Seqs, q, group_pages: int, sel_super, sel_super_count, scores,
+                           stream=None) -> None:
+    qb = _half_bits(q)
+    _check("kvq_page_scores_masked", lib().kvq_page_scores_masked(
+        ctypes.byref(cache.struct()), ctypes.byref(seqs.struct()), _ptr(qb), int(qb.shape[1]), int(group_pages),
+        _ptr(sel_super), _ptr(sel_super_count), int(sel_super.shape[-1]), _ptr(scores), _stream(stream)))
 
 
 def kvq_topk_pages(scores, seqs: Seqs, num_kv_heads: int, ratio_num: int, ratio_den: int, k_fixed: int,

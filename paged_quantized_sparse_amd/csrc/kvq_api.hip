@@ -151,6 +151,34 @@ kvq_status kvq_page_scores(const kvq_cache* cache, const kvq_seqs* seqs, const u
   return from_hip(kvq::launch_page_scores(*cache, *seqs, q, num_q_heads, scores, (hipStream_t)stream));
 }
 
+kvq_status kvq_build_coarse_meta(const kvq_cache* cache, const kvq_seqs* seqs, int32_t group_pages,
+                                 const int32_t* super_begin, float* coarse_meta, int32_t* coarse_lens,
+                                 int32_t* coarse_table, void* stream) {
+  kvq_status st = check_cache(cache, true);
+  if (st != KVQ_OK) return st;
+  if ((st = check_seqs(seqs)) != KVQ_OK) return st;
+  if (group_pages < 1 || group_pages > 64) return KVQ_ERR_INVALID_ARG;
+  if (!coarse_meta || !coarse_lens || !coarse_table || !aligned16(coarse_meta)) return KVQ_ERR_INVALID_ARG;
+  if ((long long)seqs->batch * ((seqs->max_pages + group_pages - 1) / group_pages) > 0x7FFFFFFFLL)
+    return KVQ_ERR_UNSUPPORTED;
+  return from_hip(kvq::launch_coarse_meta(*cache, *seqs, group_pages, super_begin, coarse_meta, coarse_lens,
+                                          coarse_table, (hipStream_t)stream));
+}
+
+kvq_status kvq_page_scores_masked(const kvq_cache* cache, const kvq_seqs* seqs, const uint16_t* q,
+                                  int32_t num_q_heads, int32_t group_pages, const int32_t* sel_super,
+                                  const int32_t* sel_super_count, int32_t kc_cap, float* scores, void* stream) {
+  kvq_status st = check_cache(cache, true);
+  if (st != KVQ_OK) return st;
+  if ((st = check_seqs(seqs)) != KVQ_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != KVQ_OK) return st;
+  if (!q || !scores || !sel_super || !sel_super_count || !aligned16(q)) return KVQ_ERR_INVALID_ARG;
+  if (group_pages < 1 || group_pages > 64 || kc_cap < 1) return KVQ_ERR_INVALID_ARG;
+  if ((long long)seqs->batch * cache->num_kv_heads * kc_cap > 0x7FFFFFFFLL) return KVQ_ERR_UNSUPPORTED;
+  return from_hip(kvq::launch_page_scores_masked(*cache, *seqs, q, num_q_heads, group_pages, sel_super,
+                                                 sel_super_count, kc_cap, scores, (hipStream_t)stream));
+}
+
 kvq_status kvq_topk_pages(const float* scores, const kvq_seqs* seqs, int32_t num_kv_heads, int32_t ratio_num,
                           int32_t ratio_den, int32_t k_fixed, int32_t k_cap, int32_t* sel_pages,
                           int32_t* sel_count, void* stream) {

@@ -20,7 +20,8 @@ import torch
 
 from . import (KVQ_INT8_GROUP64, PAGE_SIZE, SELECT_MAX_PAGES, STEP_MAX_SEQS, STEP_MAX_SPLIT_PAGES, PagedCache, Seqs,
                kvq_append_decode, kvq_append_decode_scores, kvq_append_quant, kvq_attn_workspace_bytes,
-               kvq_build_page_meta, kvq_decode_step, kvq_default_pages_per_split, kvq_page_scores,
+               kvq_build_coarse_meta, kvq_build_page_meta, kvq_decode_step, kvq_default_pages_per_split,
+               kvq_page_scores, kvq_page_scores_masked,
                kvq_select_decode_attn, kvq_sparse_decode_attn, kvq_step_workspace_bytes, kvq_topk_pages,
                num_selected)
 
@@ -210,3 +211,61 @@ class DecodeStep:
         kvq_topk_pages(self.scores, self.seqs, self.cache.num_kv_heads, rn, rd, kf, self.sel_pages,
                        self.sel_count, stream)
         return self.attend(q, self.sel_pages, self.sel_count, stream)
+
+
+class HierStep:
+    """Coarse-then-fine selection (TinyServe page, section 6) in front of the
+    attention of a DecodeStep: super-pages of `group` consecutive pages are
+    screened by their boxes (kvq_build_coarse_meta, kvq_page_scores on the
+    coarse view, kvq_topk_pages keeping `keep` of them per row), then only
+    their pages are scored (kvq_page_scores_masked) and the step's top-K and
+    attention run on those scores."""
+
+    def __init__(self, step: DecodeStep, group: int, keep: int, device="cuda"):
+        self.step, self.group, self.keep = step, group, keep
+        cache, seqs = step.cache, step.seqs
+        B, H, d, maxp = seqs.batch, cache.num_kv_heads, cache.head_dim, seqs.max_pages
+        self.pc_max = -(-maxp // group)
+        self.coarse = torch.full((B * self.pc_max, H, 2, d), float("nan"), dtype=torch.float32, device=device)
+        self.coarse_lens = torch.zeros(B, dtype=torch.int32, device=device)
+        self.coarse_table = torch.zeros((B, self.pc_max), dtype=torch.int32, device=device)
+        self.coarse_cache = PagedCache(cache.format, B * self.pc_max, H, d, cache.k_pages, cache.v_pages,
+                                       cache.kv_params, self.coarse)
+        self.coarse_seqs = Seqs(self.coarse_lens, self.coarse_table)
+        self.kc = min(keep, self.pc_max)
+        self.coarse_scores = torch.empty((B, H, self.pc_max), dtype=torch.float32, device=device)
+        self.sel_super = torch.empty((B, H, self.kc), dtype=torch.int32, device=device)
+        self.sel_super_count = torch.empty((B, H), dtype=torch.int32, device=device)
+
+    def build(self, super_begin=None, stream=None) -> None:
+        kvq_build_coarse_meta(self.step.cache, self.step.seqs, self.group, super_begin, self.coarse,
+                              self.coarse_lens, self.coarse_table, stream)
+
+    def screen(self, q, stream=None) -> None:
+        """Coarse scores, the kept super-pages, and the masked fine scores."""
+        st = self.step
+        kvq_page_scores(self.coarse_cache, self.coarse_seqs, q, self.coarse_scores, stream)
+        kvq_topk_pages(self.coarse_scores, self.coarse_seqs, st.cache.num_kv_heads, 0, 1, self.kc, self.sel_super,
+                       self.sel_super_count, stream)
+        kvq_page_scores_masked(st.cache, st.seqs, q, self.group, self.sel_super, self.sel_super_count, st.scores,
+                               stream)
+
+    def attend(self, q, stream=None) -> torch.Tensor:
+        st = self.step
+        if st.fused_select:
+            return st.select_attend(q, stream)
+        rn, rd, kf = st.ratio
+        kvq_topk_pages(st.scores, st.seqs, st.cache.num_kv_heads, rn, rd, kf, st.sel_pages, st.sel_count, stream)
+        return st.attend(q, st.sel_pages, st.sel_count, stream)
+
+    def run(self, q, stream=None) -> torch.Tensor:
+        self.screen(q, stream)
+        return self.attend(q, stream)
+
+    def run_with_append(self, app: "DecodeAppend", super_begin, q, stream=None) -> torch.Tensor:
+        """Append the newest rows (and their pages' metadata), refresh the boxes
+        of the super-pages they touch (super_begin[b]: the first one), then
+        screen, select and attend."""
+        app.run(stream)
+        self.build(super_begin, stream)
+        return self.run(q, stream)

@@ -58,8 +58,8 @@ def test_library_never_allocates_or_synchronizes():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == 4
-    assert "#define KVQ_ABI_VERSION 4" in open(HEADER).read()
+    assert lib.kvq_abi_version() == 5
+    assert "#define KVQ_ABI_VERSION 5" in open(HEADER).read()
     for s, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP"), (99, b"unknown")]:
         assert word in lib.kvq_status_string(s)
 
