@@ -89,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.kvqo_quant_scale.restype = None
         L.kvqo_quant_code.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_float]
         L.kvqo_quant_code.restype = ctypes.c_uint8
+        L.kvqo_quant_scale_levels.argtypes = [ctypes.c_float, ctypes.c_float, I, P, P]
+        L.kvqo_quant_scale_levels.restype = None
+        L.kvqo_quant_code_levels.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_float, I]
+        L.kvqo_quant_code_levels.restype = ctypes.c_uint8
         _lib = L
     return _lib
 
@@ -111,13 +115,14 @@ class Cache:
 
     def __init__(self, fmt: int, num_phys_pages: int, num_kv_heads: int, head_dim: int):
         self.fmt, self.P_phys, self.H, self.d = fmt, num_phys_pages, num_kv_heads, head_dim
-        shape = (num_phys_pages, num_kv_heads, PAGE, head_dim)
+        row = head_dim // 2 if fmt in (3, 4) else head_dim   # INT4: two codes per byte
+        shape = (num_phys_pages, num_kv_heads, PAGE, row)
         dt = np.uint16 if fmt == 0 else np.uint8
         self.k_pages = np.zeros(shape, dtype=dt)
         self.v_pages = np.zeros(shape, dtype=dt)
-        if fmt == 1:
+        if fmt in (1, 3):
             self.params = np.zeros((num_phys_pages, num_kv_heads, PAGE, 4), dtype=np.float32)
-        elif fmt == 2:
+        elif fmt in (2, 4):
             self.params = np.zeros((num_phys_pages, num_kv_heads, 4), dtype=np.float32)
         else:
             self.params = np.zeros((1,), dtype=np.float32)
@@ -307,6 +312,17 @@ def quant_scale(lo: float, hi: float) -> tuple[np.float32, np.float32]:
 
 def quant_code(x: float, zero: float, inv: float) -> int:
     return int(lib().kvqo_quant_code(x, zero, inv))
+
+
+def quant_scale_levels(lo: float, hi: float, levels: int) -> tuple[np.float32, np.float32]:
+    s = ctypes.c_float()
+    inv = ctypes.c_float()
+    lib().kvqo_quant_scale_levels(lo, hi, levels, ctypes.byref(s), ctypes.byref(inv))
+    return np.float32(s.value), np.float32(inv.value)
+
+
+def quant_code_levels(x: float, zero: float, inv: float, levels: int) -> int:
+    return int(lib().kvqo_quant_code_levels(x, zero, inv, levels))
 
 
 # ------------------------------------------------------- whole-workload build

@@ -24,7 +24,8 @@
  *         section 2.1, Attention(Q,K,V) = softmax(Q K^T / sqrt(d)) V.
  *
  * Readings where the pages are silent:
- *   - quantization: unsigned codes 0..255, zero = row minimum (fp32, a
+ *   - quantization: unsigned codes 0..255 (INT8) or 0..15 (INT4, two per
+ *     byte, channel 2i in the low nibble), zero = row minimum (fp32, a
  *     minimum of -0 stored as +0),
  *     scale = (max - min) / 255 in fp32, codes = clamp(rint((x - zero) * (1/scale)))
  *     with round-half-to-even and every operation rounded to fp32; a constant
@@ -42,9 +43,10 @@
  *
  * Storage layout (caller-owned arrays, the paged layout C of [LY] section 2,
  * head-major inside each page so a (page, KV head) tile is contiguous):
- *   k_pages, v_pages : [P_phys][H_kv][16][d]   fp16 bits (FP16) or uint8 codes
- *   params  INT8_TOKEN  : [P_phys][H_kv][16][4] fp32 (k_scale, k_zero, v_scale, v_zero)
- *           INT8_GROUP64: [P_phys][H_kv][4]     fp32, the group's values in each of its pages
+ *   k_pages, v_pages : [P_phys][H_kv][16][d]   fp16 bits (FP16) or uint8 codes,
+ *                      [P_phys][H_kv][16][d/2] packed 4-bit codes (INT4)
+ *   params  INT8/INT4_TOKEN  : [P_phys][H_kv][16][4] fp32 (k_scale, k_zero, v_scale, v_zero)
+ *           INT8/INT4_GROUP64: [P_phys][H_kv][4]     fp32, the group's values in each of its pages
  *   meta    : [P_phys][H_kv][2][d] fp32, row 0 = per-channel min, row 1 = max
  *   block_table : [B][max_pages] int32, logical page j of sequence b -> physical page
  *
@@ -58,7 +60,15 @@
 
 #define PAGE 16
 
-enum { FMT_FP16 = 0, FMT_INT8_TOKEN = 1, FMT_INT8_GROUP64 = 2 };
+enum { FMT_FP16 = 0, FMT_INT8_TOKEN = 1, FMT_INT8_GROUP64 = 2, FMT_INT4_TOKEN = 3, FMT_INT4_GROUP64 = 4 };
+
+/* Storage formats that keep one (scale, zero) per token, and per 64-token   */
+/* group; the largest code of each quantized format (INT8: 255, INT4: 15, the */
+/* 4-bit row of the quantization table on the KV-cache optimization page,     */
+/* section 3.2).                                                              */
+static int per_token(int fmt) { return fmt == FMT_INT8_TOKEN || fmt == FMT_INT4_TOKEN; }
+static int per_group(int fmt) { return fmt == FMT_INT8_GROUP64 || fmt == FMT_INT4_GROUP64; }
+static int code_max(int fmt) { return fmt == FMT_INT4_TOKEN || fmt == FMT_INT4_GROUP64 ? 15 : 255; }
 
 /* ------------------------------------------------------------------------- */
 /* fp16 bits -> fp32, exactly, by decoding sign / exponent / mantissa.        */
@@ -82,16 +92,21 @@ static float half_bits_to_float(uint16_t h)
 /* Asymmetric min/max INT8 quantization of one row ([LY] section 2 per token, */
 /* [GM] chapter 1 per group).                                                 */
 /* ------------------------------------------------------------------------- */
-static void quant_scale(float lo, float hi, float *scale, float *inv)
+static void quant_scale_levels(float lo, float hi, int levels, float *scale, float *inv)
 {
     if (hi > lo) {
         float range = hi - lo;          /* rounded to fp32 */
-        *scale = range / 255.0f;        /* IEEE divide, rounded to fp32 */
+        *scale = range / (float)levels; /* IEEE divide, rounded to fp32 */
         *inv = 1.0f / *scale;           /* IEEE divide, rounded to fp32 */
     } else {
         *scale = 1.0f;
         *inv = 1.0f;
     }
+}
+
+static void quant_scale(float lo, float hi, float *scale, float *inv)
+{
+    quant_scale_levels(lo, hi, 255, scale, inv);
 }
 
 /* The zero-point is the row minimum; a minimum of -0 is stored as +0 (both  */
@@ -102,14 +117,19 @@ static float zero_point(float lo)
     return lo + 0.0f;
 }
 
-static uint8_t quant_code(float x, float zero, float inv)
+static uint8_t quant_code_levels(float x, float zero, float inv, int levels)
 {
     float shifted = x - zero;           /* rounded to fp32 */
     float t = shifted * inv;            /* rounded to fp32, not contracted */
     float r = rintf(t);                 /* round half to even */
     if (r < 0.0f) r = 0.0f;
-    if (r > 255.0f) r = 255.0f;
+    if (r > (float)levels) r = (float)levels;
     return (uint8_t)r;
+}
+
+static uint8_t quant_code(float x, float zero, float inv)
+{
+    return quant_code_levels(x, zero, inv, 255);
 }
 
 static float dequant(uint8_t c, float scale, float zero)
@@ -125,16 +145,36 @@ static size_t tile_elem(int phys, int h, int slot, int ch, int H, int d)
     return (((size_t)phys * H + h) * PAGE + slot) * (size_t)d + ch;
 }
 
+/* The code of channel ch of a token row: one byte (INT8), or one nibble of   */
+/* the row's d/2 bytes (INT4: channel 2i in the low nibble of byte i, 2i+1 in */
+/* its high nibble).                                                          */
+static unsigned get_code(int fmt, const void *pages, int phys, int h, int slot, int ch, int H, int d)
+{
+    if (code_max(fmt) == 255)
+        return ((const uint8_t *)pages)[tile_elem(phys, h, slot, ch, H, d)];
+    uint8_t byte = ((const uint8_t *)pages)[tile_elem(phys, h, slot, ch / 2, H, d / 2)];
+    return ch % 2 ? byte >> 4 : byte & 0xF;
+}
+
+static void put_code(int fmt, void *pages, int phys, int h, int slot, int ch, int H, int d, unsigned code)
+{
+    if (code_max(fmt) == 255) {
+        ((uint8_t *)pages)[tile_elem(phys, h, slot, ch, H, d)] = (uint8_t)code;
+        return;
+    }
+    uint8_t *byte = (uint8_t *)pages + tile_elem(phys, h, slot, ch / 2, H, d / 2);
+    *byte = ch % 2 ? (uint8_t)((*byte & 0x0F) | (code << 4)) : (uint8_t)((*byte & 0xF0) | code);
+}
+
 /* The key of token t of sequence b, channel ch, as attention reads it. */
 static float key_decoded(int fmt, const void *k_pages, const float *params,
                          const int32_t *bt_row, int t, int h, int ch, int H, int d)
 {
     int phys = bt_row[t / PAGE], slot = t % PAGE;
-    size_t e = tile_elem(phys, h, slot, ch, H, d);
     if (fmt == FMT_FP16)
-        return half_bits_to_float(((const uint16_t *)k_pages)[e]);
-    const uint8_t c = ((const uint8_t *)k_pages)[e];
-    if (fmt == FMT_INT8_TOKEN) {
+        return half_bits_to_float(((const uint16_t *)k_pages)[tile_elem(phys, h, slot, ch, H, d)]);
+    const uint8_t c = (uint8_t)get_code(fmt, k_pages, phys, h, slot, ch, H, d);
+    if (per_token(fmt)) {
         const float *p = params + (((size_t)phys * H + h) * PAGE + slot) * 4;
         return dequant(c, p[0], p[1]);
     }
@@ -146,11 +186,10 @@ static float value_decoded(int fmt, const void *v_pages, const float *params,
                            const int32_t *bt_row, int t, int h, int ch, int H, int d)
 {
     int phys = bt_row[t / PAGE], slot = t % PAGE;
-    size_t e = tile_elem(phys, h, slot, ch, H, d);
     if (fmt == FMT_FP16)
-        return half_bits_to_float(((const uint16_t *)v_pages)[e]);
-    const uint8_t c = ((const uint8_t *)v_pages)[e];
-    if (fmt == FMT_INT8_TOKEN) {
+        return half_bits_to_float(((const uint16_t *)v_pages)[tile_elem(phys, h, slot, ch, H, d)]);
+    const uint8_t c = (uint8_t)get_code(fmt, v_pages, phys, h, slot, ch, H, d);
+    if (per_token(fmt)) {
         const float *p = params + (((size_t)phys * H + h) * PAGE + slot) * 4;
         return dequant(c, p[2], p[3]);
     }
@@ -191,7 +230,7 @@ int kvqo_append(int fmt, int B, int H, int d, int max_pages,
                         ((uint16_t *)v_pages)[e] = vb[((size_t)i * H + h) * d + ch];
                     }
             }
-        } else if (fmt == FMT_INT8_TOKEN) {
+        } else if (per_token(fmt)) {
             /* one (scale, zero) per token, KV head, and K / V */
             for (int i = 0; i < n; ++i) {
                 int t = start + i;
@@ -208,20 +247,22 @@ int kvqo_append(int fmt, int B, int H, int d, int max_pages,
                         if (vx > vhi) vhi = vx;
                     }
                     float ks, kinv, vs, vinv;
+                    int levels = code_max(fmt);
                     klo = zero_point(klo);
                     vlo = zero_point(vlo);
-                    quant_scale(klo, khi, &ks, &kinv);
-                    quant_scale(vlo, vhi, &vs, &vinv);
+                    quant_scale_levels(klo, khi, levels, &ks, &kinv);
+                    quant_scale_levels(vlo, vhi, levels, &vs, &vinv);
                     for (int ch = 0; ch < d; ++ch) {
-                        size_t e = tile_elem(phys, h, slot, ch, H, d);
-                        ((uint8_t *)k_pages)[e] = quant_code(half_bits_to_float(kr[ch]), klo, kinv);
-                        ((uint8_t *)v_pages)[e] = quant_code(half_bits_to_float(vr[ch]), vlo, vinv);
+                        put_code(fmt, k_pages, phys, h, slot, ch, H, d,
+                                 quant_code_levels(half_bits_to_float(kr[ch]), klo, kinv, levels));
+                        put_code(fmt, v_pages, phys, h, slot, ch, H, d,
+                                 quant_code_levels(half_bits_to_float(vr[ch]), vlo, vinv, levels));
                     }
                     float *p = params + (((size_t)phys * H + h) * PAGE + slot) * 4;
                     p[0] = ks; p[1] = klo; p[2] = vs; p[3] = vlo;
                 }
             }
-        } else if (fmt == FMT_INT8_GROUP64) {
+        } else if (per_group(fmt)) {
             /* one (scale, zero) per 64-token logical group, KV head, and K / V */
             if (n > 0 && start % 64 != 0)
                 return -1;
@@ -239,19 +280,19 @@ int kvqo_append(int fmt, int B, int H, int d, int max_pages,
                             if (vx > vhi) vhi = vx;
                         }
                     float ks, kinv, vs, vinv;
+                    int levels = code_max(fmt);
                     klo = zero_point(klo);
                     vlo = zero_point(vlo);
-                    quant_scale(klo, khi, &ks, &kinv);
-                    quant_scale(vlo, vhi, &vs, &vinv);
+                    quant_scale_levels(klo, khi, levels, &ks, &kinv);
+                    quant_scale_levels(vlo, vhi, levels, &vs, &vinv);
                     for (int i = g0; i < g0 + gn; ++i) {
                         int t = start + i;
                         int phys = bt[t / PAGE], slot = t % PAGE;
                         for (int ch = 0; ch < d; ++ch) {
-                            size_t e = tile_elem(phys, h, slot, ch, H, d);
                             float kx = half_bits_to_float(kb[((size_t)i * H + h) * d + ch]);
                             float vx = half_bits_to_float(vb[((size_t)i * H + h) * d + ch]);
-                            ((uint8_t *)k_pages)[e] = quant_code(kx, klo, kinv);
-                            ((uint8_t *)v_pages)[e] = quant_code(vx, vlo, vinv);
+                            put_code(fmt, k_pages, phys, h, slot, ch, H, d, quant_code_levels(kx, klo, kinv, levels));
+                            put_code(fmt, v_pages, phys, h, slot, ch, H, d, quant_code_levels(vx, vlo, vinv, levels));
                         }
                         float *p = params + ((size_t)phys * H + h) * 4;   /* every page of the group */
                         p[0] = ks; p[1] = klo; p[2] = vs; p[3] = vlo;
@@ -623,3 +664,11 @@ float kvqo_half_to_float(uint16_t h) { return half_bits_to_float(h); }
 float kvqo_dequant(uint8_t c, float scale, float zero) { return dequant(c, scale, zero); }
 void kvqo_quant_scale(float lo, float hi, float *scale, float *inv) { quant_scale(lo, hi, scale, inv); }
 uint8_t kvqo_quant_code(float x, float zero, float inv) { return quant_code(x, zero, inv); }
+void kvqo_quant_scale_levels(float lo, float hi, int levels, float *scale, float *inv)
+{
+    quant_scale_levels(lo, hi, levels, scale, inv);
+}
+uint8_t kvqo_quant_code_levels(float x, float zero, float inv, int levels)
+{
+    return quant_code_levels(x, zero, inv, levels);
+}

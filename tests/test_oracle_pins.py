@@ -787,20 +787,33 @@ def test_lazy_metadata_refresh_report():
 
 
 # ------------------------------------------------- hierarchical selection
-def _decoded_keys(cache, table, lens, b, g):
-    """float64 [L][d]: sequence b's keys for KV head g as decoded, straight
-    from the storage arrays (fp16 bits, or code * scale + zero rounded once)."""
+def _unpack4(packed):
+    """[..][d/2] bytes -> [..][d] codes: channel 2i is the low nibble of byte i."""
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), np.uint8)
+    out[..., 0::2] = packed & 0xF
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def _decoded_keys(cache, table, lens, b, g, values=False):
+    """float64 [L][d]: sequence b's keys (or values) for KV head g as decoded,
+    straight from the storage arrays (fp16 bits, or code * scale + zero
+    rounded once)."""
     L = int(lens[b])
     t = np.arange(L)
     phys = table[b, t // PAGE]
+    pages = cache.v_pages if values else cache.k_pages
     if cache.fmt == workloads.FMT_FP16:
-        return cache.k_pages[phys, g, t % PAGE].view(np.float16).astype(np.float64)
-    codes = cache.k_pages[phys, g, t % PAGE]
-    if cache.fmt == workloads.FMT_INT8_TOKEN:
+        return pages[phys, g, t % PAGE].view(np.float16).astype(np.float64)
+    codes = pages[phys, g, t % PAGE]
+    if cache.fmt in (workloads.FMT_INT4_TOKEN, workloads.FMT_INT4_GROUP64):
+        codes = _unpack4(codes)
+    sz = (2, 3) if values else (0, 1)
+    if cache.fmt in (workloads.FMT_INT8_TOKEN, workloads.FMT_INT4_TOKEN):
         p = cache.params[phys, g, t % PAGE]
     else:
         p = cache.params[phys, g]
-    return np_dequant(codes, p[:, 0:1], p[:, 1:2]).astype(np.float64)
+    return np_dequant(codes, p[:, sz[0]:sz[0] + 1], p[:, sz[1]:sz[1] + 1]).astype(np.float64)
 
 
 @pytest.mark.parametrize("n,group", [(4, 8), (5, 4), (2, 16), (5, 1)])
@@ -914,3 +927,87 @@ def test_hier_select_recall_report():
             read = (Pc.sum() + np.minimum(kc, Pc).sum() * group) / P.sum()
             row.append(f"keep {frac:.0%}: recall {hit / tot:.3f}, mass {mass.mean():.3f}, metadata {read:.2f}")
         print(f"[hier] {w.name}: " + "; ".join(row))
+
+
+
+# ------------------------------------------------------------ 4-bit codes
+def test_quant4_golden_rows():
+    """Hand-worked 4-bit rows pin the scale (range / 15), zero, round half to
+    even, clamping, and the nibble order of the packed bytes."""
+    for row in gold("quant_rows_int4.json")["rows"]:
+        x = np.array([row["x"]], np.float16)
+        cache, table = one_token_cache(workloads.FMT_INT4_TOKEN, x)
+        packed = cache.k_pages[0, 0, 0, :x.shape[1] // 2]
+        assert packed.tolist() == row["bytes"], row["derivation"]
+        assert _unpack4(packed).tolist() == row["codes"]
+        s, z = cache.params[0, 0, 0, 0], cache.params[0, 0, 0, 1]
+        assert s == np.float32(row["scale"]) and z == np.float32(row["zero"])
+        assert np_dequant(_unpack4(packed), s, z).tolist() == [float(v) for v in row["decoded"]]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_quant4_error_within_half_scale_and_nearest_code(d):
+    """|x - decode(code)| <= scale/2 (+fp32 slack) with scale = range / 15,
+    the code is the nearest of its neighbours, min -> 0 decoding to min
+    exactly, max -> 15."""
+    rng = np.random.default_rng(17)
+    x = _random_rows(rng, 200, d)
+    cache, table = one_token_cache(workloads.FMT_INT4_TOKEN, x)
+    L = x.shape[0]
+    t = np.arange(L)
+    codes = _unpack4(cache.k_pages[t // PAGE, 0, t % PAGE]).astype(np.int64)
+    p = cache.params[t // PAGE, 0, t % PAGE]
+    s, z = p[:, 0], p[:, 1]
+    xf = x.astype(np.float32)
+    lo, hi = xf.min(1), xf.max(1)
+    assert np.array_equal(z, lo)
+    const = hi == lo
+    assert np.allclose(s[~const].astype(np.float64), (hi - lo)[~const].astype(np.float64) / 15.0, rtol=2 ** -22)
+    dec = np_dequant(codes, s[:, None], z[:, None]).astype(np.float64)
+    err = np.abs(xf.astype(np.float64) - dec)
+    ulp = np.spacing(np.maximum(np.abs(lo), np.abs(hi)).astype(np.float32)).astype(np.float64)
+    slack = 2 * ulp + 15 * s.astype(np.float64) * 2 ** -22
+    assert np.all(err <= s[:, None] / 2 + slack[:, None])
+    for dc in (-1, 1):
+        nb = np.clip(codes + dc, 0, 15)
+        dn = np.abs(xf - np_dequant(nb, s[:, None], z[:, None])).astype(np.float64)
+        assert np.all(err <= dn + slack[:, None])
+    assert np.all(codes.max(1)[~const] == 15) and np.all(codes.min(1) == 0)
+
+
+@pytest.mark.parametrize("fmt", [workloads.FMT_INT4_TOKEN, workloads.FMT_INT4_GROUP64])
+def test_int4_cache_metadata_scores_and_dense_attention(fmt):
+    """On 4-bit caches: metadata is the brute-force min/max of the decoded
+    keys; every page score bounds its tokens' q.k; per-group storage shares
+    one (scale, zero) over each 64-token group; K = P equals numpy's dense
+    softmax attention over the decoded keys and values."""
+    w = workloads.small(5).with_(fmt=fmt)
+    cache, table = oracle.build_cache(w)
+    lens, q = w.seq_lens(), w.query()
+    sc = oracle.page_scores(cache, table, lens, q)
+    out = oracle.attention(cache, table, lens, q)
+    G = w.group
+    for b in range(w.batch):
+        P = (int(lens[b]) + PAGE - 1) // PAGE
+        for g in range(w.num_kv_heads):
+            k = _decoded_keys(cache, table, lens, b, g)
+            v = _decoded_keys(cache, table, lens, b, g, values=True)
+            for j in range(P):
+                kj = k[16 * j:16 * (j + 1)]
+                m = cache.meta[table[b, j], g].astype(np.float64)
+                assert np.array_equal(m[0], kj.min(0)) and np.array_equal(m[1], kj.max(0))
+                for hh in range(G):
+                    qh = q[b, g * G + hh].astype(np.float64)
+                    assert sc[b, g, j] >= (kj @ qh).max() - 1e-9 * (1 + np.abs(sc[b, g, j]))
+            if fmt == workloads.FMT_INT4_GROUP64 and len(k):
+                t = np.arange(int(lens[b]))
+                pr = cache.params[table[b, t // PAGE], g]
+                for g0 in range(0, int(lens[b]), 64):
+                    assert (pr[g0:g0 + 64] == pr[g0]).all()
+            for hh in range(G):
+                qh = q[b, g * G + hh].astype(np.float64)
+                if len(k):
+                    lg = k @ qh / np.sqrt(w.head_dim)
+                    p_ = np.exp(lg - lg.max())
+                    ref = p_ @ v / p_.sum()
+                    assert np.allclose(out[b, g * G + hh], ref, rtol=0, atol=1e-12)

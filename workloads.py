@@ -34,7 +34,10 @@ PAGE = 16
 FMT_FP16 = 0
 FMT_INT8_TOKEN = 1
 FMT_INT8_GROUP64 = 2
-FORMAT_NAMES = {FMT_FP16: "fp16", FMT_INT8_TOKEN: "int8_token", FMT_INT8_GROUP64: "int8_group64"}
+FMT_INT4_TOKEN = 3
+FMT_INT4_GROUP64 = 4
+FORMAT_NAMES = {FMT_FP16: "fp16", FMT_INT8_TOKEN: "int8_token", FMT_INT8_GROUP64: "int8_group64",
+                FMT_INT4_TOKEN: "int4_token", FMT_INT4_GROUP64: "int4_group64"}
 
 # stream ids: one numpy stream per (stream, index)
 _S_LENS, _S_Q, _S_K, _S_V, _S_OUT, _S_TABLE = 0, 1, 2, 3, 4, 5
