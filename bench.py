@@ -46,17 +46,20 @@ HBM_PEAK_GBS = 8000.0
 
 def algorithmic_bytes(w, k_per_row):
     """(metadata bytes of every page, selected KV bytes): each (page, KV head)
-    counted once; an INT8 tile carries its codes and its fp32 scale/zero."""
+    counted once; a quantized tile carries its codes (a byte per channel, or
+    half a byte for 4-bit codes) and its fp32 scale/zero."""
     import workloads
     d = w.head_dim
     pages = w.pages_per_seq().astype(np.int64)
     meta = int(pages.sum()) * w.num_kv_heads * 8 * d
+    int4 = w.fmt in (workloads.FMT_INT4_TOKEN, workloads.FMT_INT4_GROUP64)
+    codes = 2 * 16 * (d // 2 if int4 else d)
     if w.fmt == workloads.FMT_FP16:
         tile = 2 * 16 * d * 2
-    elif w.fmt == workloads.FMT_INT8_TOKEN:
-        tile = 2 * 16 * d + 16 * 16
+    elif w.fmt in (workloads.FMT_INT8_TOKEN, workloads.FMT_INT4_TOKEN):
+        tile = codes + 16 * 16
     else:
-        tile = 2 * 16 * d + 16
+        tile = codes + 16
     return meta, int(np.asarray(k_per_row, np.int64).sum()) * tile
 
 
@@ -150,6 +153,54 @@ def parity_stats(w, built, oracle_step, gpu):
     return st
 
 
+def hier_parity_stats(w, built, hs, gpu):
+    """The coarse-then-fine step against the oracle: kept super-pages (equal
+    to the oracle's on its own coarse scores, up to near-ties), the fine
+    selection (near-tie rule on the oracle's masked scores), the output (the
+    oracle's attention over the GPU's selection), and the recall of the flat
+    top-K (share of its pages the coarse-then-fine selection keeps)."""
+    import oracle
+    cache, table = built
+    lens, q = w.seq_lens(), w.query()
+    k_cap = oracle.num_selected(int(table.shape[1]), w.ratio_num, w.ratio_den, w.k_fixed)
+    csc, csel, ccnt, _, _, _ = oracle.hier_select(cache, table, lens, q, hs.group, hs.kc, w.ratio_num, w.ratio_den,
+                                                  w.k_fixed, k_cap)
+    st = {}
+    gcs, gcc = gpu["coarse_sel"], gpu["coarse_cnt"]
+    rows = same = 0
+    for b in range(gcs.shape[0]):
+        for g in range(gcs.shape[1]):
+            rows += 1
+            K = int(ccnt[b, g])
+            same += int(gcc[b, g]) == K and np.array_equal(gcs[b, g, :K], csel[b, g, :K])
+    st["kept_super_page_rows_identical"] = f"{same}/{rows}"
+    fine = oracle.page_scores(cache, table, lens, q)
+    masked = oracle.mask_scores(fine, hs.group, gcs, gcc)
+    osel, ocnt = oracle.topk(masked, lens, w.ratio_num, w.ratio_den, w.k_fixed, k_cap)
+    sel, cnt = gpu["sel"], gpu["cnt"]
+    same = swaps = 0
+    for b in range(sel.shape[0]):
+        for g in range(sel.shape[1]):
+            K = int(ocnt[b, g])
+            d = set(sel[b, g, :K].tolist()) ^ set(osel[b, g, :K].tolist())
+            same += not d and int(cnt[b, g]) == K
+            swaps += len(d) // 2
+    st["selection_rows_identical"] = f"{same}/{rows}"
+    st["near_tie_page_swaps"] = swaps
+    want = oracle.attention(cache, table, lens, q, sel, cnt)
+    st["out_max_abs_err"] = float(np.abs(gpu["out"].astype(np.float64) - want).max())
+    fsel, fcnt = oracle.topk(fine, lens, w.ratio_num, w.ratio_den, w.k_fixed, k_cap)
+    hit = tot = 0
+    for b in range(sel.shape[0]):
+        for g in range(sel.shape[1]):
+            K = int(fcnt[b, g])
+            hit += len(set(fsel[b, g, :K].tolist()) & set(sel[b, g, :int(cnt[b, g])].tolist()))
+            tot += K
+    st["recall_of_flat_topk"] = round(hit / max(tot, 1), 4)
+    st["tolerance"] = 2e-3
+    return st
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +212,12 @@ def main() -> int:
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--one-launch", action="store_true",
                     help="run the step as one persistent launch (kvq_decode_step) instead of three")
+    ap.add_argument("--hier", default="",
+                    help="coarse-then-fine selection GROUP:KEEP (super-pages of GROUP pages, KEEP = share of "
+                         "super-pages kept per row), e.g. 8:0.5")
+    ap.add_argument("--storage", default="",
+                    help="store the workload's cache in another format: fp16, int8_token, int8_group64, "
+                         "int4_token or int4_group64 (4-bit: head_dim 128)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle legs (CPU baseline and parity)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -193,6 +250,13 @@ def main() -> int:
     dev = "cuda:0"
     torch.cuda.set_device(0)
     w = workloads.config(args.config)
+    if args.storage:
+        fmt = {v: k for k, v in workloads.FORMAT_NAMES.items()}.get(args.storage)
+        if fmt is None:
+            print(f"bench.py: unknown storage {args.storage!r}", file=sys.stderr)
+            return 2
+        if fmt != w.fmt:
+            w = w.with_(name=f"{w.name}_as_{args.storage}", fmt=fmt)
     table, n_phys = w.block_table()
     lens = w.seq_lens()
     # each sequence's rows are drawn once: the prefill and the decode-time
@@ -243,10 +307,23 @@ def main() -> int:
                                 pages_per_split=args.pages_per_split, device=dev,
                                 fused_step=args.one_launch) for c in layers]
     NL = len(layers)
+    hiers = None
+    if args.hier:
+        group, keep_frac = args.hier.split(":")
+        group = int(group)
+        pc_max = -(-seqs.max_pages // group)
+        kc = max(1, int(np.ceil(float(keep_frac) * pc_max)))
+        hiers = [runtime.HierStep(st, group, kc, device=dev) for st in steps]
+        super_begin = [(a.page_begin // group).contiguous() for a in appends]
+        for h in hiers:
+            h.build()
     torch.cuda.synchronize()
 
     def one_step(i):
-        steps[i % NL].run_with_append(appends[i % NL], q)
+        if hiers is not None:
+            hiers[i % NL].run_with_append(appends[i % NL], super_begin[i % NL], q)
+        else:
+            steps[i % NL].run_with_append(appends[i % NL], q)
 
     # warm-up (eager), which also fills every layer's selection
     for i in range(max(args.warmup, NL)):
@@ -364,6 +441,18 @@ def main() -> int:
 
     counts = st0.sel_count.cpu().numpy() if not dense else np.tile(w.pages_per_seq()[:, None], (1, w.num_kv_heads))
     meta_b, kv_b = algorithmic_bytes(w, counts)
+    if hiers is not None:  # boxes of every super-page, then the kept super-pages' pages
+        h0 = hiers[0]
+        P = w.pages_per_seq().astype(np.int64)
+        Pc = -(-P // h0.group)
+        kept = h0.sel_super.cpu().numpy()
+        kcnt = h0.sel_super_count.cpu().numpy()
+        fine_pages = 0
+        for b in range(w.batch):
+            for g in range(w.num_kv_heads):
+                for jc in kept[b, g, :kcnt[b, g]]:
+                    fine_pages += max(0, min(int(P[b]), (int(jc) + 1) * h0.group) - int(jc) * h0.group)
+        meta_b = (int(Pc.sum()) * w.num_kv_heads + fine_pages) * 8 * w.head_dim
     step_bytes = (0 if dense else meta_b) + kv_b
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     attn_gbs = kv_b / (attn_step_us * 1e-6) / 1e9
@@ -392,6 +481,9 @@ def main() -> int:
     cpu = cpu1 = parity = None
     oracle_build_s = None
     threads = host_threads()
+    if hiers is not None:
+        gpu["coarse_sel"] = hiers[0].sel_super.cpu().numpy()
+        gpu["coarse_cnt"] = hiers[0].sel_super_count.cpu().numpy()
     if not args.no_cpu:
         import oracle
         print("[bench] building the oracle's cache ...", file=sys.stderr, flush=True)
@@ -399,15 +491,22 @@ def main() -> int:
         built = oracle.build_cache(w)
         oracle_build_s = time.perf_counter() - t0
         print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
+        # the oracle's flat step (every page scored), priced at its own bytes
+        flat_bytes = step_bytes
         t_cpu, reps, res = cpu_baseline(w, args.cpu_seconds, threads, built)
-        cpu = {"value": round(step_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        if hiers is not None:
+            flat_bytes = sum(algorithmic_bytes(w, res[2]))
+        cpu = {"value": round(flat_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": f"full decode step (scores, top-K, attention) of this workload on {threads} threads "
-                         f"({cpu_model()}), median of {reps} runs, {t_cpu * 1e3:.1f} ms each",
+                         f"({cpu_model()}), median of {reps} runs, {t_cpu * 1e3:.1f} ms each"
+                         + ("; the flat selection (every page scored)" if hiers is not None else ""),
                "us_per_step": round(t_cpu * 1e6, 1)}
         t1, reps1, _ = cpu_baseline(w, args.cpu_seconds / 2, 1, built)
-        cpu1 = {"value": round(step_bytes / t1 / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        cpu1 = {"value": round(flat_bytes / t1 / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                 "sample": f"the same step on one thread, median of {reps1} runs", "us_per_step": round(t1 * 1e6, 1)}
-        if not dense:
+        if hiers is not None:
+            parity = hier_parity_stats(w, built, hiers[0], gpu)
+        elif not dense:
             parity = parity_stats(w, built, res, gpu)
         else:
             want = oracle.attention(built[0], built[1], lens, w.query())
@@ -438,7 +537,9 @@ def main() -> int:
                    "selected_pages_per_head": int(counts.max()), "layers_rotated": NL,
                    "launch": "eager" if graphs is None else "hip_graph",
                    "pages_per_split": st0.pps, "select_in_attention_kernel": bool(st0.fused_select),
-                   "one_launch_step": bool(st0.fused_step)},
+                   "one_launch_step": bool(st0.fused_step),
+                   "coarse_then_fine": None if hiers is None else {"group_pages": hiers[0].group,
+                                                                   "kept_per_row": hiers[0].kc}},
         "bytes_per_step": {"metadata": meta_b if not dense else 0, "selected_kv": kv_b},
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -35,17 +35,21 @@
  *     KV head h / G.
  *
  * Storage layout of one layer's cache (all C-contiguous):
- *   k_pages, v_pages   [P_phys][H_kv][16][d]  fp16 bits (KVQ_FP16) or uint8 codes
- *   kv_params          KVQ_INT8_TOKEN  : [P_phys][H_kv][16][4] fp32
- *                                        (k_scale, k_zero, v_scale, v_zero) per token slot
- *                      KVQ_INT8_GROUP64: [P_phys][H_kv][4] fp32, the 64-token
- *                                        group's values repeated in each of its pages
- *                      KVQ_FP16        : unused (may be NULL)
+ *   k_pages, v_pages   [P_phys][H_kv][16][d]  fp16 bits (KVQ_FP16) or uint8 codes (INT8);
+ *                      [P_phys][H_kv][16][d/2] packed 4-bit codes (INT4: channel 2i in
+ *                      the low nibble of byte i, 2i+1 in its high nibble)
+ *   kv_params          *_TOKEN  : [P_phys][H_kv][16][4] fp32
+ *                                 (k_scale, k_zero, v_scale, v_zero) per token slot
+ *                      *_GROUP64: [P_phys][H_kv][4] fp32, the 64-token
+ *                                 group's values repeated in each of its pages
+ *                      KVQ_FP16 : unused (may be NULL)
  *   page_meta          [P_phys][H_kv][2][d] fp32: row 0 per-channel min, row 1 max
  * A stored key or value decodes to fmaf(code, scale, zero) (INT8) or to the
- * fp16 value (FP16).  Codes are unsigned 0..255 with zero = the quantized
- * row's minimum (a minimum of -0 is stored as +0) and scale = (max - min) /
- * 255; a constant row has scale 1.
+ * fp16 value (FP16).  Codes are unsigned 0..255 (INT8) or 0..15 (INT4, the
+ * 4-bit row of the quantization table on the KV-cache optimization page,
+ * section 3.2) with zero = the quantized row's minimum (a minimum of -0 is
+ * stored as +0) and scale = (max - min) / 255 (or / 15); a constant row has
+ * scale 1.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -57,7 +61,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 5
+#define KVQ_ABI_VERSION 6
 #define KVQ_PAGE_SIZE 16
 #define KVQ_SELECT_MAX_PAGES 2048 /* longest row (pages) kvq_select_decode_attn takes */
 
@@ -72,7 +76,9 @@ typedef enum {
 typedef enum {
     KVQ_FP16 = 0,
     KVQ_INT8_TOKEN = 1,
-    KVQ_INT8_GROUP64 = 2
+    KVQ_INT8_GROUP64 = 2,
+    KVQ_INT4_TOKEN = 3,    /* 4-bit codes, head_dim 128 only */
+    KVQ_INT4_GROUP64 = 4   /* 4-bit codes, head_dim 128 only */
 } kvq_format;
 
 /* Non-owning view of one layer's paged cache (host struct, device pointers). */
@@ -308,7 +314,8 @@ kvq_status kvq_select_decode_attn(const kvq_cache *cache, const kvq_seqs *seqs,
  *     bound (the launch then still ends, with wrong results, and may leave
  *     counters set); a correct launch never does that.
  *   - Limits (else KVQ_ERR_UNSUPPORTED): max_pages <= KVQ_SELECT_MAX_PAGES,
- *     batch <= KVQ_STEP_MAX_SEQS, pages_per_split <= KVQ_STEP_MAX_SPLIT_PAGES.
+ *     batch <= KVQ_STEP_MAX_SEQS, pages_per_split <= KVQ_STEP_MAX_SPLIT_PAGES,
+ *     fp16 or INT8 storage.
  * max_new may be 0 (no rows appended; k_new / v_new may then be NULL).
  */
 #define KVQ_STEP_MAX_SEQS 512

@@ -24,7 +24,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
-KVQ_FP16, KVQ_INT8_TOKEN, KVQ_INT8_GROUP64 = 0, 1, 2
+KVQ_FP16, KVQ_INT8_TOKEN, KVQ_INT8_GROUP64, KVQ_INT4_TOKEN, KVQ_INT4_GROUP64 = 0, 1, 2, 3, 4
 PAGE_SIZE = 16
 SELECT_MAX_PAGES = 2048  # KVQ_SELECT_MAX_PAGES: longest row kvq_select_decode_attn takes
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
@@ -141,13 +141,15 @@ class PagedCache:
 
     @staticmethod
     def empty(fmt: int, num_phys_pages: int, num_kv_heads: int, head_dim: int, device="cuda") -> "PagedCache":
-        shape = (num_phys_pages, num_kv_heads, PAGE_SIZE, head_dim)
+        # 4-bit codes: two channels per byte, so a token row is head_dim / 2 bytes
+        row = head_dim // 2 if fmt in (KVQ_INT4_TOKEN, KVQ_INT4_GROUP64) else head_dim
+        shape = (num_phys_pages, num_kv_heads, PAGE_SIZE, row)
         dt = torch.int16 if fmt == KVQ_FP16 else torch.uint8
         k = torch.zeros(shape, dtype=dt, device=device)
         v = torch.zeros(shape, dtype=dt, device=device)
-        if fmt == KVQ_INT8_TOKEN:
+        if fmt in (KVQ_INT8_TOKEN, KVQ_INT4_TOKEN):
             p = torch.zeros((num_phys_pages, num_kv_heads, PAGE_SIZE, 4), dtype=torch.float32, device=device)
-        elif fmt == KVQ_INT8_GROUP64:
+        elif fmt in (KVQ_INT8_GROUP64, KVQ_INT4_GROUP64):
             p = torch.zeros((num_phys_pages, num_kv_heads, 4), dtype=torch.float32, device=device)
         else:
             p = None

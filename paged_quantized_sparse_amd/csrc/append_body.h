@@ -5,7 +5,9 @@
 // Writes sequence b's newest rows for KV head h into their pages (fp16 copy,
 // INT8 per token, or INT8 per 64-token group: "KV-cache layout from the
 // HBM-bandwidth viewpoint", pzsr.cn, sections 2-3; "Gemini KV cache:
-// FlashAttention-3 adaptation", uyd888.cn, chapter 1), and rebuilds the
+// FlashAttention-3 adaptation", uyd888.cn, chapter 1; the same two with 4-bit
+// codes, two per byte: the KV-cache quantization page of intelliparadigm.com,
+// section 3.2), and rebuilds the
 // metadata phi = (per-channel min, max of the decoded keys) of every page the
 // rows touch ("TinyServe", lpnh.cn, section 2.1).  The rows end the sequence,
 // so a touched page's valid tokens are those before start + rows.
@@ -16,7 +18,7 @@
 // registers (lane l owns channels l*E .. l*E+E-1) and so holds the page's
 // whole min/max without any exchange between waves.  The metadata is written
 // to HBM and, for a caller that scores the touched pages, to `sm_meta` in LDS.
-// Decoded INT8 keys are fmaf(code, scale, zero) exactly as every other reader
+// Decoded keys are fmaf(code, scale, zero) exactly as every other reader
 // computes them.
 #pragma once
 
@@ -65,6 +67,10 @@ template <int FMT, int D, bool WT = false>
 __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b, int h,
                                                      float (*sm_meta)[2][D]) {
   constexpr int E = D / 64;
+  constexpr int BITS = fmt_int4(FMT) ? 4 : 8;
+  constexpr int LV = fmt_levels(FMT);
+  constexpr int CROW = D * BITS / 8;  // bytes of one token's codes
+  static_assert(!fmt_int4(FMT) || E == 2, "4-bit rows are built for head_dim 128");
   // at most 64 rows (the documented limit; clamping keeps every index in range)
   const int r0 = a.new_off[b], n = min(a.new_off[b + 1] - r0, 64);
   if (n <= 0) return;  // block-uniform
@@ -76,7 +82,7 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
 
   // ---- group (scale, zero): one per (64-token group, KV head), K and V apart
   float gk[2] = {0.0f, 0.0f}, gv[2] = {0.0f, 0.0f}, ginv[2] = {1.0f, 1.0f};
-  if constexpr (FMT == kInt8Group) {
+  if constexpr (fmt_group(FMT)) {
     float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
     for (int e = threadIdx.x; e < n * D; e += 256) {
       const size_t src = ((size_t)(r0 + e / D) * a.H + h) * D + e % D;
@@ -93,8 +99,8 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
     khi = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1]));
     vlo = zero_point(fminf(fminf(red[0][2], red[1][2]), fminf(red[2][2], red[3][2])));
     vhi = fmaxf(fmaxf(red[0][3], red[1][3]), fmaxf(red[2][3], red[3][3]));
-    quant_params(klo, khi, gk[0], ginv[0]);
-    quant_params(vlo, vhi, gv[0], ginv[1]);
+    quant_params<LV>(klo, khi, gk[0], ginv[0]);
+    quant_params<LV>(vlo, vhi, gv[0], ginv[1]);
     gk[1] = klo;
     gv[1] = vlo;
     if (threadIdx.x < 4 && threadIdx.x * kPage < n) {  // every page holding a row of the group
@@ -133,11 +139,14 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
 #pragma unroll
           for (int e = 0; e < E; ++e) kold[t][e] = half_bits_to_float(((const uint16_t*)a.k_pages)[row + e]);
         } else {
-          const float* p = FMT == kInt8Token ? a.params + (tile + t) * 4 : a.params + ((size_t)phys * a.H + h) * 4;
+          const float* p = fmt_token(FMT) ? a.params + (tile + t) * 4 : a.params + ((size_t)phys * a.H + h) * 4;
           const float s = p[0], z = p[1];
+          const uint8_t* cp = (const uint8_t*)a.k_pages + (tile + t) * CROW + lane * E * BITS / 8;
 #pragma unroll
-          for (int e = 0; e < E; ++e)
-            kold[t][e] = __builtin_fmaf((float)((const uint8_t*)a.k_pages)[row + e], s, z);
+          for (int e = 0; e < E; ++e) {
+            const uint32_t c = fmt_int4(FMT) ? (cp[0] >> (4 * e)) & 0xFu : cp[e];
+            kold[t][e] = __builtin_fmaf((float)c, s, z);
+          }
         }
       }
 #pragma unroll
@@ -182,7 +191,7 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
           vx[e] = half_bits_to_float(a.v_new[src + e]);
         }
         float ks = gk[0], kz = gk[1], kinv = ginv[0], vs = gv[0], vz = gv[1], vinv = ginv[1];
-        if constexpr (FMT == kInt8Token) {
+        if constexpr (fmt_token(FMT)) {
           float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
 #pragma unroll
           for (int e = 0; e < E; ++e) {
@@ -191,8 +200,8 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
           }
           klo = zero_point(min_contig<64>(klo)); khi = max_contig<64>(khi);
           vlo = zero_point(min_contig<64>(vlo)); vhi = max_contig<64>(vhi);
-          quant_params(klo, khi, ks, kinv);
-          quant_params(vlo, vhi, vs, vinv);
+          quant_params<LV>(klo, khi, ks, kinv);
+          quant_params<LV>(vlo, vhi, vs, vinv);
           kz = klo;
           vz = vlo;
           if (lane == 0) {
@@ -210,21 +219,26 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
         uint32_t kw = 0, vw = 0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const uint32_t kc = quant_code(kx[e], kz, kinv);
-          const uint32_t vc = quant_code(vx[e], vz, vinv);
-          if constexpr (WT) {
-            kw |= kc << (8 * e);
-            vw |= vc << (8 * e);
-          } else {
-            ((uint8_t*)a.k_pages)[dst + e] = (uint8_t)kc;
-            ((uint8_t*)a.v_pages)[dst + e] = (uint8_t)vc;
-          }
+          const uint32_t kc = quant_code<LV>(kx[e], kz, kinv);
+          const uint32_t vc = quant_code<LV>(vx[e], vz, vinv);
+          kw |= kc << (BITS * e);
+          vw |= vc << (BITS * e);
           kdec[e] = __builtin_fmaf((float)kc, ks, kz);
         }
+        const size_t row = (tile + t % kPage) * CROW;
         if constexpr (WT) {
-          const size_t row = (tile + t % kPage) * D;
-          store_row_dev<E>((uint8_t*)a.k_pages + row, kw);
-          store_row_dev<E>((uint8_t*)a.v_pages + row, vw);
+          store_row_dev<E * BITS / 8>((uint8_t*)a.k_pages + row, kw);
+          store_row_dev<E * BITS / 8>((uint8_t*)a.v_pages + row, vw);
+        } else {
+          uint8_t* kp = (uint8_t*)a.k_pages + row + lane * (E * BITS / 8);
+          uint8_t* vp = (uint8_t*)a.v_pages + row + lane * (E * BITS / 8);
+          if constexpr (E * BITS / 8 == 2) {
+            *(uint16_t*)kp = (uint16_t)kw;
+            *(uint16_t*)vp = (uint16_t)vw;
+          } else {
+            *kp = (uint8_t)kw;
+            *vp = (uint8_t)vw;
+          }
         }
       }
 #pragma unroll

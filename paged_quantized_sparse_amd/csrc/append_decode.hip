@@ -15,7 +15,9 @@ __global__ __launch_bounds__(256) void append_decode_kernel(AppendView a) {
 
 template <int FMT>
 hipError_t launch_fmt(const AppendView& a, int d, dim3 grid, hipStream_t st) {
-  if (d == 64)
+  if constexpr (fmt_int4(FMT))
+    hipLaunchKernelGGL((append_decode_kernel<FMT, 128>), grid, dim3(256), 0, st, a);
+  else if (d == 64)
     hipLaunchKernelGGL((append_decode_kernel<FMT, 64>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((append_decode_kernel<FMT, 128>), grid, dim3(256), 0, st, a);
@@ -32,7 +34,9 @@ hipError_t launch_append_decode(const kvq_cache& c, const kvq_seqs& s, const int
   dim3 grid(c.num_kv_heads, s.batch);
   if (c.format == KVQ_FP16) return launch_fmt<kFp16>(a, c.head_dim, grid, st);
   if (c.format == KVQ_INT8_TOKEN) return launch_fmt<kInt8Token>(a, c.head_dim, grid, st);
-  return launch_fmt<kInt8Group>(a, c.head_dim, grid, st);
+  if (c.format == KVQ_INT8_GROUP64) return launch_fmt<kInt8Group>(a, c.head_dim, grid, st);
+  if (c.format == KVQ_INT4_TOKEN) return launch_fmt<kInt4Token>(a, c.head_dim, grid, st);
+  return launch_fmt<kInt4Group>(a, c.head_dim, grid, st);
 }
 
 }  // namespace kvq

@@ -6,7 +6,9 @@
 // viewpoint", pzsr.cn, section 2 layout C and section 3 block tables).
 // Per-token INT8 from each token's own min/max (same page, section 2); one
 // scale/zero-point per 64 tokens ("Gemini KV cache: FlashAttention-3
-// adaptation", uyd888.cn, chapter 1).  Quantization arithmetic is IEEE fp32,
+// adaptation", uyd888.cn, chapter 1); the same with 4-bit codes (the
+// quantization table's 4-bit row, intelliparadigm.com KV-cache page,
+// section 3.2).  Quantization arithmetic is IEEE fp32,
 // round-to-nearest-even, without contraction, so codes are reproducible
 // bit for bit.
 #include "kvq_device.h"
@@ -51,11 +53,13 @@ __global__ __launch_bounds__(256) void append_fp16_kernel(AppendArgs a) {
   }
 }
 
-// ---------------------------------------------------------- INT8 per token
+// ------------------------------------------------- INT8 / INT4 per token
 // One wave per (token, KV head); 4 waves per block; grid (ceil(max_new*H/4), B).
-template <int D>
-__global__ __launch_bounds__(256) void append_int8_token_kernel(AppendArgs a) {
+template <int FMT, int D>
+__global__ __launch_bounds__(256) void append_token_kernel(AppendArgs a) {
   constexpr int E = D / 64;  // elements per lane
+  constexpr int LV = fmt_levels(FMT);
+  static_assert(!fmt_int4(FMT) || E == 2, "4-bit rows are built for head_dim 128");
   const int b = blockIdx.y;
   const int r0 = a.new_off[b], n = a.new_off[b + 1] - r0;
   const int pair = blockIdx.x * 4 + wave_id();
@@ -78,22 +82,25 @@ __global__ __launch_bounds__(256) void append_int8_token_kernel(AppendArgs a) {
   klo = zero_point(min_contig<64>(klo)); khi = max_contig<64>(khi);
   vlo = zero_point(min_contig<64>(vlo)); vhi = max_contig<64>(vhi);
   float ks, kinv, vs, vinv;
-  quant_params(klo, khi, ks, kinv);
-  quant_params(vlo, vhi, vs, vinv);
+  quant_params<LV>(klo, khi, ks, kinv);
+  quant_params<LV>(vlo, vhi, vs, vinv);
+  constexpr int BITS = fmt_int4(FMT) ? 4 : 8;
   uint32_t kc = 0, vc = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    kc |= quant_code(kx[e], klo, kinv) << (8 * e);
-    vc |= quant_code(vx[e], vlo, vinv) << (8 * e);
+    kc |= quant_code<LV>(kx[e], klo, kinv) << (BITS * e);
+    vc |= quant_code<LV>(vx[e], vlo, vinv) << (BITS * e);
   }
-  uint8_t* kp = (uint8_t*)a.k_pages + dst;
-  uint8_t* vp = (uint8_t*)a.v_pages + dst;
-  if constexpr (E == 2) {
-    *(uint16_t*)kp = (uint16_t)kc;
-    *(uint16_t*)vp = (uint16_t)vc;
+  if constexpr (fmt_int4(FMT)) {  // the lane's two channels are one byte of the d/2-byte row
+    const size_t byte = dst / 2;
+    ((uint8_t*)a.k_pages)[byte] = (uint8_t)kc;
+    ((uint8_t*)a.v_pages)[byte] = (uint8_t)vc;
+  } else if constexpr (E == 2) {
+    *(uint16_t*)((uint8_t*)a.k_pages + dst) = (uint16_t)kc;
+    *(uint16_t*)((uint8_t*)a.v_pages + dst) = (uint16_t)vc;
   } else {
-    *kp = (uint8_t)kc;
-    *vp = (uint8_t)vc;
+    ((uint8_t*)a.k_pages)[dst] = (uint8_t)kc;
+    ((uint8_t*)a.v_pages)[dst] = (uint8_t)vc;
   }
   if (lane == 0) {
     float4* p = (float4*)(a.params + (((size_t)phys * a.H + h) * kPage + t % kPage) * 4);
@@ -101,11 +108,12 @@ __global__ __launch_bounds__(256) void append_int8_token_kernel(AppendArgs a) {
   }
 }
 
-// ---------------------------------------------------------- INT8 per group
+// ------------------------------------------------- INT8 / INT4 per group
 // One block of 256 threads per (64-token group, KV head, sequence);
 // grid (ceil(max_new / 64), H, B).
-template <int D>
-__global__ __launch_bounds__(256) void append_int8_group_kernel(AppendArgs a) {
+template <int FMT, int D>
+__global__ __launch_bounds__(256) void append_group_kernel(AppendArgs a) {
+  constexpr int LV = fmt_levels(FMT);
   const int b = blockIdx.z, h = blockIdx.y, gi = blockIdx.x;
   const int r0 = a.new_off[b], n = a.new_off[b + 1] - r0;
   const int g0 = gi * 64;
@@ -131,16 +139,23 @@ __global__ __launch_bounds__(256) void append_int8_group_kernel(AppendArgs a) {
   vlo = zero_point(fminf(fminf(red[0][2], red[1][2]), fminf(red[2][2], red[3][2])));
   vhi = fmaxf(fmaxf(red[0][3], red[1][3]), fmaxf(red[2][3], red[3][3]));
   float ks, kinv, vs, vinv;
-  quant_params(klo, khi, ks, kinv);
-  quant_params(vlo, vhi, vs, vinv);
-  for (int e = threadIdx.x; e < elems; e += 256) {
+  quant_params<LV>(klo, khi, ks, kinv);
+  quant_params<LV>(vlo, vhi, vs, vinv);
+  constexpr int PER = fmt_int4(FMT) ? 2 : 1;  // channels per stored byte
+  for (int e = threadIdx.x * PER; e < elems; e += 256 * PER) {
     const int i = g0 + e / D, ch = e % D;
     const size_t src = ((size_t)(r0 + i) * a.H + h) * D + ch;
     const int t = start + i;
     const int phys = a.block_table[(size_t)b * a.max_pages + t / kPage];
-    const size_t dst = (((size_t)phys * a.H + h) * kPage + t % kPage) * D + ch;
-    ((uint8_t*)a.k_pages)[dst] = (uint8_t)quant_code(half_bits_to_float(a.k_new[src]), klo, kinv);
-    ((uint8_t*)a.v_pages)[dst] = (uint8_t)quant_code(half_bits_to_float(a.v_new[src]), vlo, vinv);
+    const size_t dst = ((((size_t)phys * a.H + h) * kPage + t % kPage) * D + ch) / PER;
+    uint32_t kc = 0, vc = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      kc |= quant_code<LV>(half_bits_to_float(a.k_new[src + u]), klo, kinv) << (4 * u);
+      vc |= quant_code<LV>(half_bits_to_float(a.v_new[src + u]), vlo, vinv) << (4 * u);
+    }
+    ((uint8_t*)a.k_pages)[dst] = (uint8_t)kc;
+    ((uint8_t*)a.v_pages)[dst] = (uint8_t)vc;
   }
   // the group's (scale, zero) go to every page holding one of its rows
   if (threadIdx.x < 4 && threadIdx.x * kPage < gn) {
@@ -154,15 +169,18 @@ template <int D>
 hipError_t launch_append_d(const kvq_cache& c, const kvq_seqs& s, const AppendArgs& a, int max_new,
                            hipStream_t st) {
   const int B = s.batch, H = c.num_kv_heads;
-  if (c.format == KVQ_FP16) {
-    dim3 grid((max_new + 3) / 4, B);
-    hipLaunchKernelGGL(append_fp16_kernel<D>, grid, dim3(256), 0, st, a);
-  } else if (c.format == KVQ_INT8_TOKEN) {
-    dim3 grid((unsigned)(((long long)max_new * H + 3) / 4), B);
-    hipLaunchKernelGGL(append_int8_token_kernel<D>, grid, dim3(256), 0, st, a);
-  } else {
-    dim3 grid((max_new + 63) / 64, H, B);
-    hipLaunchKernelGGL(append_int8_group_kernel<D>, grid, dim3(256), 0, st, a);
+  const dim3 token_grid((unsigned)(((long long)max_new * H + 3) / 4), B);
+  const dim3 group_grid((max_new + 63) / 64, H, B);
+  switch (c.format) {
+    case KVQ_FP16: hipLaunchKernelGGL(append_fp16_kernel<D>, dim3((max_new + 3) / 4, B), dim3(256), 0, st, a); break;
+    case KVQ_INT8_TOKEN: hipLaunchKernelGGL((append_token_kernel<kInt8Token, D>), token_grid, dim3(256), 0, st, a); break;
+    case KVQ_INT8_GROUP64: hipLaunchKernelGGL((append_group_kernel<kInt8Group, D>), group_grid, dim3(256), 0, st, a); break;
+    case KVQ_INT4_TOKEN:
+      if constexpr (D == 128) hipLaunchKernelGGL((append_token_kernel<kInt4Token, D>), token_grid, dim3(256), 0, st, a);
+      break;
+    default:
+      if constexpr (D == 128) hipLaunchKernelGGL((append_group_kernel<kInt4Group, D>), group_grid, dim3(256), 0, st, a);
+      break;
   }
   return hipGetLastError();
 }

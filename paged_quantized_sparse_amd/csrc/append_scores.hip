@@ -97,7 +97,10 @@ hipError_t launch_g(const AppendScoreArgs& a, int rows, int G, hipStream_t st) {
 
 template <int FMT>
 hipError_t launch_d(const AppendScoreArgs& a, int d, int rows, int G, hipStream_t st) {
-  return d == 64 ? launch_g<FMT, 64>(a, rows, G, st) : launch_g<FMT, 128>(a, rows, G, st);
+  if constexpr (fmt_int4(FMT))
+    return launch_g<FMT, 128>(a, rows, G, st);
+  else
+    return d == 64 ? launch_g<FMT, 64>(a, rows, G, st) : launch_g<FMT, 128>(a, rows, G, st);
 }
 
 }  // namespace
@@ -113,7 +116,9 @@ hipError_t launch_append_scores(const kvq_cache& c, const kvq_seqs& s, const int
   const int G = num_q_heads / c.num_kv_heads;
   if (c.format == KVQ_FP16) return launch_d<kFp16>(a, c.head_dim, rows, G, st);
   if (c.format == KVQ_INT8_TOKEN) return launch_d<kInt8Token>(a, c.head_dim, rows, G, st);
-  return launch_d<kInt8Group>(a, c.head_dim, rows, G, st);
+  if (c.format == KVQ_INT8_GROUP64) return launch_d<kInt8Group>(a, c.head_dim, rows, G, st);
+  if (c.format == KVQ_INT4_TOKEN) return launch_d<kInt4Token>(a, c.head_dim, rows, G, st);
+  return launch_d<kInt4Group>(a, c.head_dim, rows, G, st);
 }
 
 }  // namespace kvq

@@ -8,17 +8,19 @@
 //
 // Split-K: block (split s, KV head g, sequence b) takes selected pages
 // [s*PPS, (s+1)*PPS) of row (b, g); its waves take every NW-th page.  A wave
-// holds a whole (page, KV head) tile in flight as 16-byte loads: for a token
-// row of RB = d * elem bytes, LPT = RB/16 lanes share a token, so one load
+// holds a whole (page, KV head) tile in flight as LB-byte loads (16; 8 for
+// 4-bit codes, so a lane holds the same 16 channels as with INT8): for a
+// token row of RB bytes, LPT = RB/LB lanes share a token, so one load
 // instruction covers TPL = 64/LPT tokens, and NL = 16/TPL loads cover the page.
 // The next tile's loads are issued before the current tile is consumed.
 //
-// Keys: q.k runs on v_dot2_f32_f16 with the fp16 query.  An INT8 code c
-// becomes the fp16 value 1024 + c with one byte permute (0x64 is the high byte
-// of 1024.0h), so for per-token or per-group (scale s, zero z)
+// Keys: q.k runs on v_dot2_f32_f16 with the fp16 query.  A code c (8 or 4
+// bits) becomes the fp16 value 1024 + c with one byte permute (0x64 is the
+// high byte of 1024.0h; 4-bit codes are first split into their low and high
+// nibbles), so for per-token or per-group (scale s, zero z)
 //   q.k = s * sum q_i (1024 + c_i) + (z - 1024 s) * sum q_i.
-// Values: acc += (p s) * c per channel (byte converts + fma), plus p z once per
-// token.  The G query heads of a KV group share every loaded tile.
+// Values: acc += (p s) * c per channel (byte or nibble converts + fma), plus
+// p z once per token.  The G query heads of a KV group share every loaded tile.
 //
 // Online softmax per lane (exp2 domain): each lane keeps the running max m of
 // the tokens it saw and rescales only when a logit exceeds m by more than
@@ -74,13 +76,38 @@ struct AttnArgs {
 
 template <int FMT, int D>
 struct Tile {
-  static constexpr int ELEM = FMT == kFp16 ? 2 : 1;
-  static constexpr int RB = D * ELEM;
-  static constexpr int LPT = RB / 16;     // lanes per token
+  static constexpr int BITS = FMT == kFp16 ? 16 : fmt_int4(FMT) ? 4 : 8;  // per channel
+  static constexpr int RB = D * BITS / 8;                 // bytes of a token row
+  static constexpr int LB = fmt_int4(FMT) ? 8 : 16;       // bytes per lane and load
+  static constexpr int NWD = LB / 4;                      // words per lane and load
+  static constexpr int LPT = RB / LB;     // lanes per token
   static constexpr int TPL = 64 / LPT;    // tokens per load
   static constexpr int NL = kPage / TPL;  // loads per page
-  static constexpr int CH = 16 / ELEM;    // channels per lane
+  static constexpr int CH = LB * 8 / BITS;  // channels per lane
+  static_assert(!fmt_int4(FMT) || D == 128, "4-bit tiles are built for head_dim 128");
 };
+
+// One lane's part of one load: NWD words.
+template <int NWD>
+struct Raw {
+  uint32_t w[NWD];
+};
+
+template <int NWD>
+__device__ __forceinline__ Raw<NWD> load_raw(const void* p) {
+  if constexpr (NWD == 4) {
+    const uint4 v = load_stream_u4(p);
+    return Raw<4>{{v.x, v.y, v.z, v.w}};
+  } else {
+    const uint2 v = load_stream_u2(p);
+    return Raw<2>{{v.x, v.y}};
+  }
+}
+
+__device__ __forceinline__ Raw<4> load_raw_cached(const void* p) {
+  const uint4 v = *(const uint4*)p;
+  return Raw<4>{{v.x, v.y, v.z, v.w}};
+}
 
 __device__ __forceinline__ float byte_to_float(uint32_t w, int i) { return (float)((w >> (8 * i)) & 0xFFu); }
 
@@ -115,7 +142,7 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 // The key codes become fp16 1024 + c by byte permute, as in the vector path.
 template <int FMT, int D, int G>
 struct MfmaPath {
-  static constexpr bool on = FMT != kFp16 && G >= 2 && G <= 16;
+  static constexpr bool on = FMT != kFp16 && !fmt_int4(FMT) && G >= 2 && G <= 16;
   // value MFMAs per page (16 output channels each); also the query's groups
   // of 4 channels per lane (two per logits MFMA)
   static constexpr int NM = D / 16;
@@ -248,6 +275,7 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
   using MP = MfmaPath<FMT, D, G>;
   constexpr bool MF = MP::on;
   static_assert(!MF || NL == MP::NU, "an INT8 tile row is NL 16-byte loads per lane in both forms");
+  constexpr int NWD = T::NWD;
   const int row = b * a.H + g;
   const int first = s * a.pps;
   const int w = wave_id();
@@ -277,7 +305,9 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
   const int cc = lane % LPT;  // channel chunk
   const int ch0 = cc * CH;
 
-  // ---- query chunk in registers: fp16 pairs for v_dot2, and its fp32 sum
+  // ---- query chunk in registers: fp16 pairs for v_dot2, and its fp32 sum.
+  // With 4-bit codes each group of 8 channels is held as the pairs (0, 2),
+  // (4, 6), (1, 3), (5, 7), the order in which a key word's nibbles come out.
   half2v qh[G][CH / 2];
   float qsum[G];
 #pragma unroll
@@ -292,6 +322,12 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       for (int j = 0; j < 4; ++j) {
         qh[hh][4 * i + j] = as_half2(wd[j]);
         acc += half_bits_to_float(wd[j] & 0xFFFFu) + half_bits_to_float(wd[j] >> 16);
+      }
+      if constexpr (fmt_int4(FMT)) {
+        qh[hh][4 * i + 0] = as_half2(__builtin_amdgcn_perm(wd[1], wd[0], 0x05040100u));
+        qh[hh][4 * i + 1] = as_half2(__builtin_amdgcn_perm(wd[3], wd[2], 0x05040100u));
+        qh[hh][4 * i + 2] = as_half2(__builtin_amdgcn_perm(wd[1], wd[0], 0x07060302u));
+        qh[hh][4 * i + 3] = as_half2(__builtin_amdgcn_perm(wd[3], wd[2], 0x07060302u));
       }
     }
     qsum[hh] = acc;
@@ -378,9 +414,9 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
   const size_t tile_elems = (size_t)kPage * D;
   // scale/zero registers per tile: the matrix-core form wants tokens
   // 4(l/16) .. +3 per lane (per token) or the tile's one group pair
-  constexpr int NP = MF ? (FMT == kInt8Token ? 4 : 1) : NL;
+  constexpr int NP = MF ? (fmt_token(FMT) ? 4 : 1) : NL;
   struct PageRegs {
-    uint4 kr[NL], vr[NL];
+    Raw<NWD> kr[NL], vr[NL];
     float4 pr[NP];
     int nvalid;
   };
@@ -399,10 +435,10 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       // hint).
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
-        r.kr[u] = *(const uint4*)(kp + 16 * u);
-        r.vr[u] = *(const uint4*)(vp + 16 * u);
+        r.kr[u] = load_raw_cached(kp + 16 * u);
+        r.vr[u] = load_raw_cached(vp + 16 * u);
       }
-      if constexpr (FMT == kInt8Token) {
+      if constexpr (fmt_token(FMT)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           r.pr[i] = load_stream_f4(a.params + (((size_t)ph * a.H + g) * kPage + 4 * (lane >> 4) + i) * 4);
@@ -413,13 +449,13 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
     }
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const size_t off = (tile + (size_t)(i * TPL + tg) * D + ch0) * T::ELEM;
-      r.kr[i] = load_stream_u4((const char*)a.k_pages + off);
-      r.vr[i] = load_stream_u4((const char*)a.v_pages + off);
-      if constexpr (FMT == kInt8Token)
+      const size_t off = (tile + (size_t)(i * TPL + tg) * D + ch0) * T::BITS / 8;
+      r.kr[i] = load_raw<NWD>((const char*)a.k_pages + off);
+      r.vr[i] = load_raw<NWD>((const char*)a.v_pages + off);
+      if constexpr (fmt_token(FMT))
         r.pr[i] = load_stream_f4(a.params + ((size_t)ph * a.H + g) * (kPage * 4) + (i * TPL + tg) * 4);
     }
-    if constexpr (FMT == kInt8Group) {
+    if constexpr (fmt_group(FMT)) {
       const float4 gp = load_stream_f4(a.params + ((size_t)ph * a.H + g) * 4);
 #pragma unroll
       for (int i = 0; i < NL; ++i) r.pr[i] = gp;
@@ -434,7 +470,7 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       float4v cq = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
-        const uint32_t kw[4] = {r.kr[u].x, r.kr[u].y, r.kr[u].z, r.kr[u].w};
+        const uint32_t* kw = r.kr[u].w;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const half4v k0 = codes_1024(kw[2 * h2]), k1 = codes_1024(kw[2 * h2 + 1]);
@@ -496,7 +532,7 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       const uint32_t sel2 = (lane & 2) ? 0x07060302u : 0x01000504u;
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
-        const uint32_t vw[4] = {r.vr[u].x, r.vr[u].y, r.vr[u].z, r.vr[u].w};
+        const uint32_t* vw = r.vr[u].w;
 #pragma unroll
         for (int d4 = 0; d4 < 4; ++d4) {
           const short4v vb = codes_bf16(quad_transpose_bytes(vw[d4], sel1, sel2));
@@ -515,10 +551,8 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const bool pad = i * TPL + tg >= nvalid;
-      r.vr[i].x = pad ? 0u : r.vr[i].x;
-      r.vr[i].y = pad ? 0u : r.vr[i].y;
-      r.vr[i].z = pad ? 0u : r.vr[i].z;
-      r.vr[i].w = pad ? 0u : r.vr[i].w;
+#pragma unroll
+      for (int k = 0; k < NWD; ++k) r.vr[i].w[k] = pad ? 0u : r.vr[i].w[k];
       if constexpr (FMT != kFp16) {
         r.pr[i].z = pad ? 0.0f : r.pr[i].z;
         r.pr[i].w = pad ? 0.0f : r.pr[i].w;
@@ -528,13 +562,26 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
     float lg[G][NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const uint32_t kw[4] = {r.kr[i].x, r.kr[i].y, r.kr[i].z, r.kr[i].w};
+      const uint32_t* kw = r.kr[i].w;
       float dot[G];
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) dot[hh] = 0.0f;
 #pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4) {
-        if constexpr (FMT == kFp16) {
+      for (int d4 = 0; d4 < NWD; ++d4) {
+        if constexpr (fmt_int4(FMT)) {  // word d4: channels 8 d4 .. 8 d4 + 7 of the lane's run
+          const uint32_t lo = kw[d4] & 0x0F0F0F0Fu, hi = (kw[d4] >> 4) & 0x0F0F0F0Fu;
+          const half2v k02 = as_half2(__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u));
+          const half2v k46 = as_half2(__builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u));
+          const half2v k13 = as_half2(__builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u));
+          const half2v k57 = as_half2(__builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u));
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            dot[hh] = __builtin_amdgcn_fdot2(k02, qh[hh][4 * d4 + 0], dot[hh], false);
+            dot[hh] = __builtin_amdgcn_fdot2(k46, qh[hh][4 * d4 + 1], dot[hh], false);
+            dot[hh] = __builtin_amdgcn_fdot2(k13, qh[hh][4 * d4 + 2], dot[hh], false);
+            dot[hh] = __builtin_amdgcn_fdot2(k57, qh[hh][4 * d4 + 3], dot[hh], false);
+          }
+        } else if constexpr (FMT == kFp16) {
 #pragma unroll
           for (int hh = 0; hh < G; ++hh) dot[hh] = __builtin_amdgcn_fdot2(as_half2(kw[d4]), qh[hh][d4], dot[hh], false);
         } else {
@@ -562,10 +609,12 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
     float vf[NL][CH];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const uint32_t vw[4] = {r.vr[i].x, r.vr[i].y, r.vr[i].z, r.vr[i].w};
+      const uint32_t* vw = r.vr[i].w;
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        if constexpr (FMT == kFp16)
+        if constexpr (fmt_int4(FMT))
+          vf[i][c] = (float)((vw[c / 8] >> (4 * (c % 8))) & 0xFu);
+        else if constexpr (FMT == kFp16)
           vf[i][c] = half_bits_to_float((vw[c / 2] >> (16 * (c % 2))) & 0xFFFFu);
         else
           vf[i][c] = byte_to_float(vw[c / 4], c % 4);

@@ -74,7 +74,10 @@ hipError_t run_g(const AttnArgs& a, int B, int G, hipStream_t st) {
 
 template <int FMT>
 hipError_t run_d(const AttnArgs& a, int B, int D, int G, hipStream_t st) {
-  return D == 64 ? run_g<FMT, 64>(a, B, G, st) : run_g<FMT, 128>(a, B, G, st);
+  if constexpr (fmt_int4(FMT))
+    return run_g<FMT, 128>(a, B, G, st);
+  else
+    return D == 64 ? run_g<FMT, 64>(a, B, G, st) : run_g<FMT, 128>(a, B, G, st);
 }
 
 // Scratch for callers that cannot allocate (kvq_select_decode_attn_noalloc):
@@ -124,7 +127,9 @@ hipError_t launch_decode_attn(const kvq_cache& c, const kvq_seqs& s, const uint1
   const int G = num_q_heads / c.num_kv_heads;
   if (c.format == KVQ_FP16) return run_d<kFp16>(a, s.batch, c.head_dim, G, st);
   if (c.format == KVQ_INT8_TOKEN) return run_d<kInt8Token>(a, s.batch, c.head_dim, G, st);
-  return run_d<kInt8Group>(a, s.batch, c.head_dim, G, st);
+  if (c.format == KVQ_INT8_GROUP64) return run_d<kInt8Group>(a, s.batch, c.head_dim, G, st);
+  if (c.format == KVQ_INT4_TOKEN) return run_d<kInt4Token>(a, s.batch, c.head_dim, G, st);
+  return run_d<kInt4Group>(a, s.batch, c.head_dim, G, st);
 }
 
 }  // namespace kvq

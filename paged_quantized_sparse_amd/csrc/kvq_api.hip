@@ -15,7 +15,8 @@ kvq_status check_cache(const kvq_cache* c, bool need_meta) {
   if (!c) return KVQ_ERR_INVALID_ARG;
   if (c->page_size != KVQ_PAGE_SIZE) return KVQ_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
-  if (c->format != KVQ_FP16 && c->format != KVQ_INT8_TOKEN && c->format != KVQ_INT8_GROUP64)
+  if (c->format < KVQ_FP16 || c->format > KVQ_INT4_GROUP64) return KVQ_ERR_UNSUPPORTED;
+  if ((c->format == KVQ_INT4_TOKEN || c->format == KVQ_INT4_GROUP64) && c->head_dim != 128)
     return KVQ_ERR_UNSUPPORTED;
   if (c->num_kv_heads < 1 || c->num_kv_heads > 65535 || c->num_phys_pages < 1) return KVQ_ERR_INVALID_ARG;
   if (!c->k_pages || !c->v_pages || !aligned16(c->k_pages) || !aligned16(c->v_pages)) return KVQ_ERR_INVALID_ARG;
@@ -293,6 +294,7 @@ kvq_status kvq_decode_step(const kvq_cache* cache, const kvq_seqs* seqs, const i
   if (!(sm_scale == sm_scale)) return KVQ_ERR_INVALID_ARG;
   if (pages_per_split < 0 || pages_per_split > 4096) return KVQ_ERR_INVALID_ARG;
   if (seqs->max_pages > kvq::kSelMaxPages || seqs->batch > kvq::kStepMaxSeqs) return KVQ_ERR_UNSUPPORTED;
+  if (cache->format == KVQ_INT4_TOKEN || cache->format == KVQ_INT4_GROUP64) return KVQ_ERR_UNSUPPORTED;
   if (k_cap < kvq::num_selected(seqs->max_pages, ratio_num, ratio_den, k_fixed)) return KVQ_ERR_INVALID_ARG;
   const int32_t pps = pages_per_split ? pages_per_split
                                       : kvq_default_pages_per_split(seqs->batch, cache->num_kv_heads,

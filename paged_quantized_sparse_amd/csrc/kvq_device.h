@@ -14,7 +14,14 @@ namespace kvq {
 constexpr int kPage = 16;
 constexpr int kWave = 64;
 
-enum Format : int { kFp16 = 0, kInt8Token = 1, kInt8Group = 2 };
+enum Format : int { kFp16 = 0, kInt8Token = 1, kInt8Group = 2, kInt4Token = 3, kInt4Group = 4 };
+
+// One (scale, zero) per token slot, or per 64-token group; 4-bit codes (two
+// per byte, channel 2i in the low nibble of byte i); the largest code.
+constexpr bool fmt_token(int f) { return f == kInt8Token || f == kInt4Token; }
+constexpr bool fmt_group(int f) { return f == kInt8Group || f == kInt4Group; }
+constexpr bool fmt_int4(int f) { return f == kInt4Token || f == kInt4Group; }
+constexpr int fmt_levels(int f) { return fmt_int4(f) ? 15 : 255; }
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
@@ -181,6 +188,13 @@ __device__ __forceinline__ uint4 load_stream_u4(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint2 load_stream_u2(const void* p) {
+  const u32x2v v = __builtin_nontemporal_load((const u32x2v*)p);
+  return make_uint2(v.x, v.y);
+}
+
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float2 load_stream_f2(const float* p) {
@@ -234,15 +248,17 @@ __device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// Asymmetric min/max INT8 quantization of a row with minimum lo and maximum
-// hi: zero = lo, scale = (hi - lo) / 255, code = clamp(rint((x - zero) / scale))
-// with 1/scale precomputed; IEEE fp32, round to nearest even, no contraction,
-// so codes are reproducible bit for bit.  A constant row gets scale 1.
+// Asymmetric min/max quantization of a row with minimum lo and maximum hi to
+// codes 0..LEVELS (255: INT8, 15: 4-bit): zero = lo, scale = (hi - lo) /
+// LEVELS, code = clamp(rint((x - zero) / scale)) with 1/scale precomputed;
+// IEEE fp32, round to nearest even, no contraction, so codes are
+// reproducible bit for bit.  A constant row gets scale 1.
+template <int LEVELS = 255>
 __device__ __forceinline__ void quant_params(float lo, float hi, float& scale, float& inv) {
 #pragma clang fp contract(off)
   if (hi > lo) {
     float range = hi - lo;
-    scale = range / 255.0f;
+    scale = range / (float)LEVELS;
     inv = 1.0f / scale;
   } else {
     scale = 1.0f;
@@ -258,11 +274,12 @@ __device__ __forceinline__ float zero_point(float lo) {
   return lo + 0.0f;
 }
 
+template <int LEVELS = 255>
 __device__ __forceinline__ uint32_t quant_code(float x, float zero, float inv) {
 #pragma clang fp contract(off)
   float t = (x - zero) * inv;
   float r = __builtin_rintf(t);
-  r = fminf(fmaxf(r, 0.0f), 255.0f);
+  r = fminf(fmaxf(r, 0.0f), (float)LEVELS);
   return (uint32_t)r;
 }
 

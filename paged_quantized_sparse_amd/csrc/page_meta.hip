@@ -1,7 +1,7 @@
 // page_meta.hip -- per-page key metadata phi(K_j) = (m_j, M_j): the
 // per-channel min and max of the page's keys ("TinyServe", lpnh.cn, section
 // 2.1 direction-aware bounding box), kept in fp32 (section 5.2).  The keys
-// are taken as attention decodes them (fmaf(code, scale, zero) for INT8), so
+// are taken as attention decodes them (fmaf(code, scale, zero) for codes), so
 // the page score bounds every stored key exactly.
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -50,11 +50,17 @@ __global__ __launch_bounds__(256) void page_meta_kernel(MetaArgs a) {
 #pragma unroll
           for (int e = 0; e < E; ++e) k[e] = half_bits_to_float(src[e]);
         } else {
-          const uint8_t* src = (const uint8_t*)a.k_pages + row;
-          const float* p = FMT == kInt8Token ? a.params + (tile + t) * 4 : a.params + ((size_t)phys * a.H + h) * 4;
+          const float* p = fmt_token(FMT) ? a.params + (tile + t) * 4 : a.params + ((size_t)phys * a.H + h) * 4;
           const float sc = p[0], zr = p[1];
+          if constexpr (fmt_int4(FMT)) {  // channels 2l, 2l+1: the two nibbles of byte l
+            const uint32_t c = ((const uint8_t*)a.k_pages)[row / 2];
 #pragma unroll
-          for (int e = 0; e < E; ++e) k[e] = __builtin_fmaf((float)src[e], sc, zr);
+            for (int e = 0; e < E; ++e) k[e] = __builtin_fmaf((float)((c >> (4 * e)) & 0xFu), sc, zr);
+          } else {
+            const uint8_t* src = (const uint8_t*)a.k_pages + row;
+#pragma unroll
+            for (int e = 0; e < E; ++e) k[e] = __builtin_fmaf((float)src[e], sc, zr);
+          }
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) { lo[e] = fminf(lo[e], k[e]); hi[e] = fmaxf(hi[e], k[e]); }
@@ -68,7 +74,9 @@ __global__ __launch_bounds__(256) void page_meta_kernel(MetaArgs a) {
 
 template <int FMT>
 hipError_t launch_fmt(const MetaArgs& a, int d, dim3 grid, hipStream_t st) {
-  if (d == 64)
+  if constexpr (fmt_int4(FMT))
+    hipLaunchKernelGGL((page_meta_kernel<FMT, 128>), grid, dim3(256), 0, st, a);
+  else if (d == 64)
     hipLaunchKernelGGL((page_meta_kernel<FMT, 64>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((page_meta_kernel<FMT, 128>), grid, dim3(256), 0, st, a);
@@ -86,7 +94,9 @@ hipError_t launch_page_meta(const kvq_cache& c, const kvq_seqs& s, const int32_t
   dim3 grid((unsigned)((items + 3) / 4 < 65536 ? (items + 3) / 4 : 65536), s.batch);
   if (c.format == KVQ_FP16) return launch_fmt<kFp16>(a, c.head_dim, grid, st);
   if (c.format == KVQ_INT8_TOKEN) return launch_fmt<kInt8Token>(a, c.head_dim, grid, st);
-  return launch_fmt<kInt8Group>(a, c.head_dim, grid, st);
+  if (c.format == KVQ_INT8_GROUP64) return launch_fmt<kInt8Group>(a, c.head_dim, grid, st);
+  if (c.format == KVQ_INT4_TOKEN) return launch_fmt<kInt4Token>(a, c.head_dim, grid, st);
+  return launch_fmt<kInt4Group>(a, c.head_dim, grid, st);
 }
 
 }  // namespace kvq

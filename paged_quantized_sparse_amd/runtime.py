@@ -18,7 +18,8 @@ from typing import Callable
 import numpy as np
 import torch
 
-from . import (KVQ_INT8_GROUP64, PAGE_SIZE, SELECT_MAX_PAGES, STEP_MAX_SEQS, STEP_MAX_SPLIT_PAGES, PagedCache, Seqs,
+from . import (KVQ_INT4_GROUP64, KVQ_INT4_TOKEN, KVQ_INT8_GROUP64, PAGE_SIZE, SELECT_MAX_PAGES, STEP_MAX_SEQS,
+               STEP_MAX_SPLIT_PAGES, PagedCache, Seqs,
                kvq_append_decode, kvq_append_decode_scores, kvq_append_quant, kvq_attn_workspace_bytes,
                kvq_build_coarse_meta, kvq_build_page_meta, kvq_decode_step, kvq_default_pages_per_split,
                kvq_page_scores, kvq_page_scores_masked,
@@ -88,7 +89,7 @@ def build_cache(fmt: int, num_phys_pages: int, num_kv_heads: int, head_dim: int,
 
 class DecodeAppend:
     """Device buffers to append each sequence's newest token at position
-    L_b - 1 (INT8_GROUP64: re-supply its open 64-token group) and refresh the
+    L_b - 1 (per-group formats: re-supply its open 64-token group) and refresh the
     metadata of the pages it touched."""
 
     def __init__(self, cache: PagedCache, seqs: Seqs, seq_lens: np.ndarray, source_rows: KVSource,
@@ -96,7 +97,7 @@ class DecodeAppend:
         self.cache, self.seqs = cache, seqs
         lens = np.asarray(seq_lens, np.int64)
         last = lens - 1
-        if cache.format == KVQ_INT8_GROUP64:
+        if cache.format in (KVQ_INT8_GROUP64, KVQ_INT4_GROUP64):
             start = (last // 64) * 64
         else:
             start = last
@@ -155,8 +156,9 @@ class DecodeStep:
         self.sm_scale = 1.0 / float(np.sqrt(d))
         # the one-launch step (kvq_decode_step): its workspace starts zeroed
         # (counters) and the step keeps it so
+        # (fp16 and INT8 storage only)
         self.fused_step = (fused_step and not dense and maxp <= SELECT_MAX_PAGES and B <= STEP_MAX_SEQS
-                           and self.pps <= STEP_MAX_SPLIT_PAGES)
+                           and self.pps <= STEP_MAX_SPLIT_PAGES and cache.format < KVQ_INT4_TOKEN)
         self.step_workspace = None
         if self.fused_step:
             sb = kvq_step_workspace_bytes(B, num_q_heads, H, d, maxp, self.k_cap, self.pps)

@@ -58,8 +58,8 @@ def test_library_never_allocates_or_synchronizes():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == 5
-    assert "#define KVQ_ABI_VERSION 5" in open(HEADER).read()
+    assert lib.kvq_abi_version() == 6
+    assert "#define KVQ_ABI_VERSION 6" in open(HEADER).read()
     for s, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP"), (99, b"unknown")]:
         assert word in lib.kvq_status_string(s)
 
@@ -108,6 +108,9 @@ def test_attention_argument_errors(lib):
     assert _attn(lib, c3, s3) == UNSUPPORTED
     c4, s4 = _structs(fmt=7)
     assert _attn(lib, c4, s4) == UNSUPPORTED
+    for fmt in (3, 4):   # 4-bit storage is built for head_dim 128 only
+        c6, s6 = _structs(fmt=fmt, d=64)
+        assert _attn(lib, c6, s6) == UNSUPPORTED
     c5, s5 = _structs(B=0)
     assert _attn(lib, c5, s5) == INVALID
 
