@@ -23,6 +23,9 @@ Every function follows the pages it cites in ``kvq_oracle.c``:
                  the value sits in a minority of the KV cache)
   coarse_meta, mask_scores, hier_select -- coarse-then-fine selection over
                  super-pages of consecutive pages (TinyServe page, section 6)
+  demote      -- a mixed-precision cache (TinyServe page, section 6: pages of
+                 high importance in FP16, the rest INT8) moves a page from
+                 its FP16 pool to its INT8 pool
 """
 from __future__ import annotations
 
@@ -60,9 +63,9 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         I = ctypes.c_int
-        L.kvqo_append.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P]
+        L.kvqo_append.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P]
         L.kvqo_append.restype = I
-        L.kvqo_page_meta.argtypes = [I, I, I, I, I, P, P, P, P, P, P]
+        L.kvqo_page_meta.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P]
         L.kvqo_page_meta.restype = None
         L.kvqo_page_scores.argtypes = [I, I, I, I, I, P, P, P, P, P]
         L.kvqo_page_scores.restype = None
@@ -70,12 +73,14 @@ def lib() -> ctypes.CDLL:
         L.kvqo_num_selected.restype = I
         L.kvqo_topk.argtypes = [I, I, I, P, P, I, I, I, I, P, P]
         L.kvqo_topk.restype = I
-        L.kvqo_attention.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, ctypes.c_double, P]
+        L.kvqo_attention.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, ctypes.c_double, P]
         L.kvqo_attention.restype = None
-        L.kvqo_attention_mass.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, ctypes.c_double, P]
+        L.kvqo_attention_mass.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, I, ctypes.c_double, P]
         L.kvqo_attention_mass.restype = None
-        L.kvqo_decode_step.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, I, I, I,
+        L.kvqo_decode_step.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, I, I, I, I,
                                        ctypes.c_double, P, P, P, P, I]
+        L.kvqo_demote.argtypes = [I, I, I, I, I, I, P, P, I, P, P, P, P, P, P, P]
+        L.kvqo_demote.restype = I
         L.kvqo_decode_step.restype = I
         L.kvqo_coarse_meta.argtypes = [I, I, I, I, P, P, I, P, P]
         L.kvqo_coarse_meta.restype = None
@@ -111,16 +116,26 @@ def _bits(x: np.ndarray) -> np.ndarray:
 
 # --------------------------------------------------------------------- cache
 class Cache:
-    """One layer's paged cache as plain numpy arrays (the layout in kvq_oracle.c)."""
+    """One layer's paged cache as plain numpy arrays (the layout in kvq_oracle.c).
+    MIXED (fmt 5): physical pages 0 .. n16-1 are the FP16 pool and the rest the
+    INT8 (per token) pool, k_pages / v_pages one byte array holding both pools
+    in that order, params for the INT8 pool only."""
 
-    def __init__(self, fmt: int, num_phys_pages: int, num_kv_heads: int, head_dim: int):
+    def __init__(self, fmt: int, num_phys_pages: int, num_kv_heads: int, head_dim: int, n16: int = 0):
         self.fmt, self.P_phys, self.H, self.d = fmt, num_phys_pages, num_kv_heads, head_dim
+        self.n16 = n16 if fmt == 5 else 0
         row = head_dim // 2 if fmt in (3, 4) else head_dim   # INT4: two codes per byte
         shape = (num_phys_pages, num_kv_heads, PAGE, row)
         dt = np.uint16 if fmt == 0 else np.uint8
+        if fmt == 5:
+            assert 0 <= n16 <= num_phys_pages
+            tile = num_kv_heads * PAGE * head_dim
+            shape = (n16 * tile * 2 + (num_phys_pages - n16) * tile,)
         self.k_pages = np.zeros(shape, dtype=dt)
         self.v_pages = np.zeros(shape, dtype=dt)
-        if fmt in (1, 3):
+        if fmt == 5:
+            self.params = np.zeros((max(num_phys_pages - n16, 1), num_kv_heads, PAGE, 4), dtype=np.float32)
+        elif fmt in (1, 3):
             self.params = np.zeros((num_phys_pages, num_kv_heads, PAGE, 4), dtype=np.float32)
         elif fmt in (2, 4):
             self.params = np.zeros((num_phys_pages, num_kv_heads, 4), dtype=np.float32)
@@ -136,7 +151,7 @@ def append(cache: Cache, block_table, start_pos, new_off, k_new, v_new) -> None:
     off = np.ascontiguousarray(new_off, np.int32)
     kb, vb = _bits(k_new), _bits(v_new)
     B = sp.shape[0]
-    rc = lib().kvqo_append(cache.fmt, B, cache.H, cache.d, bt.shape[1], _p(bt), _p(sp), _p(off),
+    rc = lib().kvqo_append(cache.fmt, cache.n16, B, cache.H, cache.d, bt.shape[1], _p(bt), _p(sp), _p(off),
                            _p(kb), _p(vb), _p(cache.k_pages), _p(cache.v_pages), _p(cache.params))
     if rc != 0:
         raise ValueError("oracle append: precondition violated")
@@ -146,7 +161,7 @@ def page_meta(cache: Cache, block_table, seq_lens, page_begin=None) -> None:
     bt = np.ascontiguousarray(block_table, np.int32)
     sl = np.ascontiguousarray(seq_lens, np.int32)
     pb = None if page_begin is None else np.ascontiguousarray(page_begin, np.int32)
-    lib().kvqo_page_meta(cache.fmt, sl.shape[0], cache.H, cache.d, bt.shape[1], _p(bt), _p(sl), _p(pb),
+    lib().kvqo_page_meta(cache.fmt, cache.n16, sl.shape[0], cache.H, cache.d, bt.shape[1], _p(bt), _p(sl), _p(pb),
                          _p(cache.k_pages), _p(cache.params), _p(cache.meta))
 
 
@@ -190,7 +205,7 @@ def attention(cache: Cache, block_table, seq_lens, q, sel_pages=None, sel_count=
     sc = None if sel_count is None else np.ascontiguousarray(sel_count, np.int32)
     k_cap = 0 if sp is None else sp.shape[2]
     out = np.empty((B, Hq, d), dtype=np.float64)
-    lib().kvqo_attention(cache.fmt, B, Hq, cache.H, d, bt.shape[1], _p(bt), _p(sl), _p(qb),
+    lib().kvqo_attention(cache.fmt, cache.n16, B, Hq, cache.H, d, bt.shape[1], _p(bt), _p(sl), _p(qb),
                          _p(cache.k_pages), _p(cache.v_pages), _p(cache.params), _p(sp), _p(sc), k_cap,
                          float(sm_scale), _p(out))
     return out
@@ -209,7 +224,7 @@ def attention_mass(cache: Cache, block_table, seq_lens, q, sel_pages, sel_count,
     sp = np.ascontiguousarray(sel_pages, np.int32)
     sc = np.ascontiguousarray(sel_count, np.int32)
     out = np.empty((B, Hq), dtype=np.float64)
-    lib().kvqo_attention_mass(cache.fmt, B, Hq, cache.H, d, bt.shape[1], _p(bt), _p(sl), _p(qb),
+    lib().kvqo_attention_mass(cache.fmt, cache.n16, B, Hq, cache.H, d, bt.shape[1], _p(bt), _p(sl), _p(qb),
                               _p(cache.k_pages), _p(cache.params), _p(sp), _p(sc), sp.shape[2],
                               float(sm_scale), _p(out))
     return out
@@ -229,7 +244,7 @@ def decode_step(cache: Cache, block_table, seq_lens, q, ratio_num, ratio_den, k_
     sel = np.empty((B, cache.H, k_cap), dtype=np.int32)
     cnt = np.empty((B, cache.H), dtype=np.int32)
     out = np.empty((B, Hq, d), dtype=np.float64)
-    rc = lib().kvqo_decode_step(cache.fmt, B, Hq, cache.H, d, maxp, _p(bt), _p(sl), _p(qb),
+    rc = lib().kvqo_decode_step(cache.fmt, cache.n16, B, Hq, cache.H, d, maxp, _p(bt), _p(sl), _p(qb),
                                 _p(cache.k_pages), _p(cache.v_pages), _p(cache.params), _p(cache.meta),
                                 ratio_num, ratio_den, k_fixed, k_cap, float(sm_scale),
                                 _p(scores), _p(sel), _p(cnt), _p(out), int(nthreads))
@@ -239,6 +254,23 @@ def decode_step(cache: Cache, block_table, seq_lens, q, ratio_num, ratio_den, k_
 
 
 # -------------------------------------------------- hierarchical selection
+def demote(cache: Cache, block_table: np.ndarray, seq_lens, seq, page, dst) -> None:
+    """Move logical page page[i] of sequence seq[i] of a MIXED cache from its
+    FP16 page to INT8 page dst[i]: its valid tokens re-quantized per token from
+    their fp16 rows, block_table[seq[i]][page[i]] = dst[i] (in place), and the
+    page's metadata rebuilt."""
+    assert cache.fmt == 5 and block_table.dtype == np.int32 and block_table.flags["C_CONTIGUOUS"]
+    sl = np.ascontiguousarray(seq_lens, np.int32)
+    sq = np.ascontiguousarray(seq, np.int32)
+    pg = np.ascontiguousarray(page, np.int32)
+    ds = np.ascontiguousarray(dst, np.int32)
+    rc = lib().kvqo_demote(cache.n16, cache.P_phys, sl.shape[0], cache.H, cache.d, block_table.shape[1],
+                           _p(block_table), _p(sl), len(sq), _p(sq), _p(pg), _p(ds), _p(cache.k_pages),
+                           _p(cache.v_pages), _p(cache.params), _p(cache.meta))
+    if rc != 0:
+        raise ValueError("demote: an item does not move an FP16 page of its sequence to an INT8 page")
+
+
 def coarse_meta(cache: Cache, block_table, seq_lens, group: int) -> np.ndarray:
     """float32 [B * pc_max][H][2][d]: each super-page's bounding box, the
     min of its pages' minima and max of their maxima (pc_max =
@@ -332,7 +364,7 @@ def build_cache(w, upto=None) -> tuple[Cache, np.ndarray]:
     tokens.  Returns (cache, block_table)."""
     table, n_phys = w.block_table()
     lens = w.seq_lens() if upto is None else np.asarray(upto, np.int32)
-    cache = Cache(w.fmt, n_phys, w.num_kv_heads, w.head_dim)
+    cache = Cache(w.fmt, n_phys, w.num_kv_heads, w.head_dim, w.fp16_pool_pages())
     for b in range(w.batch):
         L = int(lens[b])
         k = w.keys(b)[:L]

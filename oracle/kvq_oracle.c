@@ -22,6 +22,8 @@
  *         scale/zero-point).
  *   [KV]  "KV-cache optimization and memory management" (intelliparadigm.com):
  *         section 2.1, Attention(Q,K,V) = softmax(Q K^T / sqrt(d)) V.
+ *   [TS] section 6 also lists a mixed-precision cache: pages of high
+ *         importance kept in FP16, the rest in INT8 (format MIXED below).
  *
  * Readings where the pages are silent:
  *   - quantization: unsigned codes 0..255 (INT8) or 0..15 (INT4, two per
@@ -40,6 +42,10 @@
  *     ties go to the lower logical page index; output ascending.
  *   - attention: softmax over every valid token of the selected pages, with
  *     the 1/sqrt(d) scale of [KV] section 2.1, in fp64.
+ *   - mixed precision: a page's precision is where it lives.  Physical pages
+ *     0 .. n16-1 form an FP16 pool, n16 .. P_phys-1 an INT8 pool quantized
+ *     per token; which pages are important is the caller's choice (it
+ *     allocates them from the FP16 pool and demotes them later).
  *
  * Storage layout (caller-owned arrays, the paged layout C of [LY] section 2,
  * head-major inside each page so a (page, KV head) tile is contiguous):
@@ -47,6 +53,9 @@
  *                      [P_phys][H_kv][16][d/2] packed 4-bit codes (INT4)
  *   params  INT8/INT4_TOKEN  : [P_phys][H_kv][16][4] fp32 (k_scale, k_zero, v_scale, v_zero)
  *           INT8/INT4_GROUP64: [P_phys][H_kv][4]     fp32, the group's values in each of its pages
+ *   MIXED   : k_pages, v_pages = the FP16 pool [n16][H_kv][16][d] fp16 bits,
+ *             then (at byte n16*H_kv*16*d*2) the INT8 pool [P_phys-n16][H_kv][16][d];
+ *             params [P_phys-n16][H_kv][16][4] for the INT8 pool only
  *   meta    : [P_phys][H_kv][2][d] fp32, row 0 = per-channel min, row 1 = max
  *   block_table : [B][max_pages] int32, logical page j of sequence b -> physical page
  *
@@ -60,7 +69,8 @@
 
 #define PAGE 16
 
-enum { FMT_FP16 = 0, FMT_INT8_TOKEN = 1, FMT_INT8_GROUP64 = 2, FMT_INT4_TOKEN = 3, FMT_INT4_GROUP64 = 4 };
+enum { FMT_FP16 = 0, FMT_INT8_TOKEN = 1, FMT_INT8_GROUP64 = 2, FMT_INT4_TOKEN = 3, FMT_INT4_GROUP64 = 4,
+       FMT_MIXED = 5 };
 
 /* Storage formats that keep one (scale, zero) per token, and per 64-token   */
 /* group; the largest code of each quantized format (INT8: 255, INT4: 15, the */
@@ -166,11 +176,40 @@ static void put_code(int fmt, void *pages, int phys, int h, int slot, int ch, in
     *byte = ch % 2 ? (uint8_t)((*byte & 0x0F) | (code << 4)) : (uint8_t)((*byte & 0xF0) | code);
 }
 
+/* Where physical page phys is stored: its own format, the array that holds */
+/* it and its index there (a MIXED cache keeps two pools in one array, the  */
+/* INT8 pool and its params indexed from 0).  Other formats: unchanged.     */
+typedef struct {
+    int fmt;
+    const void *pages;
+    const float *params;
+    int idx;
+} PageLoc;
+
+static PageLoc locate(int fmt, int n16, const void *pages, const float *params, int phys, int H, int d)
+{
+    PageLoc l = {fmt, pages, params, phys};
+    if (fmt == FMT_MIXED) {
+        if (phys < n16) {
+            l.fmt = FMT_FP16;
+        } else {
+            l.fmt = FMT_INT8_TOKEN;
+            l.pages = (const uint8_t *)pages + (size_t)n16 * H * PAGE * d * 2;
+            l.idx = phys - n16;
+        }
+    }
+    return l;
+}
+
 /* The key of token t of sequence b, channel ch, as attention reads it. */
-static float key_decoded(int fmt, const void *k_pages, const float *params,
+static float key_decoded(int fmt, int n16, const void *k_pages, const float *params,
                          const int32_t *bt_row, int t, int h, int ch, int H, int d)
 {
-    int phys = bt_row[t / PAGE], slot = t % PAGE;
+    PageLoc l = locate(fmt, n16, k_pages, params, bt_row[t / PAGE], H, d);
+    fmt = l.fmt;
+    k_pages = l.pages;
+    params = l.params;
+    int phys = l.idx, slot = t % PAGE;
     if (fmt == FMT_FP16)
         return half_bits_to_float(((const uint16_t *)k_pages)[tile_elem(phys, h, slot, ch, H, d)]);
     const uint8_t c = (uint8_t)get_code(fmt, k_pages, phys, h, slot, ch, H, d);
@@ -182,10 +221,14 @@ static float key_decoded(int fmt, const void *k_pages, const float *params,
     return dequant(c, p[0], p[1]);
 }
 
-static float value_decoded(int fmt, const void *v_pages, const float *params,
+static float value_decoded(int fmt, int n16, const void *v_pages, const float *params,
                            const int32_t *bt_row, int t, int h, int ch, int H, int d)
 {
-    int phys = bt_row[t / PAGE], slot = t % PAGE;
+    PageLoc l = locate(fmt, n16, v_pages, params, bt_row[t / PAGE], H, d);
+    fmt = l.fmt;
+    v_pages = l.pages;
+    params = l.params;
+    int phys = l.idx, slot = t % PAGE;
     if (fmt == FMT_FP16)
         return half_bits_to_float(((const uint16_t *)v_pages)[tile_elem(phys, h, slot, ch, H, d)]);
     const uint8_t c = (uint8_t)get_code(fmt, v_pages, phys, h, slot, ch, H, d);
@@ -198,16 +241,55 @@ static float value_decoded(int fmt, const void *v_pages, const float *params,
 }
 
 /* ------------------------------------------------------------------------- */
+/* One token row of one KV head into slot `slot` of page `idx` of a pool of   */
+/* format fmt: an fp16 copy, or one (scale, zero) per token and per K / V     */
+/* ([LY] section 2), codes of `levels` + 1 values.                            */
+/* ------------------------------------------------------------------------- */
+static void write_token(int fmt, void *k_pages, void *v_pages, float *params, int idx, int h, int slot,
+                        const uint16_t *kr, const uint16_t *vr, int H, int d)
+{
+    if (fmt == FMT_FP16) {
+        for (int ch = 0; ch < d; ++ch) {
+            size_t e = tile_elem(idx, h, slot, ch, H, d);
+            ((uint16_t *)k_pages)[e] = kr[ch];
+            ((uint16_t *)v_pages)[e] = vr[ch];
+        }
+        return;
+    }
+    float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
+    for (int ch = 0; ch < d; ++ch) {
+        float kx = half_bits_to_float(kr[ch]), vx = half_bits_to_float(vr[ch]);
+        if (kx < klo) klo = kx;
+        if (kx > khi) khi = kx;
+        if (vx < vlo) vlo = vx;
+        if (vx > vhi) vhi = vx;
+    }
+    float ks, kinv, vs, vinv;
+    int levels = code_max(fmt);
+    klo = zero_point(klo);
+    vlo = zero_point(vlo);
+    quant_scale_levels(klo, khi, levels, &ks, &kinv);
+    quant_scale_levels(vlo, vhi, levels, &vs, &vinv);
+    for (int ch = 0; ch < d; ++ch) {
+        put_code(fmt, k_pages, idx, h, slot, ch, H, d, quant_code_levels(half_bits_to_float(kr[ch]), klo, kinv, levels));
+        put_code(fmt, v_pages, idx, h, slot, ch, H, d, quant_code_levels(half_bits_to_float(vr[ch]), vlo, vinv, levels));
+    }
+    float *p = params + (((size_t)idx * H + h) * PAGE + slot) * 4;
+    p[0] = ks; p[1] = klo; p[2] = vs; p[3] = vlo;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Append: write new tokens into their paged slots, quantizing as the format says.*/
 /*                                                                            */
 /* Sequence b receives rows new_off[b] .. new_off[b+1]-1 of k_new / v_new     */
 /* ([N][H][d] fp16 bits) at logical positions start_pos[b], start_pos[b]+1, . */
 /* Token t goes to physical page block_table[b][t/16], slot t%16 ([LY]        */
-/* section 3).  For INT8_GROUP64, start_pos[b] must be a multiple of 64 and   */
-/* the rows must include every token of each group they touch.               */
+/* section 3); in a MIXED cache it takes the format of that page's pool.      */
+/* For the per-group formats, start_pos[b] must be a multiple of 64 and the   */
+/* rows must include every token of each group they touch.                   */
 /* Returns 0, or -1 on a precondition violation.                              */
 /* ------------------------------------------------------------------------- */
-int kvqo_append(int fmt, int B, int H, int d, int max_pages,
+int kvqo_append(int fmt, int n16, int B, int H, int d, int max_pages,
                 const int32_t *block_table, const int32_t *start_pos, const int32_t *new_off,
                 const uint16_t *k_new, const uint16_t *v_new,
                 void *k_pages, void *v_pages, float *params)
@@ -220,47 +302,14 @@ int kvqo_append(int fmt, int B, int H, int d, int max_pages,
         const uint16_t *vb = v_new + (size_t)new_off[b] * H * d;
         if (n < 0 || start < 0 || (start + n + PAGE - 1) / PAGE > max_pages)
             return -1;
-        if (fmt == FMT_FP16) {
+        if (fmt == FMT_FP16 || per_token(fmt) || fmt == FMT_MIXED) {
             for (int i = 0; i < n; ++i) {
                 int t = start + i;
+                PageLoc kl = locate(fmt, n16, k_pages, params, bt[t / PAGE], H, d);
+                PageLoc vl = locate(fmt, n16, v_pages, params, bt[t / PAGE], H, d);
                 for (int h = 0; h < H; ++h)
-                    for (int ch = 0; ch < d; ++ch) {
-                        size_t e = tile_elem(bt[t / PAGE], h, t % PAGE, ch, H, d);
-                        ((uint16_t *)k_pages)[e] = kb[((size_t)i * H + h) * d + ch];
-                        ((uint16_t *)v_pages)[e] = vb[((size_t)i * H + h) * d + ch];
-                    }
-            }
-        } else if (per_token(fmt)) {
-            /* one (scale, zero) per token, KV head, and K / V */
-            for (int i = 0; i < n; ++i) {
-                int t = start + i;
-                int phys = bt[t / PAGE], slot = t % PAGE;
-                for (int h = 0; h < H; ++h) {
-                    const uint16_t *kr = kb + ((size_t)i * H + h) * d;
-                    const uint16_t *vr = vb + ((size_t)i * H + h) * d;
-                    float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
-                    for (int ch = 0; ch < d; ++ch) {
-                        float kx = half_bits_to_float(kr[ch]), vx = half_bits_to_float(vr[ch]);
-                        if (kx < klo) klo = kx;
-                        if (kx > khi) khi = kx;
-                        if (vx < vlo) vlo = vx;
-                        if (vx > vhi) vhi = vx;
-                    }
-                    float ks, kinv, vs, vinv;
-                    int levels = code_max(fmt);
-                    klo = zero_point(klo);
-                    vlo = zero_point(vlo);
-                    quant_scale_levels(klo, khi, levels, &ks, &kinv);
-                    quant_scale_levels(vlo, vhi, levels, &vs, &vinv);
-                    for (int ch = 0; ch < d; ++ch) {
-                        put_code(fmt, k_pages, phys, h, slot, ch, H, d,
-                                 quant_code_levels(half_bits_to_float(kr[ch]), klo, kinv, levels));
-                        put_code(fmt, v_pages, phys, h, slot, ch, H, d,
-                                 quant_code_levels(half_bits_to_float(vr[ch]), vlo, vinv, levels));
-                    }
-                    float *p = params + (((size_t)phys * H + h) * PAGE + slot) * 4;
-                    p[0] = ks; p[1] = klo; p[2] = vs; p[3] = vlo;
-                }
+                    write_token(kl.fmt, (void *)kl.pages, (void *)vl.pages, (float *)kl.params, kl.idx, h,
+                                t % PAGE, kb + ((size_t)i * H + h) * d, vb + ((size_t)i * H + h) * d, H, d);
             }
         } else if (per_group(fmt)) {
             /* one (scale, zero) per 64-token logical group, KV head, and K / V */
@@ -311,7 +360,7 @@ int kvqo_append(int fmt, int B, int H, int d, int max_pages,
 /* the page's keys ([TS] section 2.1), in fp32 ([TS] section 5.2), over the   */
 /* valid tokens of logical pages page_begin[b] .. P_b-1 (page_begin NULL: 0). */
 /* ------------------------------------------------------------------------- */
-void kvqo_page_meta(int fmt, int B, int H, int d, int max_pages,
+void kvqo_page_meta(int fmt, int n16, int B, int H, int d, int max_pages,
                     const int32_t *block_table, const int32_t *seq_lens, const int32_t *page_begin,
                     const void *k_pages, const float *params, float *meta)
 {
@@ -328,7 +377,7 @@ void kvqo_page_meta(int fmt, int B, int H, int d, int max_pages,
                 for (int ch = 0; ch < d; ++ch) {
                     float lo = INFINITY, hi = -INFINITY;
                     for (int t = t0; t < t1; ++t) {
-                        float k = key_decoded(fmt, k_pages, params, bt, t, h, ch, H, d);
+                        float k = key_decoded(fmt, n16, k_pages, params, bt, t, h, ch, H, d);
                         if (k < lo) lo = k;
                         if (k > hi) hi = k;
                     }
@@ -522,7 +571,7 @@ void kvqo_mask_scores(int B, int H, int max_pages, int group, const int32_t *sel
 /* [TS] section 3.1 phases 3-4), fp64.  sel_pages NULL: all pages.            */
 /* out: [B][Hq][d] double.                                                    */
 /* ------------------------------------------------------------------------- */
-static void attention_unit(int fmt, int b, int g, int Hq, int H, int d, int max_pages,
+static void attention_unit(int fmt, int n16, int b, int g, int Hq, int H, int d, int max_pages,
                            const int32_t *block_table, const int32_t *seq_lens, const uint16_t *q,
                            const void *k_pages, const void *v_pages, const float *params,
                            const int32_t *sel_pages, const int32_t *sel_count, int k_cap,
@@ -550,7 +599,7 @@ static void attention_unit(int fmt, int b, int g, int Hq, int H, int d, int max_
             double dot = 0.0;
             for (int i = 0; i < d; ++i)
                 dot += (double)half_bits_to_float(qh[i]) *
-                       (double)key_decoded(fmt, k_pages, params, bt, tok[u], g, i, H, d);
+                       (double)key_decoded(fmt, n16, k_pages, params, bt, tok[u], g, i, H, d);
             logit[u] = dot * sm_scale;
             if (logit[u] > mu) mu = logit[u];
         }
@@ -560,7 +609,7 @@ static void attention_unit(int fmt, int b, int g, int Hq, int H, int d, int max_
             double w = exp(logit[u] - mu);
             denom += w;
             for (int i = 0; i < d; ++i)
-                o[i] += w * (double)value_decoded(fmt, v_pages, params, bt, tok[u], g, i, H, d);
+                o[i] += w * (double)value_decoded(fmt, n16, v_pages, params, bt, tok[u], g, i, H, d);
         }
         for (int i = 0; i < d; ++i) o[i] = ntok ? o[i] / denom : 0.0;
     }
@@ -568,7 +617,7 @@ static void attention_unit(int fmt, int b, int g, int Hq, int H, int d, int max_
     free(tok);
 }
 
-void kvqo_attention(int fmt, int B, int Hq, int H, int d, int max_pages,
+void kvqo_attention(int fmt, int n16, int B, int Hq, int H, int d, int max_pages,
                     const int32_t *block_table, const int32_t *seq_lens, const uint16_t *q,
                     const void *k_pages, const void *v_pages, const float *params,
                     const int32_t *sel_pages, const int32_t *sel_count, int k_cap,
@@ -576,7 +625,7 @@ void kvqo_attention(int fmt, int B, int Hq, int H, int d, int max_pages,
 {
     for (int b = 0; b < B; ++b)
         for (int g = 0; g < H; ++g)
-            attention_unit(fmt, b, g, Hq, H, d, max_pages, block_table, seq_lens, q, k_pages, v_pages,
+            attention_unit(fmt, n16, b, g, Hq, H, d, max_pages, block_table, seq_lens, q, k_pages, v_pages,
                            params, sel_pages, sel_count, k_cap, sm_scale, out);
 }
 
@@ -588,7 +637,7 @@ void kvqo_attention(int fmt, int B, int Hq, int H, int d, int max_pages,
 /* selected for (b, h / G).  1 when every page is selected.  fp64.            */
 /* out: [B][Hq] double; 0 for an empty sequence.                              */
 /* ------------------------------------------------------------------------- */
-void kvqo_attention_mass(int fmt, int B, int Hq, int H, int d, int max_pages,
+void kvqo_attention_mass(int fmt, int n16, int B, int Hq, int H, int d, int max_pages,
                          const int32_t *block_table, const int32_t *seq_lens, const uint16_t *q,
                          const void *k_pages, const float *params,
                          const int32_t *sel_pages, const int32_t *sel_count, int k_cap,
@@ -614,7 +663,7 @@ void kvqo_attention_mass(int fmt, int B, int Hq, int H, int d, int max_pages,
                 double dot = 0.0;
                 for (int i = 0; i < d; ++i)
                     dot += (double)half_bits_to_float(qh[i]) *
-                           (double)key_decoded(fmt, k_pages, params, bt, t, g, i, H, d);
+                           (double)key_decoded(fmt, n16, k_pages, params, bt, t, g, i, H, d);
                 logit[t] = dot * sm_scale;
                 if (logit[t] > mu) mu = logit[t];
             }
@@ -636,7 +685,7 @@ void kvqo_attention_mass(int fmt, int B, int Hq, int H, int d, int max_pages,
 /* which are independent; nthreads host threads take whole units.             */
 /* scores / sel_pages / sel_count / out are outputs as above.                 */
 /* ------------------------------------------------------------------------- */
-int kvqo_decode_step(int fmt, int B, int Hq, int H, int d, int max_pages,
+int kvqo_decode_step(int fmt, int n16, int B, int Hq, int H, int d, int max_pages,
                      const int32_t *block_table, const int32_t *seq_lens, const uint16_t *q,
                      const void *k_pages, const void *v_pages, const float *params, const float *meta,
                      int ratio_num, int ratio_den, int k_fixed, int k_cap, double sm_scale,
@@ -653,8 +702,47 @@ int kvqo_decode_step(int fmt, int B, int Hq, int H, int d, int max_pages,
         scores_unit(b, g, Hq, H, d, max_pages, block_table, seq_lens, q, meta, scores);
         topk_unit(b, g, H, max_pages, seq_lens, scores, ratio_num, ratio_den, k_fixed, k_cap,
                   sel_pages, sel_count);
-        attention_unit(fmt, b, g, Hq, H, d, max_pages, block_table, seq_lens, q, k_pages, v_pages,
+        attention_unit(fmt, n16, b, g, Hq, H, d, max_pages, block_table, seq_lens, q, k_pages, v_pages,
                        params, sel_pages, sel_count, k_cap, sm_scale, out);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Demotion in a MIXED cache ([TS] section 6: pages that are no longer of     */
+/* high importance leave FP16 for INT8).  Item i moves logical page page[i]   */
+/* of sequence seq[i] from its FP16 page to INT8 page dst[i]: every valid     */
+/* token of the page is quantized per token from its fp16 rows (as an append  */
+/* of those rows to dst would), the block-table entry becomes dst[i], and the */
+/* page's metadata is rebuilt from the new decoded keys.  Slots at or past    */
+/* the sequence's length are not written.  Returns 0, or -1 if an item does   */
+/* not move an FP16 page of the sequence to an INT8 page.                     */
+/* ------------------------------------------------------------------------- */
+int kvqo_demote(int n16, int n_phys, int B, int H, int d, int max_pages, int32_t *block_table,
+                const int32_t *seq_lens, int n, const int32_t *seq, const int32_t *page, const int32_t *dst,
+                void *k_pages, void *v_pages, float *params, float *meta)
+{
+    for (int i = 0; i < n; ++i) {
+        int b = seq[i], j = page[i];
+        if (b < 0 || b >= B || j < 0 || j >= max_pages) return -1;
+        int L = seq_lens[b];
+        int32_t *bt = block_table + (size_t)b * max_pages;
+        int src = bt[j];
+        if (j * PAGE >= L || src < 0 || src >= n16 || dst[i] < n16 || dst[i] >= n_phys) return -1;
+        PageLoc from = locate(FMT_MIXED, n16, k_pages, params, src, H, d);
+        PageLoc kto = locate(FMT_MIXED, n16, k_pages, params, dst[i], H, d);
+        PageLoc vto = locate(FMT_MIXED, n16, v_pages, params, dst[i], H, d);
+        for (int t = j * PAGE; t < (j + 1) * PAGE && t < L; ++t)
+            for (int h = 0; h < H; ++h) {
+                const uint16_t *kr = (const uint16_t *)k_pages + tile_elem(from.idx, h, t % PAGE, 0, H, d);
+                const uint16_t *vr = (const uint16_t *)v_pages + tile_elem(from.idx, h, t % PAGE, 0, H, d);
+                write_token(FMT_INT8_TOKEN, (void *)kto.pages, (void *)vto.pages, (float *)kto.params, kto.idx, h,
+                            t % PAGE, kr, vr, H, d);
+            }
+        bt[j] = dst[i];
+        int32_t begin = j;
+        int32_t lens1 = (j + 1) * PAGE < L ? (j + 1) * PAGE : L;   /* the page's tokens only */
+        kvqo_page_meta(FMT_MIXED, n16, 1, H, d, max_pages, bt, &lens1, &begin, k_pages, params, meta);
     }
     return 0;
 }

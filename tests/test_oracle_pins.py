@@ -1011,3 +1011,167 @@ def test_int4_cache_metadata_scores_and_dense_attention(fmt):
                     p_ = np.exp(lg - lg.max())
                     ref = p_ @ v / p_.sum()
                     assert np.allclose(out[b, g * G + hh], ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------- mixed-precision pages
+def _pools(cache, values=False):
+    """(FP16 pool [n16][H][16][d] fp16 bits, INT8 pool [P-n16][H][16][d]) of a
+    MIXED cache, as views of its one byte array."""
+    raw = cache.v_pages if values else cache.k_pages
+    tile = cache.H * PAGE * cache.d
+    p16 = raw[: cache.n16 * tile * 2].view(np.uint16).reshape(cache.n16, cache.H, PAGE, cache.d)
+    p8 = raw[cache.n16 * tile * 2:].reshape(cache.P_phys - cache.n16, cache.H, PAGE, cache.d)
+    return p16, p8
+
+
+def _decoded_mixed(cache, table, lens, b, g, values=False):
+    """float64 [L][d]: a MIXED cache's keys (values) for (b, g), page by page
+    from the pool the block table points into."""
+    p16, p8 = _pools(cache, values)
+    sz = (2, 3) if values else (0, 1)
+    rows = []
+    for t in range(int(lens[b])):
+        phys, slot = int(table[b, t // PAGE]), t % PAGE
+        if phys < cache.n16:
+            rows.append(p16[phys, g, slot].view(np.float16).astype(np.float64))
+        else:
+            p = cache.params[phys - cache.n16, g, slot]
+            rows.append(np_dequant(p8[phys - cache.n16, g, slot], p[sz[0]], p[sz[1]]).astype(np.float64))
+    return np.array(rows).reshape(int(lens[b]), cache.d)
+
+
+def test_mixed_is_the_splice_of_fp16_and_int8_caches():
+    """A mixed-precision cache holds, page for page, exactly what an fp16 cache
+    (for its FP16-pool pages) or an INT8-per-token cache (for the others) of
+    the same tokens holds: codes, scale/zero bits and metadata."""
+    w = workloads.small(5).with_(fmt=workloads.FMT_MIXED, hot_recent=5)
+    cm, table = oracle.build_cache(w)
+    assert 0 < cm.n16 < cm.P_phys
+    c16, t16 = oracle.build_cache(w.with_(fmt=workloads.FMT_FP16))
+    c8, t8 = oracle.build_cache(w.with_(fmt=workloads.FMT_INT8_TOKEN))
+    p16, p8 = _pools(cm)
+    v16, v8 = _pools(cm, values=True)
+    P = w.pages_per_seq()
+    n_hot = 0
+    for b in range(w.batch):
+        hot = w.hot_pages(b)
+        for j in range(int(P[b])):
+            phys = int(table[b, j])
+            assert (phys < cm.n16) == bool(hot[j])
+            if phys < cm.n16:
+                n_hot += 1
+                assert np.array_equal(p16[phys], c16.k_pages[t16[b, j]])
+                assert np.array_equal(v16[phys], c16.v_pages[t16[b, j]])
+                assert np.array_equal(cm.meta[phys], c16.meta[t16[b, j]])
+            else:
+                i = phys - cm.n16
+                assert np.array_equal(p8[i], c8.k_pages[t8[b, j]]) and np.array_equal(v8[i], c8.v_pages[t8[b, j]])
+                assert np.array_equal(cm.params[i].view(np.uint32), c8.params[t8[b, j]].view(np.uint32))
+                assert np.array_equal(cm.meta[phys], c8.meta[t8[b, j]])
+    assert 0 < n_hot < int(P.sum())
+
+
+def test_mixed_with_one_pool_reduces_to_that_format():
+    """n16 = 0 (every page INT8) stores the bytes, scale/zero and metadata of
+    an INT8-per-token cache; n16 = P (every page FP16) those of an fp16 cache;
+    attention agrees with theirs exactly."""
+    w = workloads.small(4).with_(seq_len=300)
+    table, n_phys = w.with_(fmt=workloads.FMT_INT8_TOKEN).block_table()
+    lens, q = w.seq_lens(), w.query()
+    for fmt, n16 in [(workloads.FMT_INT8_TOKEN, 0), (workloads.FMT_FP16, n_phys)]:
+        ref = oracle.Cache(fmt, n_phys, w.num_kv_heads, w.head_dim)
+        mix = oracle.Cache(workloads.FMT_MIXED, n_phys, w.num_kv_heads, w.head_dim, n16)
+        for c in (ref, mix):
+            for b in range(w.batch):
+                off = np.zeros(w.batch + 1, np.int32)
+                off[b + 1:] = lens[b]
+                oracle.append(c, table, np.zeros(w.batch, np.int32), off, w.keys(b), w.values(b))
+            oracle.page_meta(c, table, lens)
+        assert np.array_equal(mix.k_pages.view(np.uint8), ref.k_pages.reshape(-1).view(np.uint8))
+        assert np.array_equal(mix.v_pages.view(np.uint8), ref.v_pages.reshape(-1).view(np.uint8))
+        if fmt == workloads.FMT_INT8_TOKEN:
+            assert np.array_equal(mix.params.view(np.uint32), ref.params.view(np.uint32))
+        assert np.array_equal(mix.meta, ref.meta)
+        assert np.array_equal(oracle.attention(mix, table, lens, q), oracle.attention(ref, table, lens, q))
+
+
+def test_mixed_metadata_scores_and_attention_by_brute_force():
+    """On a mixed cache: each page's metadata is the min/max of its decoded
+    keys taken from its own pool, its score bounds every token's q.k, and
+    attention over every page equals numpy's dense softmax over those
+    decoded keys and values; over a selection, numpy's softmax restricted to
+    the selected pages' tokens."""
+    w = workloads.small(5).with_(fmt=workloads.FMT_MIXED, hot_recent=5)
+    cache, table = oracle.build_cache(w)
+    lens, q = w.seq_lens(), w.query()
+    sc = oracle.page_scores(cache, table, lens, q)
+    out = oracle.attention(cache, table, lens, q)
+    k_cap = table.shape[1]
+    sel, cnt = oracle.topk(sc, lens, w.ratio_num, w.ratio_den, w.k_fixed, k_cap)
+    out_sel = oracle.attention(cache, table, lens, q, sel, cnt)
+    G = w.group
+    for b in range(w.batch):
+        P = (int(lens[b]) + PAGE - 1) // PAGE
+        for g in range(w.num_kv_heads):
+            k = _decoded_mixed(cache, table, lens, b, g)
+            v = _decoded_mixed(cache, table, lens, b, g, values=True)
+            for j in range(P):
+                kj = k[16 * j:16 * (j + 1)]
+                m = cache.meta[table[b, j], g].astype(np.float64)
+                assert np.array_equal(m[0], kj.min(0)) and np.array_equal(m[1], kj.max(0))
+                for hh in range(G):
+                    qh = q[b, g * G + hh].astype(np.float64)
+                    assert sc[b, g, j] >= (kj @ qh).max() - 1e-9 * (1 + np.abs(sc[b, g, j]))
+            keep = np.zeros(int(lens[b]), bool)
+            for j in sel[b, g, :cnt[b, g]]:
+                keep[16 * j:16 * (j + 1)] = True
+            for hh in range(G):
+                qh = q[b, g * G + hh].astype(np.float64)
+                if not len(k):
+                    continue
+                for o, mask in ((out, np.ones_like(keep)), (out_sel, keep)):
+                    lg = k[mask] @ qh / np.sqrt(w.head_dim)
+                    p_ = np.exp(lg - lg.max())
+                    assert np.allclose(o[b, g * G + hh], p_ @ v[mask] / p_.sum(), rtol=0, atol=1e-12)
+
+
+def test_demote_equals_building_the_page_in_int8():
+    """Demoting FP16 pages of a mixed cache to spare INT8 pages leaves the cache
+    a build with those pages in the INT8 pool from the start would give
+    (codes, scale/zero bits, metadata), points the block table at the new
+    pages, and rejects a page that is not in the FP16 pool."""
+    w = workloads.small(5).with_(fmt=workloads.FMT_MIXED, hot_recent=5, spare_pages=6)
+    cache, table = oracle.build_cache(w)
+    lens = w.seq_lens()
+    P = w.pages_per_seq()
+    # the first page of three sequences and the last page of one (partial)
+    picks = [(b, 0) for b in range(3) if P[b] > 0] + [(3, int(P[3]) - 1)]
+    seq = [b for b, _ in picks]
+    page = [j for _, j in picks]
+    dst = list(range(cache.P_phys - len(picks), cache.P_phys))
+    t2 = table.copy()
+    before16 = _pools(cache)[0].copy()
+    oracle.demote(cache, t2, lens, seq, page, dst)
+    for (b, j), dd in zip(picks, dst):
+        assert t2[b, j] == dd
+    assert np.array_equal(np.delete(t2.reshape(-1), [b * t2.shape[1] + j for b, j in picks]),
+                          np.delete(table.reshape(-1), [b * table.shape[1] + j for b, j in picks]))
+    # the same tokens built with those pages in the INT8 pool from the start
+    ref = oracle.Cache(workloads.FMT_MIXED, cache.P_phys, w.num_kv_heads, w.head_dim, cache.n16)
+    for b in range(w.batch):
+        off = np.zeros(w.batch + 1, np.int32)
+        off[b + 1:] = lens[b]
+        oracle.append(ref, t2, np.zeros(w.batch, np.int32), off, w.keys(b), w.values(b))
+    oracle.page_meta(ref, t2, lens)
+    r8 = _pools(ref)[1]
+    c16, c8 = _pools(cache)
+    for dd in dst:
+        i = dd - cache.n16
+        assert np.array_equal(c8[i], r8[i]) and np.array_equal(_pools(cache, True)[1][i], _pools(ref, True)[1][i])
+        assert np.array_equal(cache.params[i].view(np.uint32), ref.params[i].view(np.uint32))
+        assert np.array_equal(cache.meta[dd], ref.meta[dd])
+    assert np.array_equal(c16, before16)   # the FP16 pool (the old pages too) is left as it was
+    q = w.query()
+    assert np.array_equal(oracle.attention(cache, t2, lens, q), oracle.attention(ref, t2, lens, q))
+    with pytest.raises(ValueError):   # that page is in the INT8 pool now
+        oracle.demote(cache, t2, lens, [seq[0]], [page[0]], [dst[0]])

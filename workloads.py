@@ -18,7 +18,10 @@ Workload shapes follow the decode workloads named on the pages:
     section 2);
   * 16-token pages (pzsr.cn page, section 2 layout C; TinyServe page, section
     5.1 config), INT8 per-token (pzsr.cn page, section 2) or per-64-token-group
-    (uyd888.cn page, chapter 1) storage.
+    (uyd888.cn page, chapter 1) storage, 4-bit codes (intelliparadigm.com
+    page, section 3.2), or mixed precision (TinyServe page, section 6: pages
+    of high importance FP16, the rest INT8; here the first page and the most
+    recent hot_recent pages of each sequence are the FP16 ones).
 The pages evaluate on trained models and on PG19; no weights or dataset exist
 here, so N(0, 1) activations with the stated outlier structure stand in.
 """
@@ -36,8 +39,9 @@ FMT_INT8_TOKEN = 1
 FMT_INT8_GROUP64 = 2
 FMT_INT4_TOKEN = 3
 FMT_INT4_GROUP64 = 4
+FMT_MIXED = 5
 FORMAT_NAMES = {FMT_FP16: "fp16", FMT_INT8_TOKEN: "int8_token", FMT_INT8_GROUP64: "int8_group64",
-                FMT_INT4_TOKEN: "int4_token", FMT_INT4_GROUP64: "int4_group64"}
+                FMT_INT4_TOKEN: "int4_token", FMT_INT4_GROUP64: "int4_group64", FMT_MIXED: "mixed_fp16_int8"}
 
 # stream ids: one numpy stream per (stream, index)
 _S_LENS, _S_Q, _S_K, _S_V, _S_OUT, _S_TABLE = 0, 1, 2, 3, 4, 5
@@ -70,8 +74,12 @@ class Workload:
     outlier_channels: int = 0
     outlier_lo: float = 1.0
     outlier_hi: float = 1.0
-    # extra physical pages beyond the ones the block table uses
+    # extra physical pages beyond the ones the block table uses (in the INT8
+    # pool of a mixed-precision cache)
     spare_pages: int = 0
+    # mixed precision: FP16 pages per sequence besides its first page (its
+    # last hot_recent pages)
+    hot_recent: int = 64
 
     @property
     def group(self) -> int:
@@ -95,6 +103,23 @@ class Workload:
     def max_pages(self) -> int:
         return int(self.pages_per_seq().max())
 
+    def hot_pages(self, b: int) -> np.ndarray:
+        """bool [P_b]: the pages of sequence b kept in FP16 by a mixed-precision
+        cache (its first page and its last hot_recent pages)."""
+        P = int(self.pages_per_seq()[b])
+        hot = np.zeros(P, dtype=bool)
+        if self.fmt == FMT_MIXED and P:
+            hot[0] = True
+            hot[max(P - self.hot_recent, 0):] = True
+        return hot
+
+    def fp16_pool_pages(self) -> int:
+        """Physical pages 0 .. n16-1 form the FP16 pool of a mixed-precision
+        cache (0 for every other format)."""
+        if self.fmt != FMT_MIXED:
+            return 0
+        return int(sum(int(self.hot_pages(b).sum()) for b in range(self.batch)))
+
     def block_table(self) -> tuple[np.ndarray, int]:
         """(int32 [B][max_pages], number of physical pages).
 
@@ -103,6 +128,22 @@ class Workload:
         """
         pages = self.pages_per_seq()
         total = int(pages.sum())
+        if self.fmt == FMT_MIXED:   # hot pages from the FP16 pool, the others from the INT8 pool
+            n16 = self.fp16_pool_pages()
+            ids16, ids8 = np.arange(n16, dtype=np.int32), np.arange(n16, total, dtype=np.int32)
+            if self.table == "perm":
+                rng = self._rng(_S_TABLE)
+                ids16, ids8 = rng.permutation(ids16), rng.permutation(ids8)
+            table = np.full((self.batch, self.max_pages()), -1, dtype=np.int32)
+            o16 = o8 = 0
+            for b, p in enumerate(pages):
+                hot = self.hot_pages(b)
+                for j in range(int(p)):
+                    if hot[j]:
+                        table[b, j], o16 = ids16[o16], o16 + 1
+                    else:
+                        table[b, j], o8 = ids8[o8], o8 + 1
+            return table, total + self.spare_pages
         if self.table == "identity":
             phys = np.arange(total, dtype=np.int32)
         elif self.table == "perm":
