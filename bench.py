@@ -44,23 +44,41 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 
 
-def algorithmic_bytes(w, k_per_row):
+def algorithmic_bytes(w, k_per_row, n_fp16_tiles=0):
     """(metadata bytes of every page, selected KV bytes): each (page, KV head)
     counted once; a quantized tile carries its codes (a byte per channel, or
-    half a byte for 4-bit codes) and its fp32 scale/zero."""
+    half a byte for 4-bit codes) and its fp32 scale/zero.  A mixed-precision
+    cache's selected tiles are INT8 per token except n_fp16_tiles fp16 ones."""
     import workloads
     d = w.head_dim
     pages = w.pages_per_seq().astype(np.int64)
     meta = int(pages.sum()) * w.num_kv_heads * 8 * d
     int4 = w.fmt in (workloads.FMT_INT4_TOKEN, workloads.FMT_INT4_GROUP64)
     codes = 2 * 16 * (d // 2 if int4 else d)
+    fp16_tile = 2 * 16 * d * 2
     if w.fmt == workloads.FMT_FP16:
-        tile = 2 * 16 * d * 2
-    elif w.fmt in (workloads.FMT_INT8_TOKEN, workloads.FMT_INT4_TOKEN):
+        tile = fp16_tile
+    elif w.fmt in (workloads.FMT_INT8_TOKEN, workloads.FMT_INT4_TOKEN, workloads.FMT_MIXED):
         tile = codes + 16 * 16
     else:
         tile = codes + 16
-    return meta, int(np.asarray(k_per_row, np.int64).sum()) * tile
+    n = int(np.asarray(k_per_row, np.int64).sum())
+    return meta, (n - n_fp16_tiles) * tile + n_fp16_tiles * fp16_tile
+
+
+def fp16_tiles(w, table, sel, cnt):
+    """Selected (page, KV head) tiles of a mixed-precision cache that lie in its
+    FP16 pool (sel None: every page)."""
+    n16 = w.fp16_pool_pages()
+    if not n16:
+        return 0
+    P = w.pages_per_seq()
+    tot = 0
+    for b in range(w.batch):
+        for g in range(w.num_kv_heads):
+            pages = np.arange(P[b]) if sel is None else sel[b, g, :cnt[b, g]]
+            tot += int((table[b, pages] < n16).sum())
+    return tot
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_attn_cfg4_traffic.json")
@@ -265,7 +283,7 @@ def main() -> int:
     src = functools.lru_cache(maxsize=None)(lambda b: (w.keys(b), w.values(b)))
     print(f"[bench] building {w.name} ...", file=sys.stderr, flush=True)
     base, seqs = runtime.build_cache(w.fmt, n_phys, w.num_kv_heads, w.head_dim, table, lens, src,
-                                     prefill_lens=lens - 1, device=dev)
+                                     prefill_lens=lens - 1, device=dev, num_fp16_pages=w.fp16_pool_pages())
     stream = torch.cuda.current_stream()
 
     def events():
@@ -299,7 +317,7 @@ def main() -> int:
         layers.append(kvq.PagedCache(base.format, base.num_phys_pages, base.num_kv_heads, base.head_dim,
                                      base.k_pages.clone(), base.v_pages.clone(),
                                      None if base.kv_params is None else base.kv_params.clone(),
-                                     base.page_meta.clone()))
+                                     base.page_meta.clone(), base.num_fp16_pages))
     q = torch.from_numpy(w.query().view(np.int16)).to(dev)
     dense = w.is_dense()
     appends = [runtime.DecodeAppend(c, seqs, lens, src, device=dev) for c in layers]
@@ -440,7 +458,8 @@ def main() -> int:
     torch.cuda.synchronize()
 
     counts = st0.sel_count.cpu().numpy() if not dense else np.tile(w.pages_per_seq()[:, None], (1, w.num_kv_heads))
-    meta_b, kv_b = algorithmic_bytes(w, counts)
+    n16_tiles = fp16_tiles(w, table, None if dense else st0.sel_pages.cpu().numpy(), counts)
+    meta_b, kv_b = algorithmic_bytes(w, counts, n16_tiles)
     if hiers is not None:  # boxes of every super-page, then the kept super-pages' pages
         h0 = hiers[0]
         P = w.pages_per_seq().astype(np.int64)
@@ -495,7 +514,7 @@ def main() -> int:
         flat_bytes = step_bytes
         t_cpu, reps, res = cpu_baseline(w, args.cpu_seconds, threads, built)
         if hiers is not None:
-            flat_bytes = sum(algorithmic_bytes(w, res[2]))
+            flat_bytes = sum(algorithmic_bytes(w, res[2], fp16_tiles(w, table, res[1], res[2])))
         cpu = {"value": round(flat_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": f"full decode step (scores, top-K, attention) of this workload on {threads} threads "
                          f"({cpu_model()}), median of {reps} runs, {t_cpu * 1e3:.1f} ms each"
@@ -540,7 +559,9 @@ def main() -> int:
                    "one_launch_step": bool(st0.fused_step),
                    "coarse_then_fine": None if hiers is None else {"group_pages": hiers[0].group,
                                                                    "kept_per_row": hiers[0].kc}},
-        "bytes_per_step": {"metadata": meta_b if not dense else 0, "selected_kv": kv_b},
+        "bytes_per_step": {"metadata": meta_b if not dense else 0, "selected_kv": kv_b,
+                           **({"selected_fp16_tiles": n16_tiles, "fp16_pool_pages": w.fp16_pool_pages()}
+                              if w.fmt == workloads.FMT_MIXED else {})},
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4),

@@ -9,7 +9,9 @@
  *     page_size 16);
  *   - storage as fp16, INT8 per token (same pzsr.cn page, section 2: each
  *     token's vector quantized with its own min/max) or INT8 per 64-token group
- *     ("Gemini KV cache: FlashAttention-3 adaptation", uyd888.cn, chapter 1);
+ *     ("Gemini KV cache: FlashAttention-3 adaptation", uyd888.cn, chapter 1),
+ *     4-bit codes, or mixed precision (FP16 for the pages of high importance,
+ *     INT8 for the rest: "TinyServe", section 6);
  *   - per-page fp32 metadata phi(K_j) = (per-channel min, per-channel max) of
  *     the page's keys, page score r = sum_i (q_i >= 0 ? q_i M_i : q_i m_i),
  *     top-K page selection, attention over the selected pages only
@@ -43,6 +45,15 @@
  *                      *_GROUP64: [P_phys][H_kv][4] fp32, the 64-token
  *                                 group's values repeated in each of its pages
  *                      KVQ_FP16 : unused (may be NULL)
+ *   KVQ_MIXED_FP16_INT8: physical pages 0 .. n16-1 (n16 = num_fp16_pages) are
+ *                      the FP16 pool and pages n16 .. P_phys-1 the INT8-per-token
+ *                      pool.  k_pages (v_pages) is one array: the FP16 pool
+ *                      [n16][H_kv][16][d] fp16 bits, then, at byte
+ *                      n16 * H_kv * 16 * d * 2, the INT8 pool [P_phys-n16][H_kv][16][d];
+ *                      kv_params is [P_phys-n16][H_kv][16][4] for the INT8 pool
+ *                      (its page p - n16).  Which pages are important is the
+ *                      caller's choice: it allocates them from the FP16 pool and
+ *                      moves them later with kvq_demote_pages.
  *   page_meta          [P_phys][H_kv][2][d] fp32: row 0 per-channel min, row 1 max
  * A stored key or value decodes to fmaf(code, scale, zero) (INT8) or to the
  * fp16 value (FP16).  Codes are unsigned 0..255 (INT8) or 0..15 (INT4, the
@@ -61,7 +72,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 6
+#define KVQ_ABI_VERSION 7
 #define KVQ_PAGE_SIZE 16
 #define KVQ_SELECT_MAX_PAGES 2048 /* longest row (pages) kvq_select_decode_attn takes */
 
@@ -78,7 +89,8 @@ typedef enum {
     KVQ_INT8_TOKEN = 1,
     KVQ_INT8_GROUP64 = 2,
     KVQ_INT4_TOKEN = 3,    /* 4-bit codes, head_dim 128 only */
-    KVQ_INT4_GROUP64 = 4   /* 4-bit codes, head_dim 128 only */
+    KVQ_INT4_GROUP64 = 4,  /* 4-bit codes, head_dim 128 only */
+    KVQ_MIXED_FP16_INT8 = 5 /* FP16 pool + INT8-per-token pool (layout above) */
 } kvq_format;
 
 /* Non-owning view of one layer's paged cache (host struct, device pointers). */
@@ -92,6 +104,7 @@ typedef struct {
     void *v_pages;
     float *kv_params;
     float *page_meta;
+    int32_t num_fp16_pages;    /* KVQ_MIXED_FP16_INT8: n16, 0 <= n16 <= P_phys; otherwise ignored */
 } kvq_cache;
 
 /* The batch of sequences (host struct, device pointers). */
@@ -161,6 +174,27 @@ kvq_status kvq_append_decode(const kvq_cache *cache, const kvq_seqs *seqs,
  */
 kvq_status kvq_build_page_meta(const kvq_cache *cache, const kvq_seqs *seqs,
                                const int32_t *page_begin, int32_t max_span, void *stream);
+
+/*
+ * kvq_demote_pages -- a mixed-precision cache moves pages out of its FP16
+ * pool ("TinyServe", section 6: high-importance pages stay FP16, the rest
+ * are INT8; a page that is no longer important leaves FP16).  Item i moves
+ * logical page page[i] of sequence seq[i] from its FP16-pool page to
+ * INT8-pool page dst[i]: every valid token of the page (t < L_b) is quantized
+ * per token from its fp16 rows, exactly as kvq_append_quant writes an INT8
+ * page; the page's metadata is rebuilt from the new decoded keys (as
+ * kvq_build_page_meta); and block_table[seq[i]][page[i]] becomes dst[i]
+ * (the block table is written: seqs->block_table must point to writable
+ * memory).  Slots at or past L_b are not written; the old FP16 page is left
+ * as it was, for the caller to reuse.
+ * seq, page, dst: [n] int32 device arrays.  Preconditions (not checked):
+ * each item's page is below ceil(L_b / 16) and lives in the FP16 pool, each
+ * dst lies in the INT8 pool, and no two items name the same page or the same
+ * dst.  Only KVQ_MIXED_FP16_INT8 (else KVQ_ERR_UNSUPPORTED); n = 0 enqueues
+ * nothing.
+ */
+kvq_status kvq_demote_pages(const kvq_cache *cache, const kvq_seqs *seqs, int32_t n, const int32_t *seq,
+                            const int32_t *page, const int32_t *dst, void *stream);
 
 /*
  * kvq_page_scores -- page relevance of every logical page ("TinyServe",

@@ -24,7 +24,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
-KVQ_FP16, KVQ_INT8_TOKEN, KVQ_INT8_GROUP64, KVQ_INT4_TOKEN, KVQ_INT4_GROUP64 = 0, 1, 2, 3, 4
+KVQ_FP16, KVQ_INT8_TOKEN, KVQ_INT8_GROUP64, KVQ_INT4_TOKEN, KVQ_INT4_GROUP64, KVQ_MIXED_FP16_INT8 = 0, 1, 2, 3, 4, 5
 PAGE_SIZE = 16
 SELECT_MAX_PAGES = 2048  # KVQ_SELECT_MAX_PAGES: longest row kvq_select_decode_attn takes
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
@@ -41,7 +41,7 @@ class CacheStruct(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("num_phys_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
-                ("kv_params", ctypes.c_void_p), ("page_meta", ctypes.c_void_p)]
+                ("kv_params", ctypes.c_void_p), ("page_meta", ctypes.c_void_p), ("num_fp16_pages", ctypes.c_int32)]
 
 
 class SeqsStruct(ctypes.Structure):
@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_size_t, P]
         L.kvq_build_coarse_meta.argtypes = [C, S, I, P, P, P, P, P]
         L.kvq_page_scores_masked.argtypes = [C, S, P, I, I, P, P, I, P, P]
+        L.kvq_demote_pages.argtypes = [C, S, I, P, P, P, P]
         L.kvq_step_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.kvq_step_workspace_bytes.restype = ctypes.c_size_t
         L.kvq_step_counter_bytes.argtypes = [I, I]
@@ -82,7 +83,7 @@ def lib() -> ctypes.CDLL:
         for f in ("kvq_append_quant", "kvq_append_decode", "kvq_append_decode_scores", "kvq_build_page_meta",
                   "kvq_page_scores", "kvq_topk_pages", "kvq_sparse_decode_attn", "kvq_select_decode_attn",
                   "kvq_select_decode_attn_noalloc", "kvq_decode_step", "kvq_build_coarse_meta",
-                  "kvq_page_scores_masked"):
+                  "kvq_page_scores_masked", "kvq_demote_pages"):
             getattr(L, f).restype = ctypes.c_int
         L.kvq_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
         L.kvq_read_probe.restype = ctypes.c_int
@@ -128,7 +129,10 @@ def _check(fn: str, status: int) -> None:
 # ----------------------------------------------------------- device views
 @dataclass
 class PagedCache:
-    """One layer's paged cache in device memory (layout of include/kvq.h)."""
+    """One layer's paged cache in device memory (layout of include/kvq.h).
+    KVQ_MIXED_FP16_INT8: k_pages / v_pages are one byte array each (the FP16
+    pool of num_fp16_pages pages, then the INT8 pool), kv_params the INT8
+    pool's."""
 
     format: int
     num_phys_pages: int
@@ -138,27 +142,39 @@ class PagedCache:
     v_pages: torch.Tensor
     kv_params: torch.Tensor | None
     page_meta: torch.Tensor
+    num_fp16_pages: int = 0
 
     @staticmethod
-    def empty(fmt: int, num_phys_pages: int, num_kv_heads: int, head_dim: int, device="cuda") -> "PagedCache":
+    def empty(fmt: int, num_phys_pages: int, num_kv_heads: int, head_dim: int, device="cuda",
+              num_fp16_pages: int = 0) -> "PagedCache":
         # 4-bit codes: two channels per byte, so a token row is head_dim / 2 bytes
         row = head_dim // 2 if fmt in (KVQ_INT4_TOKEN, KVQ_INT4_GROUP64) else head_dim
         shape = (num_phys_pages, num_kv_heads, PAGE_SIZE, row)
         dt = torch.int16 if fmt == KVQ_FP16 else torch.uint8
+        n16 = num_fp16_pages if fmt == KVQ_MIXED_FP16_INT8 else 0
+        if fmt == KVQ_MIXED_FP16_INT8:
+            if not 0 <= n16 <= num_phys_pages:
+                raise ValueError("num_fp16_pages must lie in [0, num_phys_pages]")
+            tile = num_kv_heads * PAGE_SIZE * head_dim
+            shape = (n16 * tile * 2 + (num_phys_pages - n16) * tile,)
         k = torch.zeros(shape, dtype=dt, device=device)
         v = torch.zeros(shape, dtype=dt, device=device)
-        if fmt in (KVQ_INT8_TOKEN, KVQ_INT4_TOKEN):
+        if fmt == KVQ_MIXED_FP16_INT8:
+            p = torch.zeros((max(num_phys_pages - n16, 1), num_kv_heads, PAGE_SIZE, 4), dtype=torch.float32,
+                            device=device)
+        elif fmt in (KVQ_INT8_TOKEN, KVQ_INT4_TOKEN):
             p = torch.zeros((num_phys_pages, num_kv_heads, PAGE_SIZE, 4), dtype=torch.float32, device=device)
         elif fmt in (KVQ_INT8_GROUP64, KVQ_INT4_GROUP64):
             p = torch.zeros((num_phys_pages, num_kv_heads, 4), dtype=torch.float32, device=device)
         else:
             p = None
         meta = torch.zeros((num_phys_pages, num_kv_heads, 2, head_dim), dtype=torch.float32, device=device)
-        return PagedCache(fmt, num_phys_pages, num_kv_heads, head_dim, k, v, p, meta)
+        return PagedCache(fmt, num_phys_pages, num_kv_heads, head_dim, k, v, p, meta, n16)
 
     def struct(self) -> CacheStruct:
         return CacheStruct(self.format, self.num_phys_pages, PAGE_SIZE, self.num_kv_heads, self.head_dim,
-                           _ptr(self.k_pages), _ptr(self.v_pages), _ptr(self.kv_params), _ptr(self.page_meta))
+                           _ptr(self.k_pages), _ptr(self.v_pages), _ptr(self.kv_params), _ptr(self.page_meta),
+                           self.num_fp16_pages)
 
 
 @dataclass
@@ -222,6 +238,18 @@ def kvq_append_decode_scores(cache: PagedCache, seqs: Seqs, start_pos, new_off, 
 def kvq_build_page_meta(cache: PagedCache, seqs: Seqs, page_begin=None, max_span: int = 0, stream=None) -> None:
     _check("kvq_build_page_meta", lib().kvq_build_page_meta(
         ctypes.byref(cache.struct()), ctypes.byref(seqs.struct()), _ptr(page_begin), int(max_span),
+        _stream(stream)))
+
+
+def kvq_demote_pages(cache: PagedCache, seqs: Seqs, seq, page, dst, stream=None) -> None:
+    """Move logical page page[i] of sequence seq[i] from the FP16 pool to
+    INT8-pool page dst[i] (int32 device tensors of one length); rewrites
+    seqs.block_table in place."""
+    n = int(seq.numel())
+    if int(page.numel()) != n or int(dst.numel()) != n:
+        raise ValueError("seq, page and dst must have one length")
+    _check("kvq_demote_pages", lib().kvq_demote_pages(
+        ctypes.byref(cache.struct()), ctypes.byref(seqs.struct()), n, _ptr(seq), _ptr(page), _ptr(dst),
         _stream(stream)))
 
 

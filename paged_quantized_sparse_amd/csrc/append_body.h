@@ -40,6 +40,7 @@ struct AppendView {
   const uint16_t* v_new;
   int H;
   int max_pages;
+  int n16;  // mixed precision: physical pages below n16 are the FP16 pool
 };
 
 // One token row's codes, NB bytes per lane (lane l holding bytes NB l ..
@@ -60,6 +61,149 @@ __device__ __forceinline__ void store_row_dev(uint8_t* row, uint32_t bits) {
   }
 }
 
+// One touched page j of sequence b, KV head h, stored in format PF at index
+// idx of the arrays kpool / vpool / params: its older tokens decoded and its
+// new rows written (rows r0 .. r0+n-1 hold tokens start .. start+n-1), each
+// decoded key folded into lo / hi (lane l: channels l*E .. l*E+E-1).  gk, gv,
+// ginv: the group's (scale, zero) and 1/scale for the per-group formats.
+template <int PF, int D, bool WT>
+__device__ __forceinline__ void append_page(const AppendView& a, void* kpool, void* vpool, float* params, int idx,
+                                            int j, int h, int start, int n, int r0, const float* gk,
+                                            const float* gv, const float* ginv, float* lo, float* hi) {
+  constexpr int E = D / 64;
+  constexpr int BITS = fmt_int4(PF) ? 4 : 8;
+  constexpr int LV = fmt_levels(PF);
+  constexpr int CROW = D * BITS / 8;  // bytes of one token's codes
+  const int lane = lane_id();
+  {
+    const size_t tile = ((size_t)idx * a.H + h) * kPage;  // first token row of the page
+    const int t_begin = max(start, j * kPage), t_end = min(start + n, (j + 1) * kPage);
+
+    // older tokens of the page (only the first touched page has any): all 16
+    // slots are loaded at once and the slots at or past `start` masked out,
+    // so no load waits on another
+    const int nold = t_begin - j * kPage;
+    if (nold > 0) {  // wave-uniform
+      float kold[kPage][E];
+#pragma unroll
+      for (int t = 0; t < kPage; ++t) {
+        const size_t row = (tile + t) * D + lane * E;
+        if constexpr (PF == kFp16) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) kold[t][e] = half_bits_to_float(((const uint16_t*)kpool)[row + e]);
+        } else {
+          const float* p = fmt_token(PF) ? params + (tile + t) * 4 : params + ((size_t)idx * a.H + h) * 4;
+          const float s = p[0], z = p[1];
+          const uint8_t* cp = (const uint8_t*)kpool + (tile + t) * CROW + lane * E * BITS / 8;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const uint32_t c = fmt_int4(PF) ? (cp[0] >> (4 * e)) & 0xFu : cp[e];
+            kold[t][e] = __builtin_fmaf((float)c, s, z);
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kPage; ++t)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          lo[e] = fminf(lo[e], t < nold ? kold[t][e] : INFINITY);
+          hi[e] = fmaxf(hi[e], t < nold ? kold[t][e] : -INFINITY);
+        }
+    }
+
+    // the page's new rows
+    for (int t = t_begin; t < t_end; ++t) {
+      const size_t src = ((size_t)(r0 + t - start) * a.H + h) * D + lane * E;
+      const size_t dst = (tile + t % kPage) * D + lane * E;
+      float kdec[E];
+      if constexpr (PF == kFp16) {
+        uint32_t kw = 0, vw = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint16_t kb = a.k_new[src + e];
+          const uint16_t vb = a.v_new[src + e];
+          if constexpr (WT) {
+            kw |= (uint32_t)kb << (16 * e);
+            vw |= (uint32_t)vb << (16 * e);
+          } else {
+            ((uint16_t*)kpool)[dst + e] = kb;
+            ((uint16_t*)vpool)[dst + e] = vb;
+          }
+          kdec[e] = half_bits_to_float(kb);
+        }
+        if constexpr (WT) {
+          const size_t row = (tile + t % kPage) * D * 2;
+          store_row_dev<2 * E>((uint8_t*)kpool + row, kw);
+          store_row_dev<2 * E>((uint8_t*)vpool + row, vw);
+        }
+      } else {
+        float kx[E], vx[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          kx[e] = half_bits_to_float(a.k_new[src + e]);
+          vx[e] = half_bits_to_float(a.v_new[src + e]);
+        }
+        float ks = gk[0], kz = gk[1], kinv = ginv[0], vs = gv[0], vz = gv[1], vinv = ginv[1];
+        if constexpr (fmt_token(PF)) {
+          float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            klo = fminf(klo, kx[e]); khi = fmaxf(khi, kx[e]);
+            vlo = fminf(vlo, vx[e]); vhi = fmaxf(vhi, vx[e]);
+          }
+          klo = zero_point(min_contig<64>(klo)); khi = max_contig<64>(khi);
+          vlo = zero_point(min_contig<64>(vlo)); vhi = max_contig<64>(vhi);
+          quant_params<LV>(klo, khi, ks, kinv);
+          quant_params<LV>(vlo, vhi, vs, vinv);
+          kz = klo;
+          vz = vlo;
+          if (lane == 0) {
+            float* tp = params + (tile + t % kPage) * 4;
+            if constexpr (WT) {
+              store_f<true>(tp, ks);
+              store_f<true>(tp + 1, kz);
+              store_f<true>(tp + 2, vs);
+              store_f<true>(tp + 3, vz);
+            } else {
+              *(float4*)tp = make_float4(ks, kz, vs, vz);
+            }
+          }
+        }
+        uint32_t kw = 0, vw = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint32_t kc = quant_code<LV>(kx[e], kz, kinv);
+          const uint32_t vc = quant_code<LV>(vx[e], vz, vinv);
+          kw |= kc << (BITS * e);
+          vw |= vc << (BITS * e);
+          kdec[e] = __builtin_fmaf((float)kc, ks, kz);
+        }
+        const size_t row = (tile + t % kPage) * CROW;
+        if constexpr (WT) {
+          store_row_dev<E * BITS / 8>((uint8_t*)kpool + row, kw);
+          store_row_dev<E * BITS / 8>((uint8_t*)vpool + row, vw);
+        } else {
+          uint8_t* kp = (uint8_t*)kpool + row + lane * (E * BITS / 8);
+          uint8_t* vp = (uint8_t*)vpool + row + lane * (E * BITS / 8);
+          if constexpr (E * BITS / 8 == 2) {
+            *(uint16_t*)kp = (uint16_t)kw;
+            *(uint16_t*)vp = (uint16_t)vw;
+          } else {
+            *kp = (uint8_t)kw;
+            *vp = (uint8_t)vw;
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        lo[e] = fminf(lo[e], kdec[e]);
+        hi[e] = fmaxf(hi[e], kdec[e]);
+      }
+    }
+
+  }
+}
+
 // WT: every store is a device-scope (written-through) store, for readers in
 // other blocks of the same launch (the fused decode step); otherwise the
 // stores are ordinary.
@@ -67,9 +211,7 @@ template <int FMT, int D, bool WT = false>
 __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b, int h,
                                                      float (*sm_meta)[2][D]) {
   constexpr int E = D / 64;
-  constexpr int BITS = fmt_int4(FMT) ? 4 : 8;
   constexpr int LV = fmt_levels(FMT);
-  constexpr int CROW = D * BITS / 8;  // bytes of one token's codes
   static_assert(!fmt_int4(FMT) || E == 2, "4-bit rows are built for head_dim 128");
   // at most 64 rows (the documented limit; clamping keeps every index in range)
   const int r0 = a.new_off[b], n = min(a.new_off[b + 1] - r0, 64);
@@ -120,132 +262,20 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
   for (int pi = w; pi < npages; pi += 4) {  // wave-uniform
     const int j = j_lo + pi;
     const int phys = bt[j];
-    const size_t tile = ((size_t)phys * a.H + h) * kPage;  // first token row of the page
-    const int t_begin = max(start, j * kPage), t_end = min(start + n, (j + 1) * kPage);
     float lo[E], hi[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) { lo[e] = INFINITY; hi[e] = -INFINITY; }
-
-    // older tokens of the page (only the first touched page has any): all 16
-    // slots are loaded at once and the slots at or past `start` masked out,
-    // so no load waits on another
-    const int nold = t_begin - j * kPage;
-    if (nold > 0) {  // wave-uniform
-      float kold[kPage][E];
-#pragma unroll
-      for (int t = 0; t < kPage; ++t) {
-        const size_t row = (tile + t) * D + lane * E;
-        if constexpr (FMT == kFp16) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) kold[t][e] = half_bits_to_float(((const uint16_t*)a.k_pages)[row + e]);
-        } else {
-          const float* p = fmt_token(FMT) ? a.params + (tile + t) * 4 : a.params + ((size_t)phys * a.H + h) * 4;
-          const float s = p[0], z = p[1];
-          const uint8_t* cp = (const uint8_t*)a.k_pages + (tile + t) * CROW + lane * E * BITS / 8;
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const uint32_t c = fmt_int4(FMT) ? (cp[0] >> (4 * e)) & 0xFu : cp[e];
-            kold[t][e] = __builtin_fmaf((float)c, s, z);
-          }
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < kPage; ++t)
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          lo[e] = fminf(lo[e], t < nold ? kold[t][e] : INFINITY);
-          hi[e] = fmaxf(hi[e], t < nold ? kold[t][e] : -INFINITY);
-        }
-    }
-
-    // the page's new rows
-    for (int t = t_begin; t < t_end; ++t) {
-      const size_t src = ((size_t)(r0 + t - start) * a.H + h) * D + lane * E;
-      const size_t dst = (tile + t % kPage) * D + lane * E;
-      float kdec[E];
-      if constexpr (FMT == kFp16) {
-        uint32_t kw = 0, vw = 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const uint16_t kb = a.k_new[src + e];
-          const uint16_t vb = a.v_new[src + e];
-          if constexpr (WT) {
-            kw |= (uint32_t)kb << (16 * e);
-            vw |= (uint32_t)vb << (16 * e);
-          } else {
-            ((uint16_t*)a.k_pages)[dst + e] = kb;
-            ((uint16_t*)a.v_pages)[dst + e] = vb;
-          }
-          kdec[e] = half_bits_to_float(kb);
-        }
-        if constexpr (WT) {
-          const size_t row = (tile + t % kPage) * D * 2;
-          store_row_dev<2 * E>((uint8_t*)a.k_pages + row, kw);
-          store_row_dev<2 * E>((uint8_t*)a.v_pages + row, vw);
-        }
+    if constexpr (FMT == kMixed) {  // the page's pool decides its format
+      if (phys < a.n16) {
+        append_page<kFp16, D, WT>(a, a.k_pages, a.v_pages, a.params, phys, j, h, start, n, r0, gk, gv, ginv, lo,
+                                  hi);
       } else {
-        float kx[E], vx[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          kx[e] = half_bits_to_float(a.k_new[src + e]);
-          vx[e] = half_bits_to_float(a.v_new[src + e]);
-        }
-        float ks = gk[0], kz = gk[1], kinv = ginv[0], vs = gv[0], vz = gv[1], vinv = ginv[1];
-        if constexpr (fmt_token(FMT)) {
-          float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            klo = fminf(klo, kx[e]); khi = fmaxf(khi, kx[e]);
-            vlo = fminf(vlo, vx[e]); vhi = fmaxf(vhi, vx[e]);
-          }
-          klo = zero_point(min_contig<64>(klo)); khi = max_contig<64>(khi);
-          vlo = zero_point(min_contig<64>(vlo)); vhi = max_contig<64>(vhi);
-          quant_params<LV>(klo, khi, ks, kinv);
-          quant_params<LV>(vlo, vhi, vs, vinv);
-          kz = klo;
-          vz = vlo;
-          if (lane == 0) {
-            float* tp = a.params + (tile + t % kPage) * 4;
-            if constexpr (WT) {
-              store_f<true>(tp, ks);
-              store_f<true>(tp + 1, kz);
-              store_f<true>(tp + 2, vs);
-              store_f<true>(tp + 3, vz);
-            } else {
-              *(float4*)tp = make_float4(ks, kz, vs, vz);
-            }
-          }
-        }
-        uint32_t kw = 0, vw = 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const uint32_t kc = quant_code<LV>(kx[e], kz, kinv);
-          const uint32_t vc = quant_code<LV>(vx[e], vz, vinv);
-          kw |= kc << (BITS * e);
-          vw |= vc << (BITS * e);
-          kdec[e] = __builtin_fmaf((float)kc, ks, kz);
-        }
-        const size_t row = (tile + t % kPage) * CROW;
-        if constexpr (WT) {
-          store_row_dev<E * BITS / 8>((uint8_t*)a.k_pages + row, kw);
-          store_row_dev<E * BITS / 8>((uint8_t*)a.v_pages + row, vw);
-        } else {
-          uint8_t* kp = (uint8_t*)a.k_pages + row + lane * (E * BITS / 8);
-          uint8_t* vp = (uint8_t*)a.v_pages + row + lane * (E * BITS / 8);
-          if constexpr (E * BITS / 8 == 2) {
-            *(uint16_t*)kp = (uint16_t)kw;
-            *(uint16_t*)vp = (uint16_t)vw;
-          } else {
-            *kp = (uint8_t)kw;
-            *vp = (uint8_t)vw;
-          }
-        }
+        const size_t off = (size_t)a.n16 * a.H * kPage * D * 2;
+        append_page<kInt8Token, D, WT>(a, (char*)a.k_pages + off, (char*)a.v_pages + off, a.params, phys - a.n16,
+                                       j, h, start, n, r0, gk, gv, ginv, lo, hi);
       }
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        lo[e] = fminf(lo[e], kdec[e]);
-        hi[e] = fmaxf(hi[e], kdec[e]);
-      }
+    } else {
+      append_page<FMT, D, WT>(a, a.k_pages, a.v_pages, a.params, phys, j, h, start, n, r0, gk, gv, ginv, lo, hi);
     }
 
     // the page's metadata: min row then max row

@@ -30,12 +30,13 @@ hipError_t launch_append_decode(const kvq_cache& c, const kvq_seqs& s, const int
                                 const int32_t* new_off, const uint16_t* k_new, const uint16_t* v_new,
                                 hipStream_t st) {
   AppendView a{c.k_pages, c.v_pages, c.kv_params, c.page_meta, s.block_table, start_pos, new_off,
-               k_new, v_new, c.num_kv_heads, s.max_pages};
+               k_new, v_new, c.num_kv_heads, s.max_pages, fp16_pool(c)};
   dim3 grid(c.num_kv_heads, s.batch);
   if (c.format == KVQ_FP16) return launch_fmt<kFp16>(a, c.head_dim, grid, st);
   if (c.format == KVQ_INT8_TOKEN) return launch_fmt<kInt8Token>(a, c.head_dim, grid, st);
   if (c.format == KVQ_INT8_GROUP64) return launch_fmt<kInt8Group>(a, c.head_dim, grid, st);
   if (c.format == KVQ_INT4_TOKEN) return launch_fmt<kInt4Token>(a, c.head_dim, grid, st);
+  if (c.format == KVQ_MIXED_FP16_INT8) return launch_fmt<kMixed>(a, c.head_dim, grid, st);
   return launch_fmt<kInt4Group>(a, c.head_dim, grid, st);
 }
 

@@ -28,6 +28,7 @@ struct AppendArgs {
   const uint16_t* v_new;
   int H;
   int max_pages;
+  int n16;  // mixed precision: physical pages below n16 are the FP16 pool
 };
 
 // ---------------------------------------------------------------- fp16 copy
@@ -53,8 +54,10 @@ __global__ __launch_bounds__(256) void append_fp16_kernel(AppendArgs a) {
   }
 }
 
-// ------------------------------------------------- INT8 / INT4 per token
+// ----------------------------------------- INT8 / INT4 per token, mixed
 // One wave per (token, KV head); 4 waves per block; grid (ceil(max_new*H/4), B).
+// A mixed-precision cache copies the row into an FP16-pool page and
+// quantizes it per token into an INT8-pool page.
 template <int FMT, int D>
 __global__ __launch_bounds__(256) void append_token_kernel(AppendArgs a) {
   constexpr int E = D / 64;  // elements per lane
@@ -67,8 +70,23 @@ __global__ __launch_bounds__(256) void append_token_kernel(AppendArgs a) {
   if (i >= n) return;
   const int lane = lane_id();
   const int t = a.start_pos[b] + i;
-  const int phys = a.block_table[(size_t)b * a.max_pages + t / kPage];
+  int phys = a.block_table[(size_t)b * a.max_pages + t / kPage];
   const size_t src = ((size_t)(r0 + i) * a.H + h) * D + lane * E;
+  if constexpr (FMT == kMixed) {
+    if (phys < a.n16) {  // wave-uniform: an fp16 copy
+      const size_t dst16 = (((size_t)phys * a.H + h) * kPage + t % kPage) * D + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        ((uint16_t*)a.k_pages)[dst16 + e] = a.k_new[src + e];
+        ((uint16_t*)a.v_pages)[dst16 + e] = a.v_new[src + e];
+      }
+      return;
+    }
+    const size_t off = (size_t)a.n16 * a.H * kPage * D * 2;  // the INT8 pool
+    a.k_pages = (char*)a.k_pages + off;
+    a.v_pages = (char*)a.v_pages + off;
+    phys -= a.n16;
+  }
   const size_t dst = (((size_t)phys * a.H + h) * kPage + t % kPage) * D + lane * E;
   float kx[E], vx[E];
   float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
@@ -178,6 +196,7 @@ hipError_t launch_append_d(const kvq_cache& c, const kvq_seqs& s, const AppendAr
     case KVQ_INT4_TOKEN:
       if constexpr (D == 128) hipLaunchKernelGGL((append_token_kernel<kInt4Token, D>), token_grid, dim3(256), 0, st, a);
       break;
+    case KVQ_MIXED_FP16_INT8: hipLaunchKernelGGL((append_token_kernel<kMixed, D>), token_grid, dim3(256), 0, st, a); break;
     default:
       if constexpr (D == 128) hipLaunchKernelGGL((append_group_kernel<kInt4Group, D>), group_grid, dim3(256), 0, st, a);
       break;
@@ -192,7 +211,7 @@ hipError_t launch_append(const kvq_cache& c, const kvq_seqs& s, const int32_t* s
                          const uint16_t* v_new, hipStream_t st) {
   if (max_new == 0) return hipSuccess;
   AppendArgs a{c.k_pages, c.v_pages, c.kv_params, s.block_table, start_pos, new_off, k_new, v_new,
-               c.num_kv_heads, s.max_pages};
+               c.num_kv_heads, s.max_pages, fp16_pool(c)};
   return c.head_dim == 64 ? launch_append_d<64>(c, s, a, max_new, st)
                           : launch_append_d<128>(c, s, a, max_new, st);
 }

@@ -109,7 +109,7 @@ hipError_t launch_append_scores(const kvq_cache& c, const kvq_seqs& s, const int
                                 const int32_t* new_off, const uint16_t* k_new, const uint16_t* v_new,
                                 const uint16_t* q, int num_q_heads, float* scores, hipStream_t st) {
   AppendScoreArgs a{{c.k_pages, c.v_pages, c.kv_params, c.page_meta, s.block_table, start_pos, new_off, k_new,
-                     v_new, c.num_kv_heads, s.max_pages},
+                     v_new, c.num_kv_heads, s.max_pages, fp16_pool(c)},
                     {c.page_meta, s.block_table, q, scores, c.num_kv_heads, num_q_heads, s.max_pages},
                     s.seq_lens};
   const int rows = s.batch * c.num_kv_heads;
@@ -118,6 +118,7 @@ hipError_t launch_append_scores(const kvq_cache& c, const kvq_seqs& s, const int
   if (c.format == KVQ_INT8_TOKEN) return launch_d<kInt8Token>(a, c.head_dim, rows, G, st);
   if (c.format == KVQ_INT8_GROUP64) return launch_d<kInt8Group>(a, c.head_dim, rows, G, st);
   if (c.format == KVQ_INT4_TOKEN) return launch_d<kInt4Token>(a, c.head_dim, rows, G, st);
+  if (c.format == KVQ_MIXED_FP16_INT8) return launch_d<kMixed>(a, c.head_dim, rows, G, st);
   return launch_d<kInt4Group>(a, c.head_dim, rows, G, st);
 }
 

@@ -72,7 +72,37 @@ struct AttnArgs {
   int pps;  // pages per split
   int max_splits;
   float scale_log2;  // sm_scale * log2(e)
+  int n16;           // mixed precision: physical pages below n16 are the FP16 pool
 };
+
+// The per-wave partials a block merges: NWS slots of (m, l) and acc per head.
+template <int G, int D, int NWS>
+struct WaveParts {
+  float ml[NWS][G][2];
+  float acc[NWS][G][D];
+};
+
+template <int G, int D, int NWS>
+__device__ __forceinline__ WaveParts<G, D, NWS>* wave_parts() {
+  __shared__ WaveParts<G, D, NWS> parts;
+  return &parts;
+}
+
+// Mixed-precision pages, one phase per pool: of the first `valid` lanes (one
+// page each), keep those whose physical page lies in phase PH's pool (1: the
+// FP16 pool, pages below n16; 2: the INT8 pool), packed in order into the low
+// lanes, with the INT8 pool's pages renumbered from 0.  Returns their count.
+template <int PH>
+__device__ __forceinline__ int pool_filter(int& jlog, int& phys, int valid, int n16) {
+  const bool keep = lane_id() < valid && ((phys < n16) == (PH == 1));
+  const uint64_t mask = __ballot(keep);
+  const int cnt = __popcll(mask);
+  // a dropped lane sends to lane 63, which is unused unless every lane is kept
+  const int to = keep ? lanes_below(mask) : kWave - 1;
+  jlog = __builtin_amdgcn_ds_permute(4 * to, jlog);
+  phys = __builtin_amdgcn_ds_permute(4 * to, phys) - (PH == 2 ? n16 : 0);
+  return cnt;
+}
 
 template <int FMT, int D>
 struct Tile {
@@ -267,7 +297,12 @@ __device__ __forceinline__ void combine_one(const AttnArgs& a, int bh) {
 // `list` (LDS, pps entries).  COH: the row's scores are read, and the partials
 // written, at device scope (the fused step kernel, where other blocks of the
 // same launch wrote the scores and merge the partials).
-template <int FMT, int D, int G, int NW, bool SEL, bool COH>
+// PH: 0 for a single-format cache.  A mixed-precision cache runs two phases
+// over the same split: PH 1 (FMT = fp16) attends to the split's FP16-pool
+// pages and leaves its waves' partials in LDS; PH 2 (FMT = INT8 per token)
+// reuses the selection, attends to the INT8-pool pages, and merges all 2 NW
+// wave partials into the split's partial.
+template <int FMT, int D, int G, int NW, bool SEL, bool COH, int PH = 0>
 __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, int s, int* list) {
   static_assert(NW == 4, "the split merge and the combine assume 4 waves");
   using T = Tile<FMT, D>;
@@ -294,7 +329,11 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
   const bool sparse = !SEL && a.sel_pages != nullptr;
   const int idx0 = first + w + lane * NW;
   SelPrefetch<NW * 64> pre;
-  if constexpr (SEL) pre.template load<COH>(a.scores + (size_t)row * a.max_pages, a.max_pages);
+  if constexpr (SEL && PH != 2) pre.template load<COH>(a.scores + (size_t)row * a.max_pages, a.max_pages);
+  // the tiles of a mixed cache's INT8 pool start after its FP16 pool
+  const size_t pool_off = PH == 2 ? (size_t)a.n16 * a.H * kPage * D * 2 : 0;
+  const char* const k_base = (const char*)a.k_pages + pool_off;
+  const char* const v_base = (const char*)a.v_pages + pool_off;
   const int slot_raw = SEL      ? 0
                        : sparse ? vload_i32(a.sel_pages, (size_t)row * a.k_cap + min(idx0, a.k_cap - 1))
                                 : vload_i32(a.block_table, (size_t)b * a.max_pages + min(idx0, a.max_pages - 1));
@@ -365,7 +404,7 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
   const int cnt = __builtin_amdgcn_readfirstlane(cnt_v);
   const int Pc = (cnt + kPage - 1) / kPage;
   const int K = SEL ? num_selected(Pc, a.rnum, a.rden, a.k_fixed) : (sparse ? cnt : Pc);
-  if constexpr (SEL) {  // the selection's count and padding, once per row
+  if constexpr (SEL && PH != 2) {  // the selection's count and padding, once per row
     if (s == 0 && a.sel_out) {
       if (threadIdx.x == 0) a.cnt_out[row] = K;
       for (int i = K + threadIdx.x; i < a.k_cap; i += NW * 64) a.sel_out[(size_t)row * a.k_cap + i] = -1;
@@ -378,14 +417,16 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
     __shared__ int sm_hist[2 * kSelBins];
     __shared__ int sm_wtot[2 * NW];
     __shared__ uint32_t sm_wrange[2 * NW];
-    if (K < P) {
-      select_chunk<NW>(pre, P, K, first, n, SelShared{sm_hist, sm_wtot, sm_wrange}, list);
-    } else {
-      for (int i = threadIdx.x; i < n; i += NW * 64) list[i] = first + i;
-      __syncthreads();
+    if constexpr (PH != 2) {  // (the second phase of a mixed cache reuses the first one's list)
+      if (K < P) {
+        select_chunk<NW>(pre, P, K, first, n, SelShared{sm_hist, sm_wtot, sm_wrange}, list);
+      } else {
+        for (int i = threadIdx.x; i < n; i += NW * 64) list[i] = first + i;
+        __syncthreads();
+      }
+      if (a.sel_out)
+        for (int i = threadIdx.x; i < n; i += NW * 64) a.sel_out[(size_t)row * a.k_cap + first + i] = list[i];
     }
-    if (a.sel_out)
-      for (int i = threadIdx.x; i < n; i += NW * 64) a.sel_out[(size_t)row * a.k_cap + first + i] = list[i];
     jlog0 = list[min(w + lane * NW, n - 1)];
   } else {
     jlog0 = sparse ? min(max(slot_raw, 0), a.max_pages - 1) : min(idx0, a.max_pages - 1);
@@ -426,8 +467,8 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
     const size_t tile = ((size_t)ph * a.H + g) * tile_elems;
     if constexpr (MF) {
       // K: token l%16, run (D/4)(l/16); V: token 4(l/16) + l%4, run (D/4)((l/4)%4)
-      const char* kp = (const char*)a.k_pages + tile + (lane & 15) * D + (D / 4) * (lane >> 4);
-      const char* vp = (const char*)a.v_pages + tile + (4 * (lane >> 4) + (lane & 3)) * D + (D / 4) * ((lane >> 2) & 3);
+      const char* kp = k_base + tile + (lane & 15) * D + (D / 4) * (lane >> 4);
+      const char* vp = v_base + tile + (4 * (lane >> 4) + (lane & 3)) * D + (D / 4) * ((lane >> 2) & 3);
       // Each of these loads covers half of every 128-byte row of the tile (the
       // other half comes with the next), so they are ordinary loads, which keep
       // the line in L2 for its second half (64 ragged sequences, 8 KV heads in
@@ -450,8 +491,8 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const size_t off = (tile + (size_t)(i * TPL + tg) * D + ch0) * T::BITS / 8;
-      r.kr[i] = load_raw<NWD>((const char*)a.k_pages + off);
-      r.vr[i] = load_raw<NWD>((const char*)a.v_pages + off);
+      r.kr[i] = load_raw<NWD>(k_base + off);
+      r.vr[i] = load_raw<NWD>(v_base + off);
       if constexpr (fmt_token(FMT))
         r.pr[i] = load_stream_f4(a.params + ((size_t)ph * a.H + g) * (kPage * 4) + (i * TPL + tg) * 4);
     }
@@ -666,7 +707,11 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
         jlog_v = sparse ? min(max(a.sel_pages[(size_t)row * a.k_cap + idx], 0), a.max_pages - 1) : idx;
       phys_v = a.block_table[(size_t)b * a.max_pages + jlog_v];
     }
-    const int cnt = min(64, nw - k0);
+    int cnt = min(64, nw - k0);
+    if constexpr (PH != 0) {  // this phase's pool only
+      cnt = pool_filter<PH>(jlog_v, phys_v, cnt, a.n16);
+      if (cnt == 0) continue;  // wave-uniform
+    }
     // Software pipeline over a ring of R = PF + 1 register tiles: the loads of
     // tiles k+1 .. k+PF are in flight while tile k is consumed.
     // Every load is unconditional (an index past the chunk re-reads its last
@@ -708,8 +753,11 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
   }
 
   // ---- merge the block's waves through LDS and write the split's partials
-  __shared__ float sm_ml[NW][G][2];
-  __shared__ float sm_acc[NW][G][D];
+  // (a mixed cache's phases fill slots [0, NW) and [NW, 2 NW))
+  constexpr int NWS = PH == 0 ? NW : 2 * NW;
+  WaveParts<G, D, NWS>* const parts = wave_parts<G, D, NWS>();
+  float(*const sm_ml)[G][2] = parts->ml + (PH == 2 ? NW : 0);
+  float(*const sm_acc)[G][D] = parts->acc + (PH == 2 ? NW : 0);
   if constexpr (MF) {
     // (l, z) of head lane%16 summed over its four lanes; O[h][c] = acc + z,
     // lane l register i holding head 4(l/16) + i at channel
@@ -743,19 +791,20 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       }
     }
   }
+  if constexpr (PH == 1) return;  // the second phase merges
   __syncthreads();
   for (int e = threadIdx.x; e < G * D; e += NW * 64) {
     const int hh = e / D, c = e % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) M = fmaxf(M, sm_ml[v][hh][0]);
+    for (int v = 0; v < NWS; ++v) M = fmaxf(M, parts->ml[v][hh][0]);
     float sa = 0.0f, sl = 0.0f;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      const float mv = sm_ml[v][hh][0];
+    for (int v = 0; v < NWS; ++v) {
+      const float mv = parts->ml[v][hh][0];
       const float f = mv == -INFINITY ? 0.0f : exp2f(mv - M);  // 0 for a wave without pages
-      sa = __builtin_fmaf(f, sm_acc[v][hh][c], sa);
-      sl = __builtin_fmaf(f, sm_ml[v][hh][1], sl);
+      sa = __builtin_fmaf(f, parts->acc[v][hh][c], sa);
+      sl = __builtin_fmaf(f, parts->ml[v][hh][1], sl);
     }
     const size_t prow = ((size_t)b * a.Hq + g * G + hh) * a.max_splits + s;
     store_f<COH>(a.part_acc + prow * D + c, sa);

@@ -20,10 +20,17 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
 // ragged batch's full first splits go out first and its shorter last splits
 // last, and all splits of a head share the XCD of block id mod 8.  The SEL
 // instance's dynamic LDS holds the block's pages (pps entries).
+// A mixed-precision cache attends to each split's FP16-pool pages, then its
+// INT8-pool pages, and merges the two (attend_split phases 1 and 2).
 template <int FMT, int D, int G, int NW, bool SEL>
 __global__ __launch_bounds__(NW * 64) void decode_attn_kernel(AttnArgs a) {
   extern __shared__ int sm_dyn[];
-  attend_split<FMT, D, G, NW, SEL, false>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm_dyn);
+  if constexpr (FMT == kMixed) {
+    attend_split<kFp16, D, G, NW, SEL, false, 1>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm_dyn);
+    attend_split<kInt8Token, D, G, NW, SEL, false, 2>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm_dyn);
+  } else {
+    attend_split<FMT, D, G, NW, SEL, false>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm_dyn);
+  }
 }
 
 // Room for dynamic LDS a launch of the SEL kernel has under the device's
@@ -123,12 +130,13 @@ hipError_t launch_decode_attn(const kvq_cache& c, const kvq_seqs& s, const uint1
              ks ? ks->scores : nullptr, ks ? ks->sel_out : nullptr, ks ? ks->cnt_out : nullptr,
              ks ? ks->rnum : 0, ks ? ks->rden : 1, ks ? ks->k_fixed : 0,
              part_acc, part_ml, out, c.num_kv_heads, num_q_heads, s.max_pages, k_cap,
-             pages_per_split, max_splits, sm_scale * 1.4426950408889634f};
+             pages_per_split, max_splits, sm_scale * 1.4426950408889634f, fp16_pool(c)};
   const int G = num_q_heads / c.num_kv_heads;
   if (c.format == KVQ_FP16) return run_d<kFp16>(a, s.batch, c.head_dim, G, st);
   if (c.format == KVQ_INT8_TOKEN) return run_d<kInt8Token>(a, s.batch, c.head_dim, G, st);
   if (c.format == KVQ_INT8_GROUP64) return run_d<kInt8Group>(a, s.batch, c.head_dim, G, st);
   if (c.format == KVQ_INT4_TOKEN) return run_d<kInt4Token>(a, s.batch, c.head_dim, G, st);
+  if (c.format == KVQ_MIXED_FP16_INT8) return run_d<kMixed>(a, s.batch, c.head_dim, G, st);
   return run_d<kInt4Group>(a, s.batch, c.head_dim, G, st);
 }
 

@@ -15,10 +15,12 @@ kvq_status check_cache(const kvq_cache* c, bool need_meta) {
   if (!c) return KVQ_ERR_INVALID_ARG;
   if (c->page_size != KVQ_PAGE_SIZE) return KVQ_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
-  if (c->format < KVQ_FP16 || c->format > KVQ_INT4_GROUP64) return KVQ_ERR_UNSUPPORTED;
+  if (c->format < KVQ_FP16 || c->format > KVQ_MIXED_FP16_INT8) return KVQ_ERR_UNSUPPORTED;
   if ((c->format == KVQ_INT4_TOKEN || c->format == KVQ_INT4_GROUP64) && c->head_dim != 128)
     return KVQ_ERR_UNSUPPORTED;
   if (c->num_kv_heads < 1 || c->num_kv_heads > 65535 || c->num_phys_pages < 1) return KVQ_ERR_INVALID_ARG;
+  if (c->format == KVQ_MIXED_FP16_INT8 && (c->num_fp16_pages < 0 || c->num_fp16_pages > c->num_phys_pages))
+    return KVQ_ERR_INVALID_ARG;
   if (!c->k_pages || !c->v_pages || !aligned16(c->k_pages) || !aligned16(c->v_pages)) return KVQ_ERR_INVALID_ARG;
   if (c->format != KVQ_FP16 && (!c->kv_params || !aligned16(c->kv_params))) return KVQ_ERR_INVALID_ARG;
   if (need_meta && (!c->page_meta || !aligned16(c->page_meta))) return KVQ_ERR_INVALID_ARG;
@@ -140,6 +142,18 @@ kvq_status kvq_build_page_meta(const kvq_cache* cache, const kvq_seqs* seqs, con
   if ((st = check_seqs(seqs)) != KVQ_OK) return st;
   if (max_span < 0) return KVQ_ERR_INVALID_ARG;
   return from_hip(kvq::launch_page_meta(*cache, *seqs, page_begin, max_span, (hipStream_t)stream));
+}
+
+kvq_status kvq_demote_pages(const kvq_cache* cache, const kvq_seqs* seqs, int32_t n, const int32_t* seq,
+                            const int32_t* page, const int32_t* dst, void* stream) {
+  kvq_status st = check_cache(cache, true);
+  if (st != KVQ_OK) return st;
+  if ((st = check_seqs(seqs)) != KVQ_OK) return st;
+  if (cache->format != KVQ_MIXED_FP16_INT8) return KVQ_ERR_UNSUPPORTED;
+  if (n < 0) return KVQ_ERR_INVALID_ARG;
+  if (n == 0) return KVQ_OK;
+  if (!seq || !page || !dst) return KVQ_ERR_INVALID_ARG;
+  return from_hip(kvq::launch_demote(*cache, *seqs, n, seq, page, dst, (hipStream_t)stream));
 }
 
 kvq_status kvq_page_scores(const kvq_cache* cache, const kvq_seqs* seqs, const uint16_t* q,
@@ -294,7 +308,8 @@ kvq_status kvq_decode_step(const kvq_cache* cache, const kvq_seqs* seqs, const i
   if (!(sm_scale == sm_scale)) return KVQ_ERR_INVALID_ARG;
   if (pages_per_split < 0 || pages_per_split > 4096) return KVQ_ERR_INVALID_ARG;
   if (seqs->max_pages > kvq::kSelMaxPages || seqs->batch > kvq::kStepMaxSeqs) return KVQ_ERR_UNSUPPORTED;
-  if (cache->format == KVQ_INT4_TOKEN || cache->format == KVQ_INT4_GROUP64) return KVQ_ERR_UNSUPPORTED;
+  if (cache->format != KVQ_FP16 && cache->format != KVQ_INT8_TOKEN && cache->format != KVQ_INT8_GROUP64)
+    return KVQ_ERR_UNSUPPORTED;
   if (k_cap < kvq::num_selected(seqs->max_pages, ratio_num, ratio_den, k_fixed)) return KVQ_ERR_INVALID_ARG;
   const int32_t pps = pages_per_split ? pages_per_split
                                       : kvq_default_pages_per_split(seqs->batch, cache->num_kv_heads,

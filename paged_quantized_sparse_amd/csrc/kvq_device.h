@@ -14,7 +14,8 @@ namespace kvq {
 constexpr int kPage = 16;
 constexpr int kWave = 64;
 
-enum Format : int { kFp16 = 0, kInt8Token = 1, kInt8Group = 2, kInt4Token = 3, kInt4Group = 4 };
+// kMixed: an FP16 pool of pages and an INT8-per-token pool in one cache.
+enum Format : int { kFp16 = 0, kInt8Token = 1, kInt8Group = 2, kInt4Token = 3, kInt4Group = 4, kMixed = 5 };
 
 // One (scale, zero) per token slot, or per 64-token group; 4-bit codes (two
 // per byte, channel 2i in the low nibble of byte i); the largest code.

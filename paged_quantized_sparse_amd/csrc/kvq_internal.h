@@ -30,9 +30,15 @@ long long per_device(std::atomic<long long> (&memo)[kMaxDevices], F compute) {
   return v - 1;
 }
 
+// The FP16 pool size of a mixed-precision cache (its physical pages below
+// this are FP16); 0 for every other format.
+inline int fp16_pool(const kvq_cache& c) { return c.format == KVQ_MIXED_FP16_INT8 ? c.num_fp16_pages : 0; }
+
 hipError_t launch_append(const kvq_cache& c, const kvq_seqs& s, const int32_t* start_pos,
                          const int32_t* new_off, int max_new, const uint16_t* k_new,
                          const uint16_t* v_new, hipStream_t st);
+hipError_t launch_demote(const kvq_cache& c, const kvq_seqs& s, int n, const int32_t* seq, const int32_t* page,
+                         const int32_t* dst, hipStream_t st);
 
 hipError_t launch_append_decode(const kvq_cache& c, const kvq_seqs& s, const int32_t* start_pos,
                                 const int32_t* new_off, const uint16_t* k_new, const uint16_t* v_new,

@@ -60,11 +60,12 @@ def append_rows(cache: PagedCache, seqs: Seqs, rows: dict[int, tuple[int, np.nda
 
 def build_cache(fmt: int, num_phys_pages: int, num_kv_heads: int, head_dim: int, block_table: np.ndarray,
                 seq_lens: np.ndarray, source: KVSource, prefill_lens: np.ndarray | None = None,
-                device="cuda", rows_per_call: int = 1 << 20) -> tuple[PagedCache, Seqs]:
+                device="cuda", rows_per_call: int = 1 << 20, num_fp16_pages: int = 0) -> tuple[PagedCache, Seqs]:
     """Allocate a cache and prefill sequence b with its first prefill_lens[b]
     tokens (default: all) from source(b), then build every page's metadata.
-    Uploads are batched to about rows_per_call tokens per append call."""
-    cache = PagedCache.empty(fmt, num_phys_pages, num_kv_heads, head_dim, device)
+    Uploads are batched to about rows_per_call tokens per append call.
+    num_fp16_pages: the FP16 pool of a mixed-precision cache."""
+    cache = PagedCache.empty(fmt, num_phys_pages, num_kv_heads, head_dim, device, num_fp16_pages)
     seqs = Seqs(_dev_i32(seq_lens, device), _dev_i32(block_table, device))
     pre = np.asarray(seq_lens if prefill_lens is None else prefill_lens, np.int64)
     batch: dict[int, tuple[int, np.ndarray, np.ndarray]] = {}

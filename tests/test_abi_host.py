@@ -58,8 +58,8 @@ def test_library_never_allocates_or_synchronizes():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == 6
-    assert "#define KVQ_ABI_VERSION 6" in open(HEADER).read()
+    assert lib.kvq_abi_version() == 7
+    assert "#define KVQ_ABI_VERSION 7" in open(HEADER).read()
     for s, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP"), (99, b"unknown")]:
         assert word in lib.kvq_status_string(s)
 
@@ -137,6 +137,29 @@ def test_stage_argument_errors(lib):
     assert lib.kvq_topk_pages(FAKE, ctypes.byref(s), 4, 3, 10, -1, 8, FAKE, FAKE, None) == INVALID
     _, s_long = _structs(maxp=20000)
     assert lib.kvq_topk_pages(FAKE, ctypes.byref(s_long), 4, 3, 10, 0, 8000, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def test_mixed_precision_argument_errors(lib):
+    """A mixed-precision cache needs 0 <= num_fp16_pages <= P_phys; demotion
+    takes only that format, a non-negative count and its three arrays; a
+    count of 0 enqueues nothing."""
+    for n16 in (-1, 65):   # P_phys is 64
+        c, s = _structs(fmt=5)
+        c.num_fp16_pages = n16
+        assert lib.kvq_build_page_meta(ctypes.byref(c), ctypes.byref(s), None, 0, None) == INVALID
+        assert lib.kvq_demote_pages(ctypes.byref(c), ctypes.byref(s), 1, FAKE, FAKE, FAKE, None) == INVALID
+    c, s = _structs(fmt=1)
+    assert lib.kvq_demote_pages(ctypes.byref(c), ctypes.byref(s), 1, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    c, s = _structs(fmt=5)
+    c.num_fp16_pages = 16
+    assert lib.kvq_demote_pages(ctypes.byref(c), ctypes.byref(s), -1, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.kvq_demote_pages(ctypes.byref(c), ctypes.byref(s), 2, FAKE, None, FAKE, None) == INVALID
+    assert lib.kvq_demote_pages(ctypes.byref(c), ctypes.byref(s), 0, None, None, None, None) == 0
+    # the one-launch step takes fp16 and INT8 storage only
+    for fmt in (3, 5):
+        c, s = _structs(fmt=fmt)
+        assert lib.kvq_decode_step(ctypes.byref(c), ctypes.byref(s), FAKE, FAKE, 1, FAKE, FAKE, FAKE, 4, FAKE,
+                                   3, 10, 0, 8, FAKE, FAKE, 0.1, 0, FAKE, None, 1 << 30, None) == UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

@@ -60,7 +60,8 @@ class Built:
         log(f"[build] {w.name} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
             f"fmt={workloads.FORMAT_NAMES[w.fmt]} pages={self.n_phys}")
         self.cache, self.seqs = runtime.build_cache(w.fmt, self.n_phys, w.num_kv_heads, w.head_dim, self.table,
-                                                    self.lens, src, prefill_lens=self.lens - 1)
+                                                    self.lens, src, prefill_lens=self.lens - 1,
+                                                    num_fp16_pages=w.fp16_pool_pages())
         runtime.DecodeAppend(self.cache, self.seqs, self.lens, src).run()
         torch.cuda.synchronize()
         self.q = w.query()
