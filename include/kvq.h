@@ -283,7 +283,9 @@ kvq_status kvq_topk_pages(const float *scores, const kvq_seqs *seqs, int32_t num
  * ids, any order, no repeats), or over every page when sel_pages is NULL
  * (sel_count is then ignored).  Computed split-K: each split of
  * pages_per_split selected pages keeps an online (max, sum, acc) in fp32, and
- * a second kernel merges the splits with log-sum-exp weights.  For a query
+ * a second kernel merges the splits with log-sum-exp weights (when no row
+ * has more than one split, the split kernel writes out itself and no merge
+ * runs; the output is the same bit for bit).  For a query
  * group (G = 2, 4, 8) over an INT8 cache the products run on the matrix cores:
  * q.k as fp16 x fp16 with fp32 accumulation, p.v with the weights split into
  * three bf16 parts (~2^-21 relative) against exact bf16 codes, fp32

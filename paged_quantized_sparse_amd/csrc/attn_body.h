@@ -73,6 +73,7 @@ struct AttnArgs {
   int max_splits;
   float scale_log2;  // sm_scale * log2(e)
   int n16;           // mixed precision: physical pages below n16 are the FP16 pool
+  int direct;        // every row has at most one split: its block writes out, no combine follows
 };
 
 // The per-wave partials a block merges: NWS slots of (m, l) and acc per head.
@@ -410,7 +411,12 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       for (int i = K + threadIdx.x; i < a.k_cap; i += NW * 64) a.sel_out[(size_t)row * a.k_cap + i] = -1;
     }
   }
-  if (first >= K) return;
+  if (first >= K) {
+    // with one split per row and no combine, split 0 writes an empty row's zeros
+    if (!COH && PH != 1 && a.direct && s == 0)
+      for (int e = threadIdx.x; e < G * D; e += NW * 64) a.out[((size_t)b * a.Hq + g * G + e / D) * D + e % D] = 0.0f;
+    return;
+  }
   const int n = min(a.pps, K - first);
   int jlog0;
   if constexpr (SEL) {  // list: this block's pages, ascending
@@ -805,6 +811,10 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       const float f = mv == -INFINITY ? 0.0f : exp2f(mv - M);  // 0 for a wave without pages
       sa = __builtin_fmaf(f, parts->acc[v][hh][c], sa);
       sl = __builtin_fmaf(f, parts->ml[v][hh][1], sl);
+    }
+    if (!COH && a.direct) {  // the row's only split: out = acc / l, as the combine would write it
+      a.out[((size_t)b * a.Hq + g * G + hh) * D + c] = sl > 0.0f ? sa / sl : 0.0f;
+      continue;
     }
     const size_t prow = ((size_t)b * a.Hq + g * G + hh) * a.max_splits + s;
     store_f<COH>(a.part_acc + prow * D + c, sa);

@@ -64,7 +64,7 @@ hipError_t run(const AttnArgs& a, int B, hipStream_t st) {
     hipLaunchKernelGGL((decode_attn_kernel<FMT, D, G, kAttnWaves, false>), grid, dim3(kAttnWaves * 64), 0, st, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.direct) return e;  // (one split per row: the split kernel wrote out)
   hipLaunchKernelGGL((combine_kernel<D, G>), dim3(B * a.Hq), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -130,7 +130,7 @@ hipError_t launch_decode_attn(const kvq_cache& c, const kvq_seqs& s, const uint1
              ks ? ks->scores : nullptr, ks ? ks->sel_out : nullptr, ks ? ks->cnt_out : nullptr,
              ks ? ks->rnum : 0, ks ? ks->rden : 1, ks ? ks->k_fixed : 0,
              part_acc, part_ml, out, c.num_kv_heads, num_q_heads, s.max_pages, k_cap,
-             pages_per_split, max_splits, sm_scale * 1.4426950408889634f, fp16_pool(c)};
+             pages_per_split, max_splits, sm_scale * 1.4426950408889634f, fp16_pool(c), max_splits == 1};
   const int G = num_q_heads / c.num_kv_heads;
   if (c.format == KVQ_FP16) return run_d<kFp16>(a, s.batch, c.head_dim, G, st);
   if (c.format == KVQ_INT8_TOKEN) return run_d<kInt8Token>(a, s.batch, c.head_dim, G, st);

@@ -386,6 +386,41 @@ def test_empty_sequences_in_batch(fused):
     assert np.abs(out - want).max() <= ATTN_ATOL
 
 
+@pytest.mark.parametrize("n,fmt", [(5, 2), (5, 1), (4, 0), (1, 0)], ids=["gqa_int8grp", "gqa_int8tok", "mha_fp16",
+                                                                       "config1"])
+def test_one_split_per_row_writes_out_without_combine(n, fmt):
+    """When no row has more than one split the split kernel writes out itself:
+    the output equals, bit for bit, the split-then-combine result over the same
+    single live split (forced by a selection stride of two splits), empty rows
+    are zero (out prefilled with NaN), and it matches the oracle."""
+    kvq, runtime = kvq_mod()
+    w = workloads.small(n).with_(fmt=fmt)
+    bt = built(("one_split", n, fmt), w)
+    lens = bt.lens.copy()
+    if w.batch > 3:
+        lens[[1, 3]] = 0
+    seqs = kvq.Seqs(torch.from_numpy(lens.astype(np.int32)).cuda(), bt.seqs.block_table)
+    osc = oracle.page_scores(bt.ocache, bt.table, lens, bt.q)
+    maxp = bt.table.shape[1]
+    k_max = kvq.num_selected(maxp, w.ratio_num, w.ratio_den, w.k_fixed)
+    pps = max(k_max, 1)
+    outs = []
+    for k_cap in (k_max, 2 * pps):   # one split per row: no combine; two (the second empty): combine
+        osel, ocnt = oracle.topk(osc, lens, w.ratio_num, w.ratio_den, w.k_fixed, k_cap)
+        out = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.zeros(kvq.kvq_attn_workspace_bytes(w.batch, w.num_q_heads, w.head_dim, maxp, k_cap, pps) // 4 + 64,
+                         dtype=torch.float32, device="cuda")
+        kvq.kvq_sparse_decode_attn(bt.cache, seqs, bt.q_dev, torch.from_numpy(osel).cuda(),
+                                   torch.from_numpy(ocnt).cuda(), out, ws, w.sm_scale(), pps)
+        torch.cuda.synchronize()
+        outs.append(to_np(out).astype(np.float64))
+    assert np.array_equal(outs[0], outs[1])
+    if w.batch > 3:
+        assert (outs[0][[1, 3]] == 0).all()
+    want = oracle.attention(bt.ocache, bt.table, lens, bt.q, osel, ocnt)
+    assert np.abs(outs[0] - want).max() <= ATTN_ATOL
+
+
 def test_topk_longest_rows():
     """kvq_topk_pages at its longest supported row (12000 pages), on random
     and on tied scores, against the oracle's top-K exactly."""
