@@ -286,7 +286,8 @@ kvq_status kvq_topk_pages(const float *scores, const kvq_seqs *seqs, int32_t num
  * a second kernel merges the splits with log-sum-exp weights (when no row
  * has more than one split, the split kernel writes out itself and no merge
  * runs; the output is the same bit for bit).  For a query
- * group (G = 2, 4, 8) over an INT8 cache the products run on the matrix cores:
+ * group (G = 2, 4, 8) over INT8 or 4-bit codes (a mixed cache's INT8 pages
+ * included) the products run on the matrix cores:
  * q.k as fp16 x fp16 with fp32 accumulation, p.v with the weights split into
  * three bf16 parts (~2^-21 relative) against exact bf16 codes, fp32
  * accumulation.

@@ -19,6 +19,10 @@
 // high byte of 1024.0h; 4-bit codes are first split into their low and high
 // nibbles), so for per-token or per-group (scale s, zero z)
 //   q.k = s * sum q_i (1024 + c_i) + (z - 1024 s) * sum q_i.
+// 4-bit codes take one packed fp16 subtraction more (1024 + c - 1024 = c,
+// exact), so that q.k = s * sum q_i c_i + z * sum q_i: their scale is 17x an
+// INT8 one's for the same range, and the cancelling 1024 s sum q_i term would
+// cost that much more accuracy.
 // Values: acc += (p s) * c per channel (byte or nibble converts + fma), plus
 // p z once per token.  The G query heads of a KV group share every loaded tile.
 //
@@ -149,8 +153,8 @@ typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));  // four bf16 bit patterns
 typedef float float4v __attribute__((ext_vector_type(4)));
 
-// Matrix-core form for a GQA group (G >= 2 query heads per KV head) over an
-// INT8 cache, where q.k and p.v are small GEMMs per 16-token page.  A
+// Matrix-core form for a GQA group (G >= 2 query heads per KV head) over
+// INT8 or 4-bit codes, where q.k and p.v are small GEMMs per 16-token page.  A
 // 16x16xKB MFMA takes A[i][k] from lane i + 16(k/KL), element k%KL, B[k][j]
 // from lane j + 16(k/KL), element k%KL (KL = KB/4 elements per lane), and
 // leaves D[i][j] in lane j + 16(i/4), register i%4.
@@ -173,12 +177,31 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 // The key codes become fp16 1024 + c by byte permute, as in the vector path.
 template <int FMT, int D, int G>
 struct MfmaPath {
-  static constexpr bool on = FMT != kFp16 && !fmt_int4(FMT) && G >= 2 && G <= 16;
+  static constexpr bool on = FMT != kFp16 && G >= 2 && G <= 16;
   // value MFMAs per page (16 output channels each); also the query's groups
   // of 4 channels per lane (two per logits MFMA)
   static constexpr int NM = D / 16;
-  static constexpr int NU = D / 64;  // 16-byte loads per lane per tile, K and V each
+  // 16-byte loads per lane per tile, K and V each (a lane's run of D/4
+  // channels: D/4 bytes of INT8 codes, D/8 of 4-bit codes)
+  static constexpr int NU = fmt_int4(FMT) ? D / 128 : D / 64;
 };
+
+// The fp16 pair (1024 + c0, 1024 + c1) less 1024: (c0, c1), exact.
+__device__ __forceinline__ half2v minus_1024(uint32_t x) { return as_half2(x) - half2v{1024.0f16, 1024.0f16}; }
+
+// 4-bit codes in the matrix-core form: a dword holds channels 0..7 of its run
+// as nibbles (2i low, 2i+1 high).  Its codes as exact fp16 values in the
+// order 0, 2, 4, 6, 1, 3, 5, 7 (the query is laid out in the same order, so
+// the products pair up); the values take the even and the odd channels as
+// two dwords of byte codes.
+__device__ __forceinline__ half8v nibbles_f16(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const half2v a = minus_1024(__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u));
+  const half2v b = minus_1024(__builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u));
+  const half2v c = minus_1024(__builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u));
+  const half2v d = minus_1024(__builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u));
+  return half8v{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 
 // Lane-quad byte transpose: lane r of each quad holds word W_r with bytes
 // (token r, channels c..c+3); afterwards it holds (tokens 0..3, channel c+r).
@@ -310,7 +333,9 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
   constexpr int LPT = T::LPT, TPL = T::TPL, NL = T::NL, CH = T::CH;
   using MP = MfmaPath<FMT, D, G>;
   constexpr bool MF = MP::on;
-  static_assert(!MF || NL == MP::NU, "an INT8 tile row is NL 16-byte loads per lane in both forms");
+  static_assert(!MF || NL * T::LB == 16 * MP::NU, "a lane's tile row is the same bytes in both forms");
+  // the offset left in the fp16 key codes (INT8: 1024 + c; 4-bit: c)
+  constexpr float kCodeOffset = fmt_int4(FMT) ? 0.0f : 1024.0f;
   constexpr int NWD = T::NWD;
   const int row = b * a.H + g;
   const int first = s * a.pps;
@@ -387,8 +412,16 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       const uint32_t wd[4] = {hn < G ? raw.x : 0u, hn < G ? raw.y : 0u, hn < G ? raw.z : 0u, hn < G ? raw.w : 0u};
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc += half_bits_to_float(wd[j] & 0xFFFFu) + half_bits_to_float(wd[j] >> 16);
-      qB[2 * i] = __builtin_bit_cast(half4v, ((uint64_t)wd[1] << 32) | wd[0]);
-      qB[2 * i + 1] = __builtin_bit_cast(half4v, ((uint64_t)wd[3] << 32) | wd[2]);
+      if constexpr (fmt_int4(FMT)) {  // channels 0, 2, 4, 6 then 1, 3, 5, 7 (as nibbles_f16)
+        qB[2 * i] = __builtin_bit_cast(half4v, ((uint64_t)__builtin_amdgcn_perm(wd[3], wd[2], 0x05040100u) << 32) |
+                                                   __builtin_amdgcn_perm(wd[1], wd[0], 0x05040100u));
+        qB[2 * i + 1] = __builtin_bit_cast(half4v,
+                                           ((uint64_t)__builtin_amdgcn_perm(wd[3], wd[2], 0x07060302u) << 32) |
+                                               __builtin_amdgcn_perm(wd[1], wd[0], 0x07060302u));
+      } else {
+        qB[2 * i] = __builtin_bit_cast(half4v, ((uint64_t)wd[1] << 32) | wd[0]);
+        qB[2 * i + 1] = __builtin_bit_cast(half4v, ((uint64_t)wd[3] << 32) | wd[2]);
+      }
     }
     qs_mf = acc;
   }
@@ -471,7 +504,21 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
   auto load_page = [&](int jl, int ph, PageRegs& r) {
     r.nvalid = min(kPage, L - jl * kPage);
     const size_t tile = ((size_t)ph * a.H + g) * tile_elems;
-    if constexpr (MF) {
+    if constexpr (MF && fmt_int4(FMT)) {
+      // as below, at half a byte per channel: one 16-byte load per lane, K and V each
+      const char* kp = k_base + tile / 2 + (lane & 15) * (D / 2) + (D / 8) * (lane >> 4);
+      const char* vp = v_base + tile / 2 + (4 * (lane >> 4) + (lane & 3)) * (D / 2) + (D / 8) * ((lane >> 2) & 3);
+      const Raw<4> kk = load_raw_cached(kp), vv = load_raw_cached(vp);
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+#pragma unroll
+        for (int x = 0; x < NWD; ++x) {
+          r.kr[u].w[x] = kk.w[NWD * u + x];
+          r.vr[u].w[x] = vv.w[NWD * u + x];
+        }
+      }
+    }
+    if constexpr (MF && !fmt_int4(FMT)) {
       // K: token l%16, run (D/4)(l/16); V: token 4(l/16) + l%4, run (D/4)((l/4)%4)
       const char* kp = k_base + tile + (lane & 15) * D + (D / 4) * (lane >> 4);
       const char* vp = v_base + tile + (4 * (lane >> 4) + (lane & 3)) * D + (D / 4) * ((lane >> 2) & 3);
@@ -485,6 +532,8 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
         r.kr[u] = load_raw_cached(kp + 16 * u);
         r.vr[u] = load_raw_cached(vp + 16 * u);
       }
+    }
+    if constexpr (MF) {
       if constexpr (fmt_token(FMT)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -516,7 +565,7 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       // logits of tokens 4 g4 + i for head hn: C = K Q^T on the matrix cores
       float4v cq = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int u = 0; u < NL; ++u) {
+      for (int u = 0; u < (fmt_int4(FMT) ? 0 : NL); ++u) {
         const uint32_t* kw = r.kr[u].w;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
@@ -527,6 +576,14 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
           cq = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qa, cq, 0, 0, 0);
         }
       }
+      if constexpr (fmt_int4(FMT)) {  // MFMA m: dword m of the lane's run, channels 8m .. 8m+7
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const half4v q0 = qB[2 * m], q1 = qB[2 * m + 1];
+          const half8v qa = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+          cq = __builtin_amdgcn_mfma_f32_16x16x32_f16(nibbles_f16(r.kr[m / NWD].w[m % NWD]), qa, cq, 0, 0, 0);
+        }
+      }
       float lg[4];
       bool valid[4];
       float lm = -INFINITY;
@@ -534,7 +591,7 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       for (int i = 0; i < 4; ++i) {
         valid[i] = 4 * g4 + i < nvalid && hn < G;
         const float4 pp = r.pr[NP == 4 ? i : 0];
-        const float zz = __builtin_fmaf(-1024.0f, pp.x, pp.y);
+        const float zz = __builtin_fmaf(-kCodeOffset, pp.x, pp.y);
         const float part = __builtin_fmaf(pp.x, cq[i], zz * qs_mf);
         lg[i] = valid[i] ? part * a.scale_log2 : -INFINITY;
         lm = fmaxf(lm, lg[i]);
@@ -578,16 +635,20 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       const uint32_t sel1 = (lane & 1) ? 0x07030501u : 0x02060004u;
       const uint32_t sel2 = (lane & 2) ? 0x07060302u : 0x01000504u;
 #pragma unroll
-      for (int u = 0; u < NL; ++u) {
-        const uint32_t* vw = r.vr[u].w;
-#pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4) {
-          const short4v vb = codes_bf16(quad_transpose_bytes(vw[d4], sel1, sel2));
-          const int j = 4 * u + d4;
-          mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa2, vb, mf_acc[j], 0, 0, 0);
-          mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa1, vb, mf_acc[j], 0, 0, 0);
-          mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa0, vb, mf_acc[j], 0, 0, 0);
+      for (int j = 0; j < MP::NM; ++j) {
+        // INT8: dword j of the lane's run, channels 4j .. 4j+3; 4-bit: the
+        // even (j even) or odd channels of dword j/2, as bytes
+        uint32_t x;
+        if constexpr (fmt_int4(FMT)) {
+          const uint32_t wv = r.vr[(j / 2) / NWD].w[(j / 2) % NWD];
+          x = (j % 2 ? wv >> 4 : wv) & 0x0F0F0F0Fu;
+        } else {
+          x = r.vr[j / 4].w[j % 4];
         }
+        const short4v vb = codes_bf16(quad_transpose_bytes(x, sel1, sel2));
+        mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa2, vb, mf_acc[j], 0, 0, 0);
+        mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa1, vb, mf_acc[j], 0, 0, 0);
+        mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa0, vb, mf_acc[j], 0, 0, 0);
       }
       return;
     }
@@ -617,10 +678,10 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       for (int d4 = 0; d4 < NWD; ++d4) {
         if constexpr (fmt_int4(FMT)) {  // word d4: channels 8 d4 .. 8 d4 + 7 of the lane's run
           const uint32_t lo = kw[d4] & 0x0F0F0F0Fu, hi = (kw[d4] >> 4) & 0x0F0F0F0Fu;
-          const half2v k02 = as_half2(__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u));
-          const half2v k46 = as_half2(__builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u));
-          const half2v k13 = as_half2(__builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u));
-          const half2v k57 = as_half2(__builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u));
+          const half2v k02 = minus_1024(__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u));
+          const half2v k46 = minus_1024(__builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u));
+          const half2v k13 = minus_1024(__builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u));
+          const half2v k57 = minus_1024(__builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u));
 #pragma unroll
           for (int hh = 0; hh < G; ++hh) {
             dot[hh] = __builtin_amdgcn_fdot2(k02, qh[hh][4 * d4 + 0], dot[hh], false);
@@ -643,7 +704,7 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       }
       const bool valid = i * TPL + tg < nvalid;
       float zz = 0.0f;
-      if constexpr (FMT != kFp16) zz = __builtin_fmaf(-1024.0f, r.pr[i].x, r.pr[i].y);
+      if constexpr (FMT != kFp16) zz = __builtin_fmaf(-kCodeOffset, r.pr[i].x, r.pr[i].y);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float part = dot[hh];
@@ -783,7 +844,13 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       const float zh = __shfl(mf_z, hh, kWave);
       if (hh < G) {
 #pragma unroll
-        for (int j = 0; j < MP::NM; ++j) sm_acc[w][hh][(D / 4) * (hn >> 2) + 4 * j + (hn & 3)] = mf_acc[j][i] + zh;
+        for (int j = 0; j < MP::NM; ++j) {
+          // column n = hn of MFMA j: channel (D/4)(n/4) + 4j + n%4 (INT8), or
+          // (D/4)(n/4) + 8(j/2) + 2(n%4) + j%2 (4-bit, even then odd channels)
+          const int ch = fmt_int4(FMT) ? (D / 4) * (hn >> 2) + 8 * (j >> 1) + 2 * (hn & 3) + (j & 1)
+                                       : (D / 4) * (hn >> 2) + 4 * j + (hn & 3);
+          sm_acc[w][hh][ch] = mf_acc[j][i] + zh;
+        }
       }
     }
   } else if (tg == 0) {

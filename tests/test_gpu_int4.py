@@ -7,9 +7,9 @@ the fused append + scores, and edge rows); page scores to 1e-4; top-K exact on
 identical scores, near-tie rule on its own; attention within 2e-3 of fp64 on
 the oracle's selection and on the GPU's; the in-kernel selection equal, bit
 for bit, to top-K then attention.  4-bit storage is built for head_dim 128;
-its attention runs on the vector path for every group size, so group sizes
-1, 2, 4 and 8 are all covered.  The one-launch step does not take 4-bit
-storage and says so.
+its attention runs on the vector units for one query head per KV head and on
+the matrix cores for query groups (2, 4 and 8 heads), all covered here.  The
+one-launch step does not take 4-bit storage and says so.
 """
 import numpy as np
 import pytest
@@ -154,8 +154,8 @@ def test_int4_select_attention_and_step(kind, n, fmt):
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2)], ids=["g1", "g2", "g4", "g8"])
 def test_int4_group_sizes(fmt, hq, hkv):
-    """Every group size of the vector path (4-bit storage has no matrix-core
-    form): scores, the selecting step and the output against the oracle."""
+    """Every group size (1 on the vector units, 2, 4 and 8 on the matrix
+    cores): scores, the selecting step and the output against the oracle."""
     from test_gpu_parity import Built, check_scores, check_selection_near_ties, score_tolerance
     kvq, _ = mods()
     w = workloads.small(5).with_(name=f"int4_f{fmt}_{hq}x{hkv}", fmt=fmt, num_q_heads=hq, num_kv_heads=hkv)
