@@ -17,12 +17,12 @@
 // Keys: q.k runs on v_dot2_f32_f16 with the fp16 query.  A code c (8 or 4
 // bits) becomes the fp16 value 1024 + c with one byte permute (0x64 is the
 // high byte of 1024.0h; 4-bit codes are first split into their low and high
-// nibbles), so for per-token or per-group (scale s, zero z)
-//   q.k = s * sum q_i (1024 + c_i) + (z - 1024 s) * sum q_i.
-// 4-bit codes take one packed fp16 subtraction more (1024 + c - 1024 = c,
-// exact), so that q.k = s * sum q_i c_i + z * sum q_i: their scale is 17x an
-// INT8 one's for the same range, and the cancelling 1024 s sum q_i term would
-// cost that much more accuracy.
+// nibbles), and one packed fp16 subtraction makes it c exactly, so for
+// per-token or per-group (scale s, zero z)
+//   q.k = s * sum q_i c_i + z * sum q_i.
+// (Keeping the 1024 and folding -1024 s sum q_i into the zero term saves the
+// subtraction but cancels a term ~1024 s |sum q_i| in fp32: ten times the
+// output error on the 32K INT8 layer at the same speed.)
 // Values: acc += (p s) * c per channel (byte or nibble converts + fma), plus
 // p z once per token.  The G query heads of a KV group share every loaded tile.
 //
@@ -174,7 +174,7 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 //   4g + l%4) and a 4x4 byte transpose inside each lane quad (two DPP
 //   exchanges and byte permutes) hands lane (g, q, r) channel
 //   (D/4)q + 4j + r of tokens 4g .. 4g+3 for MFMA j.
-// The key codes become fp16 1024 + c by byte permute, as in the vector path.
+// The key codes become exact fp16 values as in the vector path.
 template <int FMT, int D, int G>
 struct MfmaPath {
   static constexpr bool on = FMT != kFp16 && G >= 2 && G <= 16;
@@ -228,11 +228,11 @@ __device__ __forceinline__ short4v codes_bf16(uint32_t w) {
                    __builtin_bit_cast(uint32_t, (float)(w >> 24)));
 }
 
-// Four INT8 codes (bytes of w) as fp16 1024 + c.
-__device__ __forceinline__ half4v codes_1024(uint32_t w) {
-  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, w, 0x04010400u);
-  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, w, 0x04030402u);
-  return __builtin_bit_cast(half4v, ((uint64_t)hi << 32) | lo);
+// Four INT8 codes (bytes of w) as exact fp16 values.
+__device__ __forceinline__ half4v codes_f16(uint32_t w) {
+  const half2v lo = minus_1024(__builtin_amdgcn_perm(0x64646464u, w, 0x04010400u));
+  const half2v hi = minus_1024(__builtin_amdgcn_perm(0x64646464u, w, 0x04030402u));
+  return half4v{lo[0], lo[1], hi[0], hi[1]};
 }
 
 // grid (B * Hq), 256 threads: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
@@ -334,8 +334,6 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
   using MP = MfmaPath<FMT, D, G>;
   constexpr bool MF = MP::on;
   static_assert(!MF || NL * T::LB == 16 * MP::NU, "a lane's tile row is the same bytes in both forms");
-  // the offset left in the fp16 key codes (INT8: 1024 + c; 4-bit: c)
-  constexpr float kCodeOffset = fmt_int4(FMT) ? 0.0f : 1024.0f;
   constexpr int NWD = T::NWD;
   const int row = b * a.H + g;
   const int first = s * a.pps;
@@ -569,7 +567,7 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
         const uint32_t* kw = r.kr[u].w;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          const half4v k0 = codes_1024(kw[2 * h2]), k1 = codes_1024(kw[2 * h2 + 1]);
+          const half4v k0 = codes_f16(kw[2 * h2]), k1 = codes_f16(kw[2 * h2 + 1]);
           const half4v q0 = qB[4 * u + 2 * h2], q1 = qB[4 * u + 2 * h2 + 1];
           const half8v ka = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
           const half8v qa = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
@@ -591,8 +589,7 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       for (int i = 0; i < 4; ++i) {
         valid[i] = 4 * g4 + i < nvalid && hn < G;
         const float4 pp = r.pr[NP == 4 ? i : 0];
-        const float zz = __builtin_fmaf(-kCodeOffset, pp.x, pp.y);
-        const float part = __builtin_fmaf(pp.x, cq[i], zz * qs_mf);
+        const float part = __builtin_fmaf(pp.x, cq[i], pp.y * qs_mf);
         lg[i] = valid[i] ? part * a.scale_log2 : -INFINITY;
         lm = fmaxf(lm, lg[i]);
       }
@@ -693,8 +690,8 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
 #pragma unroll
           for (int hh = 0; hh < G; ++hh) dot[hh] = __builtin_amdgcn_fdot2(as_half2(kw[d4]), qh[hh][d4], dot[hh], false);
         } else {
-          const half2v lo = as_half2(__builtin_amdgcn_perm(0x64646464u, kw[d4], 0x04010400u));
-          const half2v hi = as_half2(__builtin_amdgcn_perm(0x64646464u, kw[d4], 0x04030402u));
+          const half2v lo = minus_1024(__builtin_amdgcn_perm(0x64646464u, kw[d4], 0x04010400u));
+          const half2v hi = minus_1024(__builtin_amdgcn_perm(0x64646464u, kw[d4], 0x04030402u));
 #pragma unroll
           for (int hh = 0; hh < G; ++hh) {
             dot[hh] = __builtin_amdgcn_fdot2(lo, qh[hh][2 * d4], dot[hh], false);
@@ -704,7 +701,7 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       }
       const bool valid = i * TPL + tg < nvalid;
       float zz = 0.0f;
-      if constexpr (FMT != kFp16) zz = __builtin_fmaf(-kCodeOffset, r.pr[i].x, r.pr[i].y);
+      if constexpr (FMT != kFp16) zz = r.pr[i].y;
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float part = dot[hh];
