@@ -294,12 +294,14 @@ def test_select_attention_equals_topk_then_attention(kind, n):
         assert torch.equal(out_fus, out_sep), pps
 
 
-def test_select_attention_on_tied_scores():
-    """Heavily tied scores (small integers, -0 and +0, plateaus) on a ragged
-    GQA batch: the in-kernel selection equals the oracle's top-K exactly and
-    the output equals top-K then attention bit for bit."""
+@pytest.mark.parametrize("n", [5, 4], ids=["ragged_gqa_short_rows", "rows_of_127_pages"])
+def test_select_attention_on_tied_scores(n):
+    """Heavily tied scores (small integers, -0 and +0, plateaus): the in-kernel
+    selection equals the oracle's top-K exactly and the output equals top-K
+    then attention bit for bit -- on a ragged GQA batch of short rows and on
+    rows of 127 pages."""
     _, runtime = kvq_mod()
-    bt = built(("small", 5), workloads.small(5))
+    bt = built(("small", n), workloads.small(n))
     w = bt.w
     B, maxp, H = bt.table.shape[0], bt.table.shape[1], w.num_kv_heads
     rng = np.random.default_rng(33)
