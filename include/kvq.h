@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 7
+#define KVQ_ABI_VERSION 8
 #define KVQ_PAGE_SIZE 16
 #define KVQ_SELECT_MAX_PAGES 2048 /* longest row (pages) kvq_select_decode_attn takes */
 
@@ -229,7 +229,10 @@ kvq_status kvq_append_decode_scores(const kvq_cache *cache, const kvq_seqs *seqs
  * kvq_build_coarse_meta -- each super-page's box: the channel-wise min of its
  * valid pages' metadata minima and max of their maxima, exact (min/max of
  * page_meta, which must be current).  Written for super-pages
- * super_begin[b] <= jc < ceil(P_b / group_pages) (super_begin NULL: all), as
+ * super_begin[b] <= jc < ceil(P_b / group_pages) (super_begin NULL: all);
+ * max_span (host, >= 0), when super_begin is given, bounds how many of them
+ * each sequence needs refreshed and only sizes the grid (0: all of them,
+ * e.g. 1 + the pages a decode-time append touches / group_pages), as
  *   coarse_meta  [B * pc_max][H_kv][2][d] fp32 (the page_meta layout with
  *                "physical page" b * pc_max + jc),
  *   coarse_lens  [B] int32: 16 * ceil(P_b / group_pages), and
@@ -241,8 +244,8 @@ kvq_status kvq_append_decode_scores(const kvq_cache *cache, const kvq_seqs *seqs
  * k_fixed = kc the kept super-pages.
  */
 kvq_status kvq_build_coarse_meta(const kvq_cache *cache, const kvq_seqs *seqs, int32_t group_pages,
-                                 const int32_t *super_begin, float *coarse_meta, int32_t *coarse_lens,
-                                 int32_t *coarse_table, void *stream);
+                                 const int32_t *super_begin, int32_t max_span, float *coarse_meta,
+                                 int32_t *coarse_lens, int32_t *coarse_table, void *stream);
 
 /*
  * kvq_page_scores_masked -- kvq_page_scores restricted to the kept

@@ -73,7 +73,7 @@ def lib() -> ctypes.CDLL:
         L.kvq_select_decode_attn_noalloc.argtypes = [C, S, P, I, P, I, I, I, I, P, P, ctypes.c_float, I, P, P]
         L.kvq_decode_step.argtypes = [C, S, P, P, I, P, P, P, I, P, I, I, I, I, P, P, ctypes.c_float, I, P, P,
                                       ctypes.c_size_t, P]
-        L.kvq_build_coarse_meta.argtypes = [C, S, I, P, P, P, P, P]
+        L.kvq_build_coarse_meta.argtypes = [C, S, I, P, I, P, P, P, P]
         L.kvq_page_scores_masked.argtypes = [C, S, P, I, I, P, P, I, P, P]
         L.kvq_demote_pages.argtypes = [C, S, I, P, P, P, P]
         L.kvq_step_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
@@ -261,10 +261,10 @@ def kvq_page_scores(cache: PagedCache, seqs: Seqs, q, scores, stream=None) -> No
 
 
 def kvq_build_coarse_meta(cache: PagedCache, seqs: Seqs, group_pages: int, super_begin, coarse_meta, coarse_lens,
-                          coarse_table, stream=None) -> None:
+                          coarse_table, stream=None, max_span: int = 0) -> None:
     _check("kvq_build_coarse_meta", lib().kvq_build_coarse_meta(
         ctypes.byref(cache.struct()), ctypes.byref(seqs.struct()), int(group_pages), _ptr(super_begin),
-        _ptr(coarse_meta), _ptr(coarse_lens), _ptr(coarse_table), _stream(stream)))
+        int(max_span), _ptr(coarse_meta), _ptr(coarse_lens), _ptr(coarse_table), _stream(stream)))
 
 
 def kvq_page_scores_masked(cache: PagedCache, seqs: Seqs, q, group_pages: int, sel_super, sel_super_count, scores,

@@ -22,6 +22,7 @@ struct CoarseArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   const int32_t* super_begin;  // [B] or NULL
+  int from_begin;              // 1: the grid covers super-pages from super_begin[b] on
   float* coarse;               // [B * pc_max][H][2][D]
   int32_t* coarse_lens;        // [B]: 16 * super-pages of the sequence
   int32_t* coarse_table;       // [B][pc_max]: b * pc_max + jc
@@ -31,18 +32,20 @@ struct CoarseArgs {
 // One wave per (super-page slot jc, KV head, sequence): lanes 0-31 hold
 // min-row channels and lanes 32-63 max-row channels, E each, as the scorer
 // reads a page's metadata; the wave folds the member pages' rows with min
-// (lanes < 32) or max.  Grid (ceil(pc_max / 4), H, B), 4 waves per block.
+// (lanes < 32) or max.  Grid (ceil(span / 4), H, B), 4 waves per block; the
+// slots start at 0, or at super_begin[b] when the grid covers only the
+// super-pages from there (from_begin).
 template <int D>
 __global__ __launch_bounds__(256) void coarse_meta_kernel(CoarseArgs a) {
   constexpr int E = 2 * D / 64;
   const int b = blockIdx.z, h = blockIdx.y;
-  const int jc = blockIdx.x * 4 + wave_id();
+  const int first = a.super_begin ? max(a.super_begin[b], 0) : 0;
+  const int jc = (a.from_begin ? first : 0) + blockIdx.x * 4 + wave_id();
   const int lane = lane_id();
   if (h == 0 && jc < a.pc_max && lane == 0) a.coarse_table[(size_t)b * a.pc_max + jc] = b * a.pc_max + jc;
   const int P = min((a.seq_lens[b] + kPage - 1) / kPage, a.max_pages);
   const int Pc = (P + a.group - 1) / a.group;
   if (h == 0 && blockIdx.x == 0 && threadIdx.x == 0) a.coarse_lens[b] = kPage * Pc;
-  const int first = a.super_begin ? max(a.super_begin[b], 0) : 0;
   if (jc >= Pc || jc < first) return;  // wave-uniform
   const bool max_row = lane >= 32;
   float acc[E];
@@ -145,11 +148,14 @@ hipError_t masked_d(const MaskedArgs& a, int rows, int G, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_coarse_meta(const kvq_cache& c, const kvq_seqs& s, int group, const int32_t* super_begin,
-                              float* coarse, int32_t* coarse_lens, int32_t* coarse_table, hipStream_t st) {
+                              int max_span, float* coarse, int32_t* coarse_lens, int32_t* coarse_table,
+                              hipStream_t st) {
   const int pc_max = (s.max_pages + group - 1) / group;
-  CoarseArgs a{c.page_meta, s.block_table, s.seq_lens, super_begin, coarse, coarse_lens, coarse_table,
-               c.num_kv_heads, s.max_pages, group, pc_max, s.batch};
-  const dim3 grid((pc_max + 3) / 4, c.num_kv_heads, s.batch);
+  const bool from_begin = super_begin && max_span > 0 && max_span < pc_max;
+  const int span = from_begin ? max_span : pc_max;
+  CoarseArgs a{c.page_meta, s.block_table, s.seq_lens, super_begin, from_begin ? 1 : 0, coarse, coarse_lens,
+               coarse_table, c.num_kv_heads, s.max_pages, group, pc_max, s.batch};
+  const dim3 grid((span + 3) / 4, c.num_kv_heads, s.batch);
   if (c.head_dim == 64)
     hipLaunchKernelGGL(coarse_meta_kernel<64>, grid, dim3(256), 0, st, a);
   else

@@ -167,17 +167,17 @@ kvq_status kvq_page_scores(const kvq_cache* cache, const kvq_seqs* seqs, const u
 }
 
 kvq_status kvq_build_coarse_meta(const kvq_cache* cache, const kvq_seqs* seqs, int32_t group_pages,
-                                 const int32_t* super_begin, float* coarse_meta, int32_t* coarse_lens,
-                                 int32_t* coarse_table, void* stream) {
+                                 const int32_t* super_begin, int32_t max_span, float* coarse_meta,
+                                 int32_t* coarse_lens, int32_t* coarse_table, void* stream) {
   kvq_status st = check_cache(cache, true);
   if (st != KVQ_OK) return st;
   if ((st = check_seqs(seqs)) != KVQ_OK) return st;
-  if (group_pages < 1 || group_pages > 64) return KVQ_ERR_INVALID_ARG;
+  if (group_pages < 1 || group_pages > 64 || max_span < 0) return KVQ_ERR_INVALID_ARG;
   if (!coarse_meta || !coarse_lens || !coarse_table || !aligned16(coarse_meta)) return KVQ_ERR_INVALID_ARG;
   if ((long long)seqs->batch * ((seqs->max_pages + group_pages - 1) / group_pages) > 0x7FFFFFFFLL)
     return KVQ_ERR_UNSUPPORTED;
-  return from_hip(kvq::launch_coarse_meta(*cache, *seqs, group_pages, super_begin, coarse_meta, coarse_lens,
-                                          coarse_table, (hipStream_t)stream));
+  return from_hip(kvq::launch_coarse_meta(*cache, *seqs, group_pages, super_begin, max_span, coarse_meta,
+                                          coarse_lens, coarse_table, (hipStream_t)stream));
 }
 
 kvq_status kvq_page_scores_masked(const kvq_cache* cache, const kvq_seqs* seqs, const uint16_t* q,

@@ -77,7 +77,8 @@ struct InKernelSelect {
 
 // Coarse-then-fine selection (hier_select.hip).
 hipError_t launch_coarse_meta(const kvq_cache& c, const kvq_seqs& s, int group, const int32_t* super_begin,
-                              float* coarse, int32_t* coarse_lens, int32_t* coarse_table, hipStream_t st);
+                              int max_span, float* coarse, int32_t* coarse_lens, int32_t* coarse_table,
+                              hipStream_t st);
 hipError_t launch_page_scores_masked(const kvq_cache& c, const kvq_seqs& s, const uint16_t* q, int num_q_heads,
                                      int group, const int32_t* sel_super, const int32_t* sel_count, int kc_cap,
                                      float* scores, hipStream_t st);

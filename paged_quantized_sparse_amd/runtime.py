@@ -240,9 +240,11 @@ class HierStep:
         self.sel_super = torch.empty((B, H, self.kc), dtype=torch.int32, device=device)
         self.sel_super_count = torch.empty((B, H), dtype=torch.int32, device=device)
 
-    def build(self, super_begin=None, stream=None) -> None:
+    def build(self, super_begin=None, stream=None, max_span: int = 0) -> None:
+        """Boxes of every super-page, or of those from super_begin[b] on (at
+        most max_span of them per sequence when max_span > 0)."""
         kvq_build_coarse_meta(self.step.cache, self.step.seqs, self.group, super_begin, self.coarse,
-                              self.coarse_lens, self.coarse_table, stream)
+                              self.coarse_lens, self.coarse_table, stream, max_span)
 
     def screen(self, q, stream=None) -> None:
         """Coarse scores, the kept super-pages, and the masked fine scores."""
@@ -270,5 +272,6 @@ class HierStep:
         of the super-pages they touch (super_begin[b]: the first one), then
         screen, select and attend."""
         app.run(stream)
-        self.build(super_begin, stream)
+        # the app.span pages the rows touch lie in at most span // group + 2 super-pages
+        self.build(super_begin, stream, app.span // self.group + 2)
         return self.run(q, stream)

@@ -58,8 +58,8 @@ def test_library_never_allocates_or_synchronizes():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == 7
-    assert "#define KVQ_ABI_VERSION 7" in open(HEADER).read()
+    assert lib.kvq_abi_version() == 8
+    assert "#define KVQ_ABI_VERSION 8" in open(HEADER).read()
     for s, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP"), (99, b"unknown")]:
         assert word in lib.kvq_status_string(s)
 
@@ -160,6 +160,22 @@ def test_mixed_precision_argument_errors(lib):
         c, s = _structs(fmt=fmt)
         assert lib.kvq_decode_step(ctypes.byref(c), ctypes.byref(s), FAKE, FAKE, 1, FAKE, FAKE, FAKE, 4, FAKE,
                                    3, 10, 0, 8, FAKE, FAKE, 0.1, 0, FAKE, None, 1 << 30, None) == UNSUPPORTED
+
+
+def test_coarse_then_fine_argument_errors(lib):
+    """Super-page boxes need 1 <= group_pages <= 64, a non-negative span and
+    their three arrays; the masked scorer needs its selection and a valid
+    query-head count."""
+    c, s = _structs()
+    build = lib.kvq_build_coarse_meta
+    assert build(ctypes.byref(c), ctypes.byref(s), 0, None, 0, FAKE, FAKE, FAKE, None) == INVALID
+    assert build(ctypes.byref(c), ctypes.byref(s), 65, None, 0, FAKE, FAKE, FAKE, None) == INVALID
+    assert build(ctypes.byref(c), ctypes.byref(s), 8, FAKE, -1, FAKE, FAKE, FAKE, None) == INVALID
+    assert build(ctypes.byref(c), ctypes.byref(s), 8, None, 0, None, FAKE, FAKE, None) == INVALID
+    cm, sm = _structs(meta=False)
+    assert build(ctypes.byref(cm), ctypes.byref(sm), 8, None, 0, FAKE, FAKE, FAKE, None) == INVALID
+    masked = lib.kvq_page_scores_masked
+    assert masked(ctypes.byref(c), ctypes.byref(s), FAKE, 5, 8, FAKE, FAKE, 4, FAKE, None) == INVALID
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
