@@ -293,7 +293,10 @@ kvq_status kvq_topk_pages(const float *scores, const kvq_seqs *seqs, int32_t num
  * included) the products run on the matrix cores:
  * q.k as fp16 x fp16 with fp32 accumulation, p.v with the weights split into
  * three bf16 parts (~2^-21 relative) against exact bf16 codes, fp32
- * accumulation.
+ * accumulation.  A mixed cache's fp16 pages take the matrix cores too for a
+ * query group: q.k as fp16 x fp16, p.v with the weights (times 2^7) split into
+ * two fp16 parts against the fp16 values, fp32 accumulation.  A whole fp16
+ * cache runs on the vector units.
  *   q   : [B][H_q][d] fp16 bits
  *   out : [B][H_q][d] fp32
  *   ws  : workspace of at least kvq_attn_workspace_bytes(...) bytes (the

@@ -177,14 +177,34 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 // The key codes become exact fp16 values as in the vector path.
 template <int FMT, int D, int G>
 struct MfmaPath {
-  static constexpr bool on = FMT != kFp16 && G >= 2 && G <= 16;
+  static constexpr bool on = G >= 2 && G <= 16;
   // value MFMAs per page (16 output channels each); also the query's groups
   // of 4 channels per lane (two per logits MFMA)
   static constexpr int NM = D / 16;
   // 16-byte loads per lane per tile, K and V each (a lane's run of D/4
-  // channels: D/4 bytes of INT8 codes, D/8 of 4-bit codes)
-  static constexpr int NU = fmt_int4(FMT) ? D / 128 : D / 64;
+  // channels: D/2 bytes of fp16, D/4 of INT8 codes, D/8 of 4-bit codes)
+  static constexpr int NU = FMT == kFp16 ? D / 32 : fmt_int4(FMT) ? D / 128 : D / 64;
 };
+
+// fp16 tiles in the matrix-core form: the 4x4 transpose, inside each lane
+// quad, of 16-bit values.  Lane r of a quad holds (lo, hi) = channels
+// (c, c+1), (c+2, c+3) of token r; afterwards it holds channel c+r of tokens
+// 0..3, as an MFMA B operand.  sel1 is the lane's permute of the first
+// exchange (its pair-partner's half next to its own).
+__device__ __forceinline__ half4v quad_transpose_halves(uint32_t lo, uint32_t hi, uint32_t sel1) {
+  const int lane = lane_id();
+  // lanes 2k, 2k+1: channels (c, c+2) or (c+1, c+3) of tokens 2k, 2k+1
+  const uint32_t plo = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, kDppXor1, 0xF, 0xF, false);
+  const uint32_t phi = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, kDppXor1, 0xF, 0xF, false);
+  const uint32_t a = __builtin_amdgcn_perm(plo, lo, sel1);  // channel c (even lane) or c+1, tokens 2k, 2k+1
+  const uint32_t b = __builtin_amdgcn_perm(phi, hi, sel1);  // channel c+2 or c+3
+  // lanes 0, 1 keep a and take lane 2, 3's a; lanes 2, 3 take lane 0, 1's b and keep b
+  const bool upper = lane & 2;
+  const uint32_t send = upper ? a : b;
+  const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, kDppXor2, 0xF, 0xF, false);
+  const uint32_t t01 = upper ? recv : a, t23 = upper ? b : recv;
+  return __builtin_bit_cast(half4v, ((uint64_t)t23 << 32) | t01);
+}
 
 // The fp16 pair (1024 + c0, 1024 + c1) less 1024: (c0, c1), exact.
 __device__ __forceinline__ half2v minus_1024(uint32_t x) { return as_half2(x) - half2v{1024.0f16, 1024.0f16}; }
@@ -332,7 +352,12 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
   using T = Tile<FMT, D>;
   constexpr int LPT = T::LPT, TPL = T::TPL, NL = T::NL, CH = T::CH;
   using MP = MfmaPath<FMT, D, G>;
-  constexpr bool MF = MP::on;
+  // fp16 tiles take the matrix cores only in the FP16 pass of a mixed cache,
+  // whose short page lists leave the vector form's per-tile work exposed
+  // (GQA batch of 64 ragged sequences, mixed: 192 against 231 us per attention
+  // call); a whole fp16 cache is bandwidth-bound and the vector form is faster
+  // there (about 270 against 284 us on the same batch stored as fp16)
+  constexpr bool MF = MP::on && (FMT != kFp16 || PH == 1);
   static_assert(!MF || NL * T::LB == 16 * MP::NU, "a lane's tile row is the same bytes in both forms");
   constexpr int NWD = T::NWD;
   const int row = b * a.H + g;
@@ -516,7 +541,18 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
         }
       }
     }
-    if constexpr (MF && !fmt_int4(FMT)) {
+    if constexpr (MF && FMT == kFp16) {
+      // as below, at two bytes per channel: NU 16-byte loads per lane, K and V each
+      const char* kp = k_base + 2 * tile + (lane & 15) * (2 * D) + (D / 2) * (lane >> 4);
+      const char* vp = v_base + 2 * tile + (4 * (lane >> 4) + (lane & 3)) * (2 * D) + (D / 2) * ((lane >> 2) & 3);
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        r.kr[u] = load_raw_cached(kp + 16 * u);
+        r.vr[u] = load_raw_cached(vp + 16 * u);
+      }
+      return;
+    }
+    if constexpr (MF && FMT != kFp16 && !fmt_int4(FMT)) {
       // K: token l%16, run (D/4)(l/16); V: token 4(l/16) + l%4, run (D/4)((l/4)%4)
       const char* kp = k_base + tile + (lane & 15) * D + (D / 4) * (lane >> 4);
       const char* vp = v_base + tile + (4 * (lane >> 4) + (lane & 3)) * D + (D / 4) * ((lane >> 2) & 3);
@@ -563,7 +599,7 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
       // logits of tokens 4 g4 + i for head hn: C = K Q^T on the matrix cores
       float4v cq = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int u = 0; u < (fmt_int4(FMT) ? 0 : NL); ++u) {
+      for (int u = 0; u < (fmt_int4(FMT) || FMT == kFp16 ? 0 : NL); ++u) {
         const uint32_t* kw = r.kr[u].w;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
@@ -571,6 +607,18 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
           const half4v q0 = qB[4 * u + 2 * h2], q1 = qB[4 * u + 2 * h2 + 1];
           const half8v ka = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
           const half8v qa = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+          cq = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qa, cq, 0, 0, 0);
+        }
+      }
+      if constexpr (FMT == kFp16) {  // MFMA m: load m of the lane's run, channels 8m .. 8m+7
+#pragma unroll
+        for (int m = 0; m < NL; ++m) {
+          const half4v q0 = qB[2 * m], q1 = qB[2 * m + 1];
+          const half8v qa = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+          const uint32_t* kw = r.kr[m].w;
+          const half4v k0 = __builtin_bit_cast(half4v, ((uint64_t)kw[1] << 32) | kw[0]);
+          const half4v k1 = __builtin_bit_cast(half4v, ((uint64_t)kw[3] << 32) | kw[2]);
+          const half8v ka = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
           cq = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qa, cq, 0, 0, 0);
         }
       }
@@ -588,8 +636,11 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         valid[i] = 4 * g4 + i < nvalid && hn < G;
-        const float4 pp = r.pr[NP == 4 ? i : 0];
-        const float part = __builtin_fmaf(pp.x, cq[i], pp.y * qs_mf);
+        float part = cq[i];
+        if constexpr (FMT != kFp16) {
+          const float4 pp = r.pr[NP == 4 ? i : 0];
+          part = __builtin_fmaf(pp.x, cq[i], pp.y * qs_mf);
+        }
         lg[i] = valid[i] ? part * a.scale_log2 : -INFINITY;
         lm = fmaxf(lm, lg[i]);
       }
@@ -608,6 +659,33 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
           for (int j = 0; j < MP::NM; ++j) mf_acc[j][i] *= ai;
         }
         mf_m = mn;
+      }
+      if constexpr (FMT == kFp16) {
+        // values: O += (W_hi + W_lo) V on v_mfma_f32_16x16x16_f16, V exact fp16,
+        // W = 2^7 p split into two fp16 parts (~2^-22 relative; the scale keeps
+        // weights down to 2^-21 normal in fp16, and p <= 2^kLazy keeps 2^7 p
+        // below fp16's maximum), O scaled back by 2^-7 when the partial is written
+        half4v whi, wlo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = lg[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lg[i] - mf_m);
+          mf_l += p;
+          const float w = 128.0f * p;
+          whi[i] = (_Float16)w;
+          wlo[i] = (_Float16)(w - (float)whi[i]);
+        }
+        // a padding token's row may hold any bits (NaN included): zeroed
+        const bool vpad = 4 * g4 + (lane & 3) >= nvalid;
+        const uint32_t sel1 = (lane & 1) ? 0x03020706u : 0x05040100u;
+#pragma unroll
+        for (int j = 0; j < MP::NM; ++j) {  // channels 4j .. 4j+3 of the lane's run: dwords 2j, 2j+1
+          const uint32_t lo = vpad ? 0u : r.vr[j / 2].w[2 * (j % 2)];
+          const uint32_t hi = vpad ? 0u : r.vr[j / 2].w[2 * (j % 2) + 1];
+          const half4v vb = quad_transpose_halves(lo, hi, sel1);
+          mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(wlo, vb, mf_acc[j], 0, 0, 0);
+          mf_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(whi, vb, mf_acc[j], 0, 0, 0);
+        }
+        return;
       }
       uint32_t wb0[4], wb1[4], wb2[4];  // w = b0 + b1 + b2, each a bf16 (low 16 bits zero)
 #pragma unroll
@@ -846,7 +924,7 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int g, int b, in
           // (D/4)(n/4) + 8(j/2) + 2(n%4) + j%2 (4-bit, even then odd channels)
           const int ch = fmt_int4(FMT) ? (D / 4) * (hn >> 2) + 8 * (j >> 1) + 2 * (hn & 3) + (j & 1)
                                        : (D / 4) * (hn >> 2) + 4 * j + (hn & 3);
-          sm_acc[w][hh][ch] = mf_acc[j][i] + zh;
+          sm_acc[w][hh][ch] = FMT == kFp16 ? mf_acc[j][i] * 0.0078125f : mf_acc[j][i] + zh;  // fp16: 2^-7
         }
       }
     }

@@ -8,7 +8,7 @@ demotion); page scores to 1e-4; top-K exact on identical scores; attention
 within 2e-3 of fp64 on the oracle's selection and on the GPU's; the in-kernel
 selection bit-equal to top-K then attention.  The attention kernel takes each
 split's FP16 pages and INT8 pages in two passes and merges them, so a cache
-with one pool empty must give, bit for bit, the single-format kernel's output.
+with its FP16 pool empty must give, bit for bit, the INT8 kernel's output.
 """
 import numpy as np
 import pytest
@@ -148,8 +148,8 @@ def test_mixed_select_attention_and_step(kind, n, hot):
 @pytest.mark.parametrize("hq,hkv,d", [(4, 4, 128), (8, 4, 128), (8, 2, 128), (16, 2, 128), (8, 2, 64), (4, 4, 64)],
                          ids=["g1d128", "g2d128", "g4d128", "g8d128", "g4d64", "g1d64"])
 def test_mixed_group_sizes_and_head_dims(hq, hkv, d):
-    """The INT8 pass runs on the matrix cores for G >= 2 and the FP16 pass on
-    the vector units: every group size and both head dims, against the oracle."""
+    """Both passes run on the matrix cores for G >= 2 and on the vector units
+    for G = 1: every group size and both head dims, against the oracle."""
     from test_gpu_parity import Built, check_scores, check_selection_near_ties, score_tolerance
     w = mixed(workloads.small(5), 5).with_(name=f"mixed_{hq}x{hkv}_d{d}", num_q_heads=hq, num_kv_heads=hkv,
                                            head_dim=d)
@@ -171,8 +171,11 @@ def test_mixed_group_sizes_and_head_dims(hq, hkv, d):
 def test_mixed_with_one_pool_equals_the_single_format(pool, fused):
     """Every page in the INT8 pool (num_fp16_pages 0) or in the FP16 pool: the
     storage equals an INT8-per-token (fp16) cache's byte for byte, and the
-    scores, selection and output of the step equal that cache's bit for bit
-    (the other pass contributes nothing to the merge)."""
+    scores and selection of the step equal that cache's bit for bit.  The
+    output too, bit for bit, for the INT8 pool (the other pass contributes
+    nothing to the merge); for the FP16 pool of this query group the mixed
+    cache's FP16 pass runs on the matrix cores and a plain fp16 cache on the
+    vector units, so there the outputs agree to 1e-5."""
     kvq, runtime = mods()
     base = workloads.small(5)
     fmt1 = workloads.FMT_INT8_TOKEN if pool == "all_int8" else workloads.FMT_FP16
@@ -197,7 +200,11 @@ def test_mixed_with_one_pool_equals_the_single_format(pool, fused):
         outs.append((st.run(q).clone(), st.sel_pages.clone(), st.scores.clone()))
     torch.cuda.synchronize()
     (o1, p1, sc1), (om, pm, scm) = outs
-    assert torch.equal(om, o1) and torch.equal(pm, p1)
+    assert torch.equal(pm, p1)
+    if pool == "all_int8":
+        assert torch.equal(om, o1)
+    else:
+        assert (om - o1).abs().max().item() <= 1e-5
     P = (lens + PAGE - 1) // PAGE
     for b in range(len(lens)):
         assert torch.equal(scm[b, :, :P[b]], sc1[b, :, :P[b]])
