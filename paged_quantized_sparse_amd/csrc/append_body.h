@@ -27,6 +27,7 @@
 namespace kvq {
 
 constexpr int kMaxTouched = 5;  // 64 rows starting anywhere in a page touch at most 5 pages
+constexpr int kRowBatch = 4;    // new rows (or channel pairs) whose loads are issued together
 
 struct AppendView {
   void* k_pages;
@@ -111,93 +112,109 @@ __device__ __forceinline__ void append_page(const AppendView& a, void* kpool, vo
         }
     }
 
-    // the page's new rows
-    for (int t = t_begin; t < t_end; ++t) {
-      const size_t src = ((size_t)(r0 + t - start) * a.H + h) * D + lane * E;
-      const size_t dst = (tile + t % kPage) * D + lane * E;
-      float kdec[E];
-      if constexpr (PF == kFp16) {
-        uint32_t kw = 0, vw = 0;
+    // the page's new rows, four at a time: their fp16 bits are loaded
+    // together (a row past the page's last re-reads the last), so a page's
+    // rows cost a few dependent loads, not one each
+    for (int t0 = t_begin; t0 < t_end; t0 += kRowBatch) {  // wave-uniform
+      uint16_t kin[kRowBatch][E], vin[kRowBatch][E];
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        const size_t src = ((size_t)(r0 + min(t0 + u, t_end - 1) - start) * a.H + h) * D + lane * E;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const uint16_t kb = a.k_new[src + e];
-          const uint16_t vb = a.v_new[src + e];
-          if constexpr (WT) {
-            kw |= (uint32_t)kb << (16 * e);
-            vw |= (uint32_t)vb << (16 * e);
-          } else {
-            ((uint16_t*)kpool)[dst + e] = kb;
-            ((uint16_t*)vpool)[dst + e] = vb;
-          }
-          kdec[e] = half_bits_to_float(kb);
-        }
-        if constexpr (WT) {
-          const size_t row = (tile + t % kPage) * D * 2;
-          store_row_dev<2 * E>((uint8_t*)kpool + row, kw);
-          store_row_dev<2 * E>((uint8_t*)vpool + row, vw);
-        }
-      } else {
-        float kx[E], vx[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          kx[e] = half_bits_to_float(a.k_new[src + e]);
-          vx[e] = half_bits_to_float(a.v_new[src + e]);
-        }
-        float ks = gk[0], kz = gk[1], kinv = ginv[0], vs = gv[0], vz = gv[1], vinv = ginv[1];
-        if constexpr (fmt_token(PF)) {
-          float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            klo = fminf(klo, kx[e]); khi = fmaxf(khi, kx[e]);
-            vlo = fminf(vlo, vx[e]); vhi = fmaxf(vhi, vx[e]);
-          }
-          klo = zero_point(min_contig<64>(klo)); khi = max_contig<64>(khi);
-          vlo = zero_point(min_contig<64>(vlo)); vhi = max_contig<64>(vhi);
-          quant_params<LV>(klo, khi, ks, kinv);
-          quant_params<LV>(vlo, vhi, vs, vinv);
-          kz = klo;
-          vz = vlo;
-          if (lane == 0) {
-            float* tp = params + (tile + t % kPage) * 4;
-            if constexpr (WT) {
-              store_f<true>(tp, ks);
-              store_f<true>(tp + 1, kz);
-              store_f<true>(tp + 2, vs);
-              store_f<true>(tp + 3, vz);
-            } else {
-              *(float4*)tp = make_float4(ks, kz, vs, vz);
-            }
-          }
-        }
-        uint32_t kw = 0, vw = 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const uint32_t kc = quant_code<LV>(kx[e], kz, kinv);
-          const uint32_t vc = quant_code<LV>(vx[e], vz, vinv);
-          kw |= kc << (BITS * e);
-          vw |= vc << (BITS * e);
-          kdec[e] = __builtin_fmaf((float)kc, ks, kz);
-        }
-        const size_t row = (tile + t % kPage) * CROW;
-        if constexpr (WT) {
-          store_row_dev<E * BITS / 8>((uint8_t*)kpool + row, kw);
-          store_row_dev<E * BITS / 8>((uint8_t*)vpool + row, vw);
-        } else {
-          uint8_t* kp = (uint8_t*)kpool + row + lane * (E * BITS / 8);
-          uint8_t* vp = (uint8_t*)vpool + row + lane * (E * BITS / 8);
-          if constexpr (E * BITS / 8 == 2) {
-            *(uint16_t*)kp = (uint16_t)kw;
-            *(uint16_t*)vp = (uint16_t)vw;
-          } else {
-            *kp = (uint8_t)kw;
-            *vp = (uint8_t)vw;
-          }
+          kin[u][e] = a.k_new[src + e];
+          vin[u][e] = a.v_new[src + e];
         }
       }
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        lo[e] = fminf(lo[e], kdec[e]);
-        hi[e] = fmaxf(hi[e], kdec[e]);
+      for (int u = 0; u < kRowBatch; ++u) {
+        const int t = t0 + u;
+        if (t >= t_end) break;  // wave-uniform
+        const size_t dst = (tile + t % kPage) * D + lane * E;
+        float kdec[E];
+        if constexpr (PF == kFp16) {
+          uint32_t kw = 0, vw = 0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const uint16_t kb = kin[u][e];
+            const uint16_t vb = vin[u][e];
+            if constexpr (WT) {
+              kw |= (uint32_t)kb << (16 * e);
+              vw |= (uint32_t)vb << (16 * e);
+            } else {
+              ((uint16_t*)kpool)[dst + e] = kb;
+              ((uint16_t*)vpool)[dst + e] = vb;
+            }
+            kdec[e] = half_bits_to_float(kb);
+          }
+          if constexpr (WT) {
+            const size_t row = (tile + t % kPage) * D * 2;
+            store_row_dev<2 * E>((uint8_t*)kpool + row, kw);
+            store_row_dev<2 * E>((uint8_t*)vpool + row, vw);
+          }
+        } else {
+          float kx[E], vx[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            kx[e] = half_bits_to_float(kin[u][e]);
+            vx[e] = half_bits_to_float(vin[u][e]);
+          }
+          float ks = gk[0], kz = gk[1], kinv = ginv[0], vs = gv[0], vz = gv[1], vinv = ginv[1];
+          if constexpr (fmt_token(PF)) {
+            float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              klo = fminf(klo, kx[e]); khi = fmaxf(khi, kx[e]);
+              vlo = fminf(vlo, vx[e]); vhi = fmaxf(vhi, vx[e]);
+            }
+            klo = zero_point(min_contig<64>(klo)); khi = max_contig<64>(khi);
+            vlo = zero_point(min_contig<64>(vlo)); vhi = max_contig<64>(vhi);
+            quant_params<LV>(klo, khi, ks, kinv);
+            quant_params<LV>(vlo, vhi, vs, vinv);
+            kz = klo;
+            vz = vlo;
+            if (lane == 0) {
+              float* tp = params + (tile + t % kPage) * 4;
+              if constexpr (WT) {
+                store_f<true>(tp, ks);
+                store_f<true>(tp + 1, kz);
+                store_f<true>(tp + 2, vs);
+                store_f<true>(tp + 3, vz);
+              } else {
+                *(float4*)tp = make_float4(ks, kz, vs, vz);
+              }
+            }
+          }
+          uint32_t kw = 0, vw = 0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const uint32_t kc = quant_code<LV>(kx[e], kz, kinv);
+            const uint32_t vc = quant_code<LV>(vx[e], vz, vinv);
+            kw |= kc << (BITS * e);
+            vw |= vc << (BITS * e);
+            kdec[e] = __builtin_fmaf((float)kc, ks, kz);
+          }
+          const size_t row = (tile + t % kPage) * CROW;
+          if constexpr (WT) {
+            store_row_dev<E * BITS / 8>((uint8_t*)kpool + row, kw);
+            store_row_dev<E * BITS / 8>((uint8_t*)vpool + row, vw);
+          } else {
+            uint8_t* kp = (uint8_t*)kpool + row + lane * (E * BITS / 8);
+            uint8_t* vp = (uint8_t*)vpool + row + lane * (E * BITS / 8);
+            if constexpr (E * BITS / 8 == 2) {
+              *(uint16_t*)kp = (uint16_t)kw;
+              *(uint16_t*)vp = (uint16_t)vw;
+            } else {
+              *kp = (uint8_t)kw;
+              *vp = (uint8_t)vw;
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          lo[e] = fminf(lo[e], kdec[e]);
+          hi[e] = fmaxf(hi[e], kdec[e]);
+        }
       }
     }
 
@@ -225,12 +242,29 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
   // ---- group (scale, zero): one per (64-token group, KV head), K and V apart
   float gk[2] = {0.0f, 0.0f}, gv[2] = {0.0f, 0.0f}, ginv[2] = {1.0f, 1.0f};
   if constexpr (fmt_group(FMT)) {
+    // thread t takes channel pairs t, t + 256, ..., kRowBatch of them in
+    // flight (a pair past the group's last re-reads the last: min and max
+    // do not change)
     float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
-    for (int e = threadIdx.x; e < n * D; e += 256) {
-      const size_t src = ((size_t)(r0 + e / D) * a.H + h) * D + e % D;
-      const float kx = half_bits_to_float(a.k_new[src]), vx = half_bits_to_float(a.v_new[src]);
-      klo = fminf(klo, kx); khi = fmaxf(khi, kx);
-      vlo = fminf(vlo, vx); vhi = fmaxf(vhi, vx);
+    const int npairs = n * D / 2;
+    for (int p0 = threadIdx.x; p0 < npairs; p0 += 256 * kRowBatch) {
+      uint16_t kin[kRowBatch][2], vin[kRowBatch][2];
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        const int e = 2 * min(p0 + 256 * u, npairs - 1);
+        const size_t src = ((size_t)(r0 + e / D) * a.H + h) * D + e % D;
+        kin[u][0] = a.k_new[src];
+        kin[u][1] = a.k_new[src + 1];
+        vin[u][0] = a.v_new[src];
+        vin[u][1] = a.v_new[src + 1];
+      }
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        const float k0 = half_bits_to_float(kin[u][0]), k1 = half_bits_to_float(kin[u][1]);
+        const float v0 = half_bits_to_float(vin[u][0]), v1 = half_bits_to_float(vin[u][1]);
+        klo = fminf(klo, fminf(k0, k1)); khi = fmaxf(khi, fmaxf(k0, k1));
+        vlo = fminf(vlo, fminf(v0, v1)); vhi = fmaxf(vhi, fmaxf(v0, v1));
+      }
     }
     klo = min_contig<64>(klo); khi = max_contig<64>(khi);
     vlo = min_contig<64>(vlo); vhi = max_contig<64>(vhi);
