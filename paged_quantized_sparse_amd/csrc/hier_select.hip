@@ -51,12 +51,24 @@ __global__ __launch_bounds__(256) void coarse_meta_kernel(CoarseArgs a) {
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = max_row ? -INFINITY : INFINITY;
+  // member pages 8 at a time: their block-table entries in one load (lane i
+  // takes page j0 + i%8), then their 8 rows, all in flight together; a slot
+  // past the super-page's last page re-reads the last (min and max do not
+  // change)
   const int j_end = min((jc + 1) * a.group, P);
-  for (int j = jc * a.group; j < j_end; ++j) {
-    const int phys = a.block_table[(size_t)b * a.max_pages + j];
-    const float* m = a.meta + ((size_t)phys * a.H + h) * 2 * D + lane * E;
+  for (int j0 = jc * a.group; j0 < j_end; j0 += 8) {  // wave-uniform
+    const int phys_v = a.block_table[(size_t)b * a.max_pages + min(j0 + (lane & 7), j_end - 1)];
+    float v[8][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = max_row ? fmaxf(acc[e], m[e]) : fminf(acc[e], m[e]);
+    for (int p = 0; p < 8; ++p) {
+      const float* m = a.meta + ((size_t)__builtin_amdgcn_readlane(phys_v, p) * a.H + h) * 2 * D + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[p][e] = m[e];
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = max_row ? fmaxf(acc[e], v[p][e]) : fminf(acc[e], v[p][e]);
   }
   float* out = a.coarse + (((size_t)b * a.pc_max + jc) * a.H + h) * 2 * D + lane * E;
 #pragma unroll
