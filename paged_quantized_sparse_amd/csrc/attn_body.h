@@ -154,7 +154,9 @@ typedef short short4v __attribute__((ext_vector_type(4)));  // four bf16 bit pat
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 // Matrix-core form for a GQA group (G >= 2 query heads per KV head) over
-// INT8 or 4-bit codes, where q.k and p.v are small GEMMs per 16-token page.  A
+// INT8 or 4-bit codes (and over the fp16 pages of a mixed cache, see the
+// fp16 value product below), where q.k and p.v are small GEMMs per 16-token
+// page.  A
 // 16x16xKB MFMA takes A[i][k] from lane i + 16(k/KL), element k%KL, B[k][j]
 // from lane j + 16(k/KL), element k%KL (KL = KB/4 elements per lane), and
 // leaves D[i][j] in lane j + 16(i/4), register i%4.
@@ -174,7 +176,9 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 //   4g + l%4) and a 4x4 byte transpose inside each lane quad (two DPP
 //   exchanges and byte permutes) hands lane (g, q, r) channel
 //   (D/4)q + 4j + r of tokens 4g .. 4g+3 for MFMA j.
-// The key codes become exact fp16 values as in the vector path.
+// The key codes become exact fp16 values as in the vector path.  fp16 tiles
+// take the same two products with the fp16 keys and values as they are,
+// the weights for the values being 2^7 p split into two fp16 parts.
 template <int FMT, int D, int G>
 struct MfmaPath {
   static constexpr bool on = G >= 2 && G <= 16;
