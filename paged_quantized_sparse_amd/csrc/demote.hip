@@ -44,34 +44,50 @@ __global__ __launch_bounds__(256) void demote_kernel(DemoteArgs a) {
     float lo[E], hi[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) { lo[e] = INFINITY; hi[e] = -INFINITY; }
-    for (int t = 0; t < nvalid; ++t) {
-      const size_t from = (((size_t)src * a.H + h) * kPage + t) * D + lane * E;
-      const size_t row = (((size_t)to * a.H + h) * kPage + t) * D + lane * E;
-      float kx[E], vx[E];
-      float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
+    // tokens four at a time: their fp16 rows are loaded together (a slot
+    // past the page's last valid token re-reads the last one, unused)
+    for (int t0 = 0; t0 < nvalid; t0 += 4) {
+      uint16_t kin[4][E], vin[4][E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        kx[e] = half_bits_to_float(a.k16[from + e]);
-        vx[e] = half_bits_to_float(a.v16[from + e]);
-        klo = fminf(klo, kx[e]); khi = fmaxf(khi, kx[e]);
-        vlo = fminf(vlo, vx[e]); vhi = fmaxf(vhi, vx[e]);
-      }
-      klo = zero_point(min_contig<64>(klo)); khi = max_contig<64>(khi);
-      vlo = zero_point(min_contig<64>(vlo)); vhi = max_contig<64>(vhi);
-      float ks, kinv, vs, vinv;
-      quant_params(klo, khi, ks, kinv);
-      quant_params(vlo, vhi, vs, vinv);
+      for (int u = 0; u < 4; ++u) {
+        const size_t from = (((size_t)src * a.H + h) * kPage + min(t0 + u, nvalid - 1)) * D + lane * E;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const uint32_t kc = quant_code(kx[e], klo, kinv), vc = quant_code(vx[e], vlo, vinv);
-        a.k8[row + e] = (uint8_t)kc;
-        a.v8[row + e] = (uint8_t)vc;
-        const float k = __builtin_fmaf((float)kc, ks, klo);
-        lo[e] = fminf(lo[e], k);
-        hi[e] = fmaxf(hi[e], k);
+        for (int e = 0; e < E; ++e) {
+          kin[u][e] = a.k16[from + e];
+          vin[u][e] = a.v16[from + e];
+        }
       }
-      if (lane == 0)
-        *(float4*)(a.params + (((size_t)to * a.H + h) * kPage + t) * 4) = make_float4(ks, klo, vs, vlo);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + u;
+        if (t >= nvalid) break;  // wave-uniform
+        const size_t row = (((size_t)to * a.H + h) * kPage + t) * D + lane * E;
+        float kx[E], vx[E];
+        float klo = INFINITY, khi = -INFINITY, vlo = INFINITY, vhi = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          kx[e] = half_bits_to_float(kin[u][e]);
+          vx[e] = half_bits_to_float(vin[u][e]);
+          klo = fminf(klo, kx[e]); khi = fmaxf(khi, kx[e]);
+          vlo = fminf(vlo, vx[e]); vhi = fmaxf(vhi, vx[e]);
+        }
+        klo = zero_point(min_contig<64>(klo)); khi = max_contig<64>(khi);
+        vlo = zero_point(min_contig<64>(vlo)); vhi = max_contig<64>(vhi);
+        float ks, kinv, vs, vinv;
+        quant_params(klo, khi, ks, kinv);
+        quant_params(vlo, vhi, vs, vinv);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint32_t kc = quant_code(kx[e], klo, kinv), vc = quant_code(vx[e], vlo, vinv);
+          a.k8[row + e] = (uint8_t)kc;
+          a.v8[row + e] = (uint8_t)vc;
+          const float k = __builtin_fmaf((float)kc, ks, klo);
+          lo[e] = fminf(lo[e], k);
+          hi[e] = fmaxf(hi[e], k);
+        }
+        if (lane == 0)
+          *(float4*)(a.params + (((size_t)to * a.H + h) * kPage + t) * 4) = make_float4(ks, klo, vs, vlo);
+      }
     }
     float* m = a.meta + ((size_t)dst * a.H + h) * 2 * D + lane * E;
 #pragma unroll
