@@ -298,11 +298,13 @@ __device__ __forceinline__ void combine_one(const AttnArgs& a, int bh) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // a slot past the row's splits holds whatever the workspace held (any
-      // bits, NaN included): its values are replaced, not multiplied by 0
-      const bool live = s0 + part + u * PARTS < ns;
-      const float ms = live ? mlv[u].x : -INFINITY;
-      const float as = live ? av[u] : 0.0f;
-      const float ls = live ? mlv[u].y : 0.0f;
+      // bits, NaN included), so it is never read; the part is wave-uniform,
+      // so this exit is too (a dead slot merged as (-inf, 0, 0) would leave
+      // every value as it is, bit for bit, at the cost of two exp2f)
+      if (s0 + part + u * PARTS >= ns) break;
+      const float ms = mlv[u].x;
+      const float as = av[u];
+      const float ls = mlv[u].y;
       const float Mn = fmaxf(M, ms);
       const float fo = M == -INFINITY ? 0.0f : exp2f(M - Mn);
       const float fs = ms == -INFINITY ? 0.0f : exp2f(ms - Mn);
