@@ -1,6 +1,8 @@
-// append_body.h -- the decode-time append of one (sequence, KV head), as a
-// block-level device function shared by append_decode.hip and the fused
-// append + scores kernel.  Called by all 256 threads of a block.
+// append_body.h -- the append of up to 64 rows of one (sequence, KV head),
+// as a block-level device function shared by the decode-time append
+// (append_decode.hip), the fused append + scores kernel and, without the
+// metadata, the bulk append (append_quant.hip, 64-row chunks).  Called by all
+// 256 threads of a block.
 //
 // Writes sequence b's newest rows for KV head h into their pages (fp16 copy,
 // INT8 per token, or INT8 per 64-token group: "KV-cache layout from the
@@ -67,7 +69,7 @@ __device__ __forceinline__ void store_row_dev(uint8_t* row, uint32_t bits) {
 // new rows written (rows r0 .. r0+n-1 hold tokens start .. start+n-1), each
 // decoded key folded into lo / hi (lane l: channels l*E .. l*E+E-1).  gk, gv,
 // ginv: the group's (scale, zero) and 1/scale for the per-group formats.
-template <int PF, int D, bool WT>
+template <int PF, int D, bool WT, bool META = true>
 __device__ __forceinline__ void append_page(const AppendView& a, void* kpool, void* vpool, float* params, int idx,
                                             int j, int h, int start, int n, int r0, const float* gk,
                                             const float* gv, const float* ginv, float* lo, float* hi) {
@@ -83,7 +85,7 @@ __device__ __forceinline__ void append_page(const AppendView& a, void* kpool, vo
     // older tokens of the page (only the first touched page has any): all 16
     // slots are loaded at once and the slots at or past `start` masked out,
     // so no load waits on another
-    const int nold = t_begin - j * kPage;
+    const int nold = META ? t_begin - j * kPage : 0;
     if (nold > 0) {  // wave-uniform
       float kold[kPage][E];
 #pragma unroll
@@ -223,17 +225,22 @@ __device__ __forceinline__ void append_page(const AppendView& a, void* kpool, vo
 
 // WT: every store is a device-scope (written-through) store, for readers in
 // other blocks of the same launch (the fused decode step); otherwise the
-// stores are ordinary.
-template <int FMT, int D, bool WT = false>
+// stores are ordinary.  META: the touched pages' metadata is rebuilt (from
+// their older tokens too); without it only codes and scale/zero are written
+// (the bulk append, whose metadata kvq_build_page_meta builds).  `skip`: the
+// block takes sequence b's new rows skip .. skip+limit-1, limit <= 64 (the
+// bulk append's 64-row chunks; a per-group format's chunks start on its
+// groups).
+template <int FMT, int D, bool WT = false, bool META = true>
 __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b, int h,
-                                                     float (*sm_meta)[2][D]) {
+                                                     float (*sm_meta)[2][D], int skip = 0, int limit = 64) {
   constexpr int E = D / 64;
   constexpr int LV = fmt_levels(FMT);
   static_assert(!fmt_int4(FMT) || E == 2, "4-bit rows are built for head_dim 128");
   // at most 64 rows (the documented limit; clamping keeps every index in range)
-  const int r0 = a.new_off[b], n = min(a.new_off[b + 1] - r0, 64);
+  const int r0 = a.new_off[b] + skip, n = min(a.new_off[b + 1] - r0, min(limit, 64));
   if (n <= 0) return;  // block-uniform
-  const int start = a.start_pos[b];
+  const int start = a.start_pos[b] + skip;
   const int j_lo = start / kPage;
   const int npages = (start + n - 1) / kPage - j_lo + 1;
   const int w = wave_id(), lane = lane_id();
@@ -301,26 +308,27 @@ __device__ __forceinline__ void append_rows_and_meta(const AppendView& a, int b,
     for (int e = 0; e < E; ++e) { lo[e] = INFINITY; hi[e] = -INFINITY; }
     if constexpr (FMT == kMixed) {  // the page's pool decides its format
       if (phys < a.n16) {
-        append_page<kFp16, D, WT>(a, a.k_pages, a.v_pages, a.params, phys, j, h, start, n, r0, gk, gv, ginv, lo,
-                                  hi);
+        append_page<kFp16, D, WT, META>(a, a.k_pages, a.v_pages, a.params, phys, j, h, start, n, r0, gk, gv, ginv,
+                                        lo, hi);
       } else {
         const size_t off = (size_t)a.n16 * a.H * kPage * D * 2;
-        append_page<kInt8Token, D, WT>(a, (char*)a.k_pages + off, (char*)a.v_pages + off, a.params, phys - a.n16,
-                                       j, h, start, n, r0, gk, gv, ginv, lo, hi);
+        append_page<kInt8Token, D, WT, META>(a, (char*)a.k_pages + off, (char*)a.v_pages + off, a.params,
+                                             phys - a.n16, j, h, start, n, r0, gk, gv, ginv, lo, hi);
       }
     } else {
-      append_page<FMT, D, WT>(a, a.k_pages, a.v_pages, a.params, phys, j, h, start, n, r0, gk, gv, ginv, lo, hi);
+      append_page<FMT, D, WT, META>(a, a.k_pages, a.v_pages, a.params, phys, j, h, start, n, r0, gk, gv, ginv, lo,
+                                    hi);
     }
-
-    // the page's metadata: min row then max row
-    float* m = a.meta + ((size_t)phys * a.H + h) * 2 * D + lane * E;
+    if constexpr (META) {  // the page's metadata: min row then max row
+      float* m = a.meta + ((size_t)phys * a.H + h) * 2 * D + lane * E;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      store_f<WT>(m + e, lo[e]);
-      store_f<WT>(m + D + e, hi[e]);
-      if (sm_meta) {
-        sm_meta[pi][0][lane * E + e] = lo[e];
-        sm_meta[pi][1][lane * E + e] = hi[e];
+      for (int e = 0; e < E; ++e) {
+        store_f<WT>(m + e, lo[e]);
+        store_f<WT>(m + D + e, hi[e]);
+        if (sm_meta) {
+          sm_meta[pi][0][lane * E + e] = lo[e];
+          sm_meta[pi][1][lane * E + e] = hi[e];
+        }
       }
     }
   }
