@@ -34,6 +34,10 @@ __device__ __forceinline__ void page_lo_hi(const void* k_pages, const float* par
     float lo[E], hi[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) { lo[e] = INFINITY; hi[e] = -INFINITY; }
+    // per-token (scale, zero) of the 16 slots in one load: lane t < 16 takes
+    // slot t's pair, each row reads it back with readlane
+    float2 prm = make_float2(0.0f, 0.0f);
+    if constexpr (FMT != kFp16 && fmt_token(FMT)) prm = *(const float2*)(params + (tile + (lane & 15)) * 4);
 #pragma unroll
     for (int t = 0; t < kPage; ++t) {
       if (t < nvalid) {
@@ -44,8 +48,15 @@ __device__ __forceinline__ void page_lo_hi(const void* k_pages, const float* par
 #pragma unroll
           for (int e = 0; e < E; ++e) k[e] = half_bits_to_float(src[e]);
         } else {
-          const float* p = fmt_token(FMT) ? params + (tile + t) * 4 : params + ((size_t)idx * H + h) * 4;
-          const float sc = p[0], zr = p[1];
+          float sc, zr;
+          if constexpr (fmt_token(FMT)) {
+            sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, prm.x), t));
+            zr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, prm.y), t));
+          } else {
+            const float* p = params + ((size_t)idx * H + h) * 4;
+            sc = p[0];
+            zr = p[1];
+          }
           if constexpr (fmt_int4(FMT)) {  // channels 2l, 2l+1: the two nibbles of byte l
             const uint32_t c = ((const uint8_t*)k_pages)[row / 2];
 #pragma unroll
