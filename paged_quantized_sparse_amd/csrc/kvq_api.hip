@@ -224,12 +224,13 @@ int32_t kvq_num_selected(int32_t num_pages, int32_t ratio_num, int32_t ratio_den
 int32_t kvq_default_pages_per_split(int32_t batch, int32_t num_kv_heads, int32_t max_pages, int32_t k_cap) {
   // Few, long splits: each block streams its pages with the next tile in
   // flight, and every split adds a partial to merge.  Aim for about two
-  // blocks per CU (512 on 256 CUs), 16..128 pages each (measured: 40 pages
-  // at 32K x 32 heads; 96-128 beat 64 and 192 on 64 ragged GQA sequences).
+  // blocks per CU (512 on 256 CUs), 24..128 pages each (measured: 40 pages
+  // at 32K x 32 heads; 96-128 beat 64 and 192 on 64 ragged GQA sequences;
+  // 16 x 308 selected pages at 16K: 24 pages per split beat 12, 16, 32, 48).
   const long long cap = k_cap > 0 ? k_cap : max_pages;
   const long long total = (long long)batch * num_kv_heads * cap;
   long long pps = (total + 511) / 512;
-  if (pps < 16) pps = 16;
+  if (pps < 24) pps = 24;
   if (pps > 128) pps = 128;
   return (int32_t)((pps + 3) / 4 * 4);
 }

@@ -72,7 +72,8 @@ def test_workspace_bytes(lib):
     assert lib.kvq_attn_workspace_bytes(1, 32, 128, 128, 0, 0) == 0
     pps = lib.kvq_default_pages_per_split(1, 32, 2048, 615)
     assert pps == 40   # ceil(32 * 615 / 512) = 39, rounded up to a multiple of 4
-    assert lib.kvq_default_pages_per_split(1, 4, 64, 16) == 16
+    assert lib.kvq_default_pages_per_split(1, 4, 64, 16) == 24      # the minimum: one split of K = 16
+    assert lib.kvq_default_pages_per_split(1, 16, 1024, 308) == 24   # 16 rows of 308 pages
     assert lib.kvq_default_pages_per_split(64, 8, 2048, 615) == 128
 
 
