@@ -32,9 +32,10 @@ struct AppendArgs {
 };
 
 // ---------------------------------------------------------------- fp16 copy
-// grid (ceil(max_new / 4), B), 256 threads: 4 tokens per block, 16-byte chunks.
+// grid (ceil(max_new / 4), B), 256 threads: 4 tokens per block, 16-byte chunks;
+// rows past max_new are not written.
 template <int D>
-__global__ __launch_bounds__(256) void append_fp16_kernel(AppendArgs a) {
+__global__ __launch_bounds__(256) void append_fp16_kernel(AppendArgs a, int max_new) {
   const int b = blockIdx.y;
   const int r0 = a.new_off[b], n = a.new_off[b + 1] - r0;
   const int start = a.start_pos[b];
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void append_fp16_kernel(AppendArgs a) {
   const int chunks = 4 * a.H * CPR;
   for (int c = threadIdx.x; c < chunks; c += 256) {
     const int i = blockIdx.x * 4 + c / (a.H * CPR);
-    if (i >= n) continue;
+    if (i >= n || i >= max_new) continue;
     const int rem = c % (a.H * CPR);
     const int h = rem / CPR, part = rem % CPR;
     const int t = start + i;
@@ -167,7 +168,9 @@ hipError_t launch_append_d(const kvq_cache& c, const kvq_seqs& s, const AppendAr
   const AppendView v{a.k_pages, a.v_pages, a.params, nullptr, a.block_table, a.start_pos, a.new_off, a.k_new,
                      a.v_new, a.H, a.max_pages, a.n16};
   switch (c.format) {
-    case KVQ_FP16: hipLaunchKernelGGL(append_fp16_kernel<D>, dim3((max_new + 3) / 4, B), dim3(256), 0, st, a); break;
+    case KVQ_FP16:
+      hipLaunchKernelGGL(append_fp16_kernel<D>, dim3((max_new + 3) / 4, B), dim3(256), 0, st, a, max_new);
+      break;
     case KVQ_INT8_TOKEN:
       hipLaunchKernelGGL((append_token_chunk_kernel<kInt8Token, D>), chunk_grid, dim3(256), 0, st, v, max_new);
       break;

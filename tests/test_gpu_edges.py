@@ -444,3 +444,56 @@ def test_config5_every_sequence(part):
         assert err <= ATTN_ATOL, f"sequence {b} L={L}: max abs err {err:.3g}"
     log(f"[cfg5] sequences {16 * part}..{16 * part + 15}: max abs err "
         f"{max(c['errs'][b] for b in range(16 * part, 16 * part + 16)):.3g}")
+
+
+# ------------------------------------------------------ rows past max_new
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4, 5],
+                         ids=["fp16", "int8tok", "int8grp", "int4tok", "int4grp", "mixed"])
+def test_bulk_append_writes_no_row_past_max_new(fmt):
+    """kvq_append_quant writes rows 0 .. max_new-1 of each sequence and no row
+    past them: sequence 0 supplies 100 rows but max_new is 70, so its rows
+    70 .. 99 are left as they were (a byte pattern laid down first), and every
+    byte of the caches equals the oracle appending the same 70 (and 30) rows
+    into caches that hold the same pattern.  Per-token formats start mid-page;
+    per-group formats start on a group (64 tokens)."""
+    kvq, _ = mods()
+    H, d = 2, 128
+    group = fmt in (workloads.FMT_INT8_GROUP64, workloads.FMT_INT4_GROUP64)
+    start = np.array([64 if group else 21, 5 if not group else 0], np.int64)
+    rows = np.array([100, 30], np.int64)
+    max_new = 70
+    P = (start + rows + PAGE - 1) // PAGE
+    n_phys = int(P.sum()) + 2
+    table = np.full((2, int(P.max())), -1, np.int32)
+    perm = np.random.default_rng(4).permutation(n_phys)
+    table[0, :P[0]] = perm[:P[0]]
+    table[1, :P[1]] = perm[P[0]:P[0] + P[1]]
+    rng = np.random.default_rng(17)
+    k_all = [rng.standard_normal((int(r), H, d)).astype(np.float16) for r in rows]
+    v_all = [rng.standard_normal((int(r), H, d)).astype(np.float16) for r in rows]
+    n16 = n_phys // 2 if fmt == workloads.FMT_MIXED else 0
+    cache = kvq.PagedCache.empty(fmt, n_phys, H, d, num_fp16_pages=n16)
+    oc = oracle.Cache(fmt, n_phys, H, d, n16)
+    for t in (cache.k_pages, cache.v_pages):
+        t.view(torch.uint8).fill_(0xAB)
+    oc.k_pages.view(np.uint8)[...] = 0xAB
+    oc.v_pages.view(np.uint8)[...] = 0xAB
+    if cache.kv_params is not None:
+        cache.kv_params.view(torch.int32).fill_(0x7FC0ABAB)
+        oc.params.view(np.uint32)[...] = 0x7FC0ABAB
+    seqs = kvq.Seqs(dev_i32(start + rows), dev_i32(table))
+    k_new = np.concatenate(k_all)
+    v_new = np.concatenate(v_all)
+    off = np.concatenate([[0], np.cumsum(rows)])
+    kvq.kvq_append_quant(cache, seqs, dev_i32(start), dev_i32(off), max_new, f16_bits(k_new), f16_bits(v_new))
+    torch.cuda.synchronize()
+    # the oracle appends what max_new lets through: 70 rows of sequence 0, all 30 of sequence 1
+    kept = np.minimum(rows, max_new)
+    ok = np.concatenate([k_all[0][:kept[0]], k_all[1][:kept[1]]])
+    ov = np.concatenate([v_all[0][:kept[0]], v_all[1][:kept[1]]])
+    oracle.append(oc, table, start.astype(np.int32), np.concatenate([[0], np.cumsum(kept)]).astype(np.int32), ok, ov)
+    k, v = to_np(cache.k_pages), to_np(cache.v_pages)
+    assert np.array_equal(k.view(np.uint8), oc.k_pages.view(np.uint8)), "K bytes"
+    assert np.array_equal(v.view(np.uint8), oc.v_pages.view(np.uint8)), "V bytes"
+    if cache.kv_params is not None:
+        assert np.array_equal(to_np(cache.kv_params).view(np.uint32), oc.params.view(np.uint32)), "scale/zero bits"
