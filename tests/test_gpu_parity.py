@@ -395,6 +395,25 @@ def test_select_attention_rows_at_the_limit():
     assert torch.equal(out, want)                     # same splits, same pages: same bits
 
 
+@pytest.mark.parametrize("n", [2, 4, 5])
+def test_select_attention_without_selection_outputs(n):
+    """sel_pages / sel_count of kvq_select_decode_attn are optional: with both
+    NULL the output is the same, bit for bit, as with both given."""
+    kvq, _ = kvq_mod()
+    bt = built(("small", n), workloads.small(n))
+    w = bt.w
+    st = bt.step()
+    assert st.fused_select
+    kvq.kvq_page_scores(bt.cache, bt.seqs, bt.q_dev, st.scores)
+    st.select_attend(bt.q_dev)
+    with_sel = st.out.clone()
+    st.out.fill_(7.0)
+    kvq.kvq_select_decode_attn(bt.cache, bt.seqs, bt.q_dev, st.scores, w.ratio_num, w.ratio_den, w.k_fixed,
+                               st.k_cap, st.out, st.workspace, st.sm_scale, st.pps)
+    torch.cuda.synchronize()
+    assert torch.equal(st.out, with_sel)
+
+
 @pytest.mark.parametrize("fused", [True, False])
 def test_empty_sequences_in_batch(fused):
     """Sequences of length 0 inside a ragged GQA batch: all their scores are
